@@ -1,0 +1,76 @@
+"""Pins of the oracle's storage-format helpers against library casts and the format definitions."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import numerics as nu
+
+
+def test_bf16_decode_all_codes_match_torch():
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    ours = nu.bf16_decode(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_bf16_encode_roundtrip_all_finite_codes():
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    vals = nu.bf16_decode(codes)
+    fin = np.isfinite(vals) & ~((vals == 0) & np.signbit(vals))
+    assert (nu.bf16_encode(vals[fin]) == codes[fin]).all()
+
+
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e4, 1e-38])
+def test_bf16_round_matches_torch_rne_on_float32(scale):
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200_000) * scale).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert (nu.bf16_round(x.astype(np.float64)) == ref).all()
+
+
+def test_bf16_ties_go_to_even():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: the even neighbour is 1.
+    assert nu.bf16_round(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+    assert nu.bf16_round(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    # Just above a midpoint rounds up.
+    assert nu.bf16_round(np.array([1.0 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    ours = nu.e4m3_decode(codes)
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+    assert np.nanmax(ours) == 448.0 and np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+    assert ours[1] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_e4m3_round_matches_torch_in_range():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(200_000) * 60).astype(np.float32)
+    x = x[np.abs(x) < 464]              # torch's cast does not saturate; compare in range only
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    assert (nu.e4m3_round(x.astype(np.float64)) == ref).all()
+    small = (rng.standard_normal(50_000) * 2e-3).astype(np.float32)
+    ref = torch.from_numpy(small).to(torch.float8_e4m3fn).double().numpy()
+    assert (nu.e4m3_round(small.astype(np.float64)) == ref).all()
+
+
+def test_e4m3_worked_values_and_saturation():
+    # 0.1 = 1.6 * 2^-4; the 3-bit neighbours are 1.5 and 1.625 -> 1.625 * 2^-4.
+    assert nu.e4m3_round(np.array([0.1]))[0] == 0.1015625
+    # 464 is halfway between 448 (mantissa 110, even) and the NaN slot 480: ties to 448.
+    assert nu.e4m3_round(np.array([464.0, 470.0, 1e6, -1e6])).tolist() == [448, 448, 448, -448]
+    # Half the smallest subnormal ties to zero; 1.5 of it rounds to 2 quanta.
+    q = 2.0 ** -9
+    assert nu.e4m3_round(np.array([0.5 * q, 1.5 * q])).tolist() == [0.0, 2 * q]
+
+
+def test_e4m3_encode_roundtrip():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = nu.e4m3_decode(codes)
+    ok = np.isfinite(vals) & (codes != 0x80)     # -0 encodes as +0
+    assert (nu.e4m3_encode(vals[ok]) == codes[ok]).all()
