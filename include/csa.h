@@ -1,0 +1,189 @@
+/* libcsa -- hybrid compressed attention (CSA + HCA) on AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as described on the pages this library follows:
+ *   [csdn]   deepseek.csdn.net "一文搞懂 DeepSeek：从 V3 的 KV 压缩与 MoE，到 V4 的百万 token 上下文",
+ *            sections "V3 看家本领一：MLA" (latent KV + decoupled RoPE key, absorbed projections)
+ *            and "V4 改进一：CSA 与 HCA" (compress, index, select, attend with window; HCA).
+ *   [yudong] yudonglee.me "DeepSeek-V4 详解", 2.2 (CSA Steps 1-4) and 2.3 (HCA Steps 1-2).
+ *   [hongke] hongke120.com/20112.html, 2.2-2.3 and 4.1 (four cache entry types: raw tail tokens,
+ *            CSA blocks, HCA summaries, indexer keys).
+ *   [jaylab] jaylab-temp.pages.dev "DeepSeek-V4 — 百万 Token 上下文的高效 MoE 模型",
+ *            其他技术细节 (cache rows: RoPE dims bf16, the rest fp8).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never allocates and
+ *     keeps no state besides its loaded kernels. Calls that need scratch take (ws, ws_bytes),
+ *     sized by the matching *_workspace_bytes() query; ws may be NULL when that query returns 0.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns. No call synchronises. Calls are safe from any host thread.
+ *   - Arguments are validated on the host before anything is enqueued; on any error nothing is
+ *     enqueued and the outputs are untouched. Device-array contents (positions, sequence ids,
+ *     indices) are trusted preconditions.
+ *   - Layouts are row-major and dense unless a leading dimension (ld, in elements) says
+ *     otherwise. bf16 data is passed as raw 16-bit codes; E4M3 as raw bytes (OCP E4M3FN, max 448).
+ *   - The library prints nothing and throws nothing across this boundary.
+ *
+ * Numerics (per call below): fp32 accumulation everywhere. The MFMA attention paths compute in
+ * fp16 on operands converted exactly from bf16 / (fp8 x row scale): they require every cache and
+ * query value to have magnitude below 65504 (values under 2^-17 keep at most 2^-25 absolute
+ * error). The pages state that queries and KV entries are RMS-normalised before attention
+ * (jaylab, Muon bullet list), which keeps them far inside that range.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,        /* null pointer, non-positive size, inconsistent arguments          */
+  CSA_EUNSUPPORTED = 2,  /* valid request with no kernel (dtype / shape combination)          */
+  CSA_EWORKSPACE = 3,    /* ws_bytes smaller than the matching *_workspace_bytes() query      */
+  CSA_EHIP = 4           /* a HIP launch failed; csa_last_error() holds the HIP error text    */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_E4M3 = 2 } csa_dtype;
+
+/* A store of cache rows for B sequences: row = c[d_c] followed by r[d_r] ([csdn] MLA section:
+ * the latent and the decoupled RoPE key are cached per token).
+ *   c      [B][rows][ld_c] in dtype_c; the first d_c elements of a row are used.
+ *   r      [B][rows][ld_r]; bf16 when dtype_c is CSA_BF16 or CSA_E4M3, fp32 when CSA_F32.
+ *          May alias c (e.g. r = c + d_c with ld_r = ld_c for an interleaved bf16 row).
+ *          NULL iff d_r == 0.
+ *   scale  [B][rows] fp32 dequantisation scale of c; required iff dtype_c == CSA_E4M3, else NULL.
+ *          The dequantised row is (scale * c, r) ([jaylab] mixed-precision cache row).
+ *   pos0   [B] int64 absolute position of row 0 (raw-token stores); NULL means 0. */
+typedef struct {
+  const void* c;
+  const void* r;
+  const float* scale;
+  const int64_t* pos0;
+  int32_t dtype_c;
+  int32_t d_c, d_r;
+  int64_t rows;
+  int64_t ld_c, ld_r;
+} csa_kv_t;
+
+/* The writable twin of csa_kv_t (output of csa_compress; pos0 unused). */
+typedef struct {
+  void* c;
+  void* r;
+  float* scale;
+  int32_t dtype_c;
+  int32_t d_c, d_r;
+  int64_t rows;
+  int64_t ld_c, ld_r;
+} csa_kv_out_t;
+
+/* Queries: nq of them; query i belongs to sequence seq[i] (int32, device) and sits at absolute
+ * position pos[i] (int64, device). The pages' causal reading used throughout: entry j of an
+ * m-fold compressed store covers positions [j*m, (j+1)*m - 1] and is visible to a query at pos
+ * iff (j+1)*m - 1 <= pos, i.e. n_vis(pos) = min(N, floor((pos + 1) / m)). */
+typedef struct {
+  const int32_t* seq;
+  const int64_t* pos;
+  int32_t nq;
+} csa_queries_t;
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_compress -- softmax-gated pooling of every m consecutive token rows into one entry.
+ * [csdn] V4 改进一 (CSA step one) and [yudong] 2.2 Step 1 (m = 4); [yudong] 2.3 Step 1 and
+ * [hongke] 2.3 (m' = 128, HCA uses the same pooling).
+ *   For each sequence b, block j < T/m (a trailing partial block is not emitted) and channel c of
+ *   the d = d_c + d_r channels:  a_i = g[b][jm+i][c] + bias[i],  w = softmax_i(a),
+ *   e[b][j][c] = sum_i w_i x[b][jm+i][c].
+ *   x, g   [B][T][d] in in_dtype (CSA_F32 or CSA_BF16); or NULL in projection mode.
+ *   bias   [m] fp32 position bias.
+ *   Projection mode (fp32 only): x and g NULL, hidden [B][T][d_model] fp32 and w_x, w_g
+ *          [d_model][d] fp32 given; x = hidden * w_x and g = hidden * w_g are formed on the fly
+ *          ([csdn] MLA: the cached latent is a projection of the token's input), and x is also
+ *          written to raw_x_out [B][T][d] fp32 (the raw rows a sliding window reads).
+ *          Otherwise hidden, w_x, w_g and raw_x_out must be NULL.
+ *   out    entry store with out->rows == T/m: out->dtype_c CSA_F32, CSA_BF16 (RNE) or CSA_E4M3
+ *          (one fp32 scale per row, scale = amax(|e_c|)/448, codes RNE-satfinite of e_c/scale;
+ *          an all-zero row stores scale 0). The r part is stored bf16 (fp32 when out is F32).
+ *   Constraints: m >= 1, T >= 0, d % 4 == 0 (fp32) or d % 8 == 0 (bf16).
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const float* bias,
+                        int32_t m, int32_t B, int64_t T, int32_t d_c, int32_t d_r,
+                        const float* hidden, const float* w_x, const float* w_g, int32_t d_model,
+                        const csa_kv_out_t* out, float* raw_x_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_index -- lightning-indexer scores of every visible entry for every query.
+ * [csdn] V4 改进一 and [yudong] 2.2 Step 2 (a light indexer, in the manner of the V3.2 lightning
+ * indexer, scores each compressed row against the query; fp8 accelerated).
+ *   s[i][j] = sum_h w[i][h] * max(0, qI[i][h] . kI[seq[i]][j])  for j < n_vis(pos[i]).
+ *   q_i    [nq][H_I][d_I] in qi_dtype (F32, BF16 or E4M3); q_i_scale [nq][H_I] fp32 iff E4M3.
+ *   w      [nq][H_I] fp32 head weights (any sign).
+ *   k_i    [B][N][d_I] in ki_dtype (same dtype as q_i); k_i_scale [B][N] fp32 iff E4M3.
+ *          For fp8: qI = q_i_scale * q_i and kI = k_i_scale * k_i.
+ *   scores [nq][ld_scores] fp32, ld_scores >= N. Columns j >= n_vis(pos[i]) are not written.
+ *   Constraints: d_I == 64 for E4M3/BF16 fast paths; any d_I % 4 == 0 otherwise.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_index(const csa_queries_t* Q, const void* q_i, const float* q_i_scale,
+                     int32_t qi_dtype, const float* w, int32_t H_I, int32_t d_I, const void* k_i,
+                     const float* k_i_scale, int32_t ki_dtype, int32_t B, int64_t N, int32_t m,
+                     float* scores, int64_t ld_scores, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_topk -- per-query selection of the k highest-scoring visible entries.
+ * [csdn] V4 改进一 and [yudong] 2.2 Step 3 (top-k; the pages use k = 64 and k = 1024).
+ *   Among j < n_vis(pos[i]), order by score descending then index ascending (ties go to the lower
+ *   index); take the first min(k, n_vis); write them to idx[i][0..) in ascending index order and
+ *   pad with -1. -0.0 and +0.0 compare equal. Scores must not be NaN.
+ *   scores [nq][ld_scores] fp32 (columns >= n_vis are not read); idx [nq][k] int32.
+ *   Workspace: csa_topk_workspace_bytes(nq, N, k). Deterministic (integer work only).
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scores, int64_t N,
+                    int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+size_t csa_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_attend -- CSA attention: the selected entries plus the raw sliding window, one softmax.
+ * [csdn] V4 改进一 (MQA with one KV shared by all heads; a short window of the most recent raw KV
+ * bypasses compression) and [yudong] 2.2 Step 4; [csdn] MLA (key row [c; r], value row c).
+ *   Keys of query i: entries idx[i][0..k) (entries of sequence seq[i]; -1 slots skipped), then raw
+ *   rows for positions max(0, pos - window + 1) .. pos (no de-duplication). For head h:
+ *     l = sm_scale * (q[i][h][:d_c] . c_key + q[i][h][d_c:] . r_key),  p = softmax(l),
+ *     out[i][h] = sum p * c_key,  lse[i][h] = log sum exp(l)   (natural log).
+ *   An empty key set gives out = 0, lse = -inf.
+ *   q      [nq][H][d_c + d_r] in q_dtype (CSA_F32 with F32 stores, else CSA_BF16).
+ *   entries, raw  stores with identical dtype_c, d_c, d_r; raw must hold every window position
+ *          (row = pos - pos0[seq]).
+ *   out    [nq][H][d_c] fp32; lse [nq][H] fp32 (may be NULL).
+ *   Workspace: csa_attend_workspace_bytes(nq, H, d_c, k + window).
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                      const csa_kv_t* entries, int32_t m, const int32_t* idx, int32_t k,
+                      const csa_kv_t* raw, int32_t window, float sm_scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t csa_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t max_keys);
+
+/* ---------------------------------------------------------------------------------------------
+ * hca_attend -- HCA attention: dense attention over every visible m'-compressed entry.
+ * [csdn] V4 改进一 (HCA) and [yudong] 2.3 Step 2: no selection and no window.
+ *   Keys of query i: entries j < n_vis(pos[i]) of sequence seq[i] with m = m_prime; otherwise as
+ *   csa_attend. Workspace: hca_attend_workspace_bytes(nq, H, d_c, N).
+ * ------------------------------------------------------------------------------------------- */
+csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                      const csa_kv_t* entries, int32_t m_prime, float sm_scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N);
+
+/* Text of a status code; for CSA_EHIP the text of the last HIP error seen by this thread. */
+const char* csa_status_str(int32_t status);
+const char* csa_last_error(void);
+int32_t csa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,228 @@
+// extern "C" entry points of libcsa (declared in include/csa.h): host-side validation of scalars,
+// pointers and shapes, then dispatch to the kernel launchers. Nothing is enqueued on error.
+#include <string>
+
+#include "csa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+csa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CSA_OK;
+  g_last_error = hipGetErrorString(e);
+  return CSA_EHIP;
+}
+
+bool valid_dtype(int32_t d) { return d == CSA_F32 || d == CSA_BF16 || d == CSA_E4M3; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+csa::Store to_store(const csa_kv_t& k) {
+  return csa::Store{k.c, k.r, k.scale, k.pos0, k.dtype_c, k.d_c, k.d_r, k.rows, k.ld_c, k.ld_r};
+}
+
+// Shape and pointer checks common to every cache-row store.
+csa_status check_store(const csa_kv_t* s, const char* name) {
+  static thread_local std::string msg;
+  msg = std::string(name);
+  if (s == nullptr) return fail(CSA_EINVAL, (msg + ": null store").c_str());
+  if (!valid_dtype(s->dtype_c)) return fail(CSA_EINVAL, (msg + ": bad dtype_c").c_str());
+  if (s->d_c <= 0 || s->d_r < 0 || s->rows < 0) return fail(CSA_EINVAL, (msg + ": bad dims").c_str());
+  if (s->ld_c < s->d_c || (s->d_r > 0 && s->ld_r < s->d_r))
+    return fail(CSA_EINVAL, (msg + ": leading dimension below row width").c_str());
+  if (s->rows > 0 && s->c == nullptr) return fail(CSA_EINVAL, (msg + ": null c").c_str());
+  if ((s->d_r > 0) != (s->r != nullptr)) return fail(CSA_EINVAL, (msg + ": r must be set iff d_r > 0").c_str());
+  if ((s->dtype_c == CSA_E4M3) != (s->scale != nullptr))
+    return fail(CSA_EINVAL, (msg + ": scale must be set iff dtype_c is E4M3").c_str());
+  return CSA_OK;
+}
+
+csa_status check_queries(const csa_queries_t* Q) {
+  if (Q == nullptr) return fail(CSA_EINVAL, "null queries");
+  if (Q->nq < 0) return fail(CSA_EINVAL, "nq < 0");
+  if (Q->nq > 0 && (Q->seq == nullptr || Q->pos == nullptr))
+    return fail(CSA_EINVAL, "null query seq/pos");
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+const char* csa_status_str(int32_t status) {
+  switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_EINVAL: return "invalid argument";
+    case CSA_EUNSUPPORTED: return "unsupported dtype/shape combination";
+    case CSA_EWORKSPACE: return "workspace too small";
+    case CSA_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const float* bias,
+                        int32_t m, int32_t B, int64_t T, int32_t d_c, int32_t d_r,
+                        const float* hidden, const float* w_x, const float* w_g, int32_t d_model,
+                        const csa_kv_out_t* out, float* raw_x_out, void* stream) {
+  if (bias == nullptr || out == nullptr) return fail(CSA_EINVAL, "null bias or out");
+  if (m < 1 || B < 0 || T < 0 || d_c <= 0 || d_r < 0) return fail(CSA_EINVAL, "bad sizes");
+  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) return fail(CSA_EINVAL, "in_dtype must be F32 or BF16");
+  if (!valid_dtype(out->dtype_c)) return fail(CSA_EINVAL, "bad out dtype");
+  if (out->d_c != d_c || out->d_r != d_r) return fail(CSA_EINVAL, "out dims differ from d_c/d_r");
+  if (out->rows != T / m) return fail(CSA_EINVAL, "out->rows must equal T / m");
+  if (out->ld_c < d_c || (d_r > 0 && out->ld_r < d_r)) return fail(CSA_EINVAL, "out leading dimension");
+  if ((B > 0 && out->rows > 0) && out->c == nullptr) return fail(CSA_EINVAL, "null out->c");
+  if ((d_r > 0) != (out->r != nullptr)) return fail(CSA_EINVAL, "out->r must be set iff d_r > 0");
+  if ((out->dtype_c == CSA_E4M3) != (out->scale != nullptr))
+    return fail(CSA_EINVAL, "out->scale must be set iff out dtype is E4M3");
+  const int d = d_c + d_r;
+  const bool proj = hidden != nullptr || w_x != nullptr || w_g != nullptr || raw_x_out != nullptr;
+  if (proj) {
+    if (x != nullptr || g != nullptr) return fail(CSA_EINVAL, "projection mode takes no x/g");
+    if (!hidden || !w_x || !w_g || !raw_x_out) return fail(CSA_EINVAL, "projection mode needs hidden, w_x, w_g, raw_x_out");
+    if (in_dtype != CSA_F32 || d_model <= 0) return fail(CSA_EINVAL, "projection mode is fp32 with d_model > 0");
+    if (d % 64 != 0 || d_model % 4 != 0 || (m != 1 && m != 2 && m != 4) || out->dtype_c == CSA_E4M3)
+      return fail(CSA_EUNSUPPORTED, "projection mode needs d % 64 == 0, d_model % 4 == 0, m in {1,2,4}, non-fp8 out");
+    if (!aligned16(hidden) || !aligned16(w_x) || !aligned16(w_g))
+      return fail(CSA_EUNSUPPORTED, "projection operands must be 16-byte aligned");
+  } else {
+    if (B > 0 && T > 0 && (x == nullptr || g == nullptr)) return fail(CSA_EINVAL, "null x or g");
+    const int vec = in_dtype == CSA_F32 ? 4 : 8;
+    if (d % vec != 0 || d_c % vec != 0 || d / vec > 256)
+      return fail(CSA_EUNSUPPORTED, "d and d_c must be multiples of 16 bytes, d <= 256 vectors");
+    if (!aligned16(x) || !aligned16(g)) return fail(CSA_EUNSUPPORTED, "x and g must be 16-byte aligned");
+  }
+  if (B == 0) return CSA_OK;
+  csa::CompressArgs a{x, g, in_dtype, bias, m, B, T, d_c, d_r, hidden, w_x, w_g, d_model,
+                      csa::OutStore{out->c, out->r, out->scale, out->dtype_c, out->d_c, out->d_r,
+                                    out->rows, out->ld_c, out->ld_r},
+                      raw_x_out};
+  return hip_status(csa::launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_index(const csa_queries_t* Q, const void* q_i, const float* q_i_scale,
+                     int32_t qi_dtype, const float* w, int32_t H_I, int32_t d_I, const void* k_i,
+                     const float* k_i_scale, int32_t ki_dtype, int32_t B, int64_t N, int32_t m,
+                     float* scores, int64_t ld_scores, void* stream) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (!valid_dtype(qi_dtype) || qi_dtype != ki_dtype) return fail(CSA_EINVAL, "q_i and k_i must share a valid dtype");
+  if (H_I <= 0 || d_I <= 0 || B <= 0 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
+  if (Q->nq > 0 && (q_i == nullptr || w == nullptr || scores == nullptr)) return fail(CSA_EINVAL, "null q_i/w/scores");
+  if (N > 0 && k_i == nullptr) return fail(CSA_EINVAL, "null k_i");
+  if (qi_dtype == CSA_E4M3 && (q_i_scale == nullptr || k_i_scale == nullptr))
+    return fail(CSA_EINVAL, "fp8 indexer needs q_i_scale and k_i_scale");
+  if ((size_t)H_I * (d_I + 1) * sizeof(float) > 64 * 1024) return fail(CSA_EUNSUPPORTED, "H_I * d_I too large");
+  csa::IndexArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, q_i, q_i_scale, qi_dtype, w, H_I, d_I,
+                   k_i, k_i_scale, B, N, m, scores, ld_scores};
+  return hip_status(csa::launch_index(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+  return csa::topk_workspace(nq, N, k);
+}
+
+csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scores, int64_t N,
+                    int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (k < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
+  if (Q->nq > 0 && (scores == nullptr || idx == nullptr)) return fail(CSA_EINVAL, "null scores/idx");
+  const size_t need = csa::topk_workspace(Q->nq, N, k);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
+  csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, ld_scores, N, m, k, idx, ws, ws_bytes};
+  return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t max_keys) {
+  return csa::attend_workspace(nq, H, d_c, max_keys);
+}
+
+size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N) {
+  return csa::attend_workspace(nq, H, d_c, N);
+}
+
+namespace {
+
+csa_status check_attend_common(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                               const csa_kv_t* entries, int32_t m, float* out) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (csa_status st = check_store(entries, "entries")) return st;
+  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return fail(CSA_EINVAL, "q_dtype must be F32 or BF16");
+  if (H <= 0 || m < 1) return fail(CSA_EINVAL, "bad H or m");
+  if (Q->nq > 0 && (q == nullptr || out == nullptr)) return fail(CSA_EINVAL, "null q or out");
+  if (entries->d_c > 1024 || (entries->d_c + entries->d_r) % 2 != 0)
+    return fail(CSA_EUNSUPPORTED, "d_c must be <= 1024 and d_c + d_r even");
+  return CSA_OK;
+}
+
+}  // namespace
+
+csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                      const csa_kv_t* entries, int32_t m, const int32_t* idx, int32_t k,
+                      const csa_kv_t* raw, int32_t window, float sm_scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (csa_status st = check_attend_common(Q, q, q_dtype, H, entries, m, out)) return st;
+  if (k < 0 || window < 0) return fail(CSA_EINVAL, "negative k or window");
+  if (k > 0 && Q->nq > 0 && idx == nullptr) return fail(CSA_EINVAL, "null idx");
+  if (window > 0) {
+    if (csa_status st = check_store(raw, "raw")) return st;
+    if (raw->dtype_c != entries->dtype_c || raw->d_c != entries->d_c || raw->d_r != entries->d_r)
+      return fail(CSA_EINVAL, "raw and entries stores differ in dtype or dims");
+  }
+  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, (int64_t)k + window);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
+  csa::AttendArgs a{};
+  a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.H = H;
+  a.ent = to_store(*entries);
+  a.m = m;
+  a.dense = 0;
+  a.idx = idx;
+  a.k = k;
+  if (window > 0) a.raw = to_store(*raw);
+  a.window = window;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return hip_status(csa::launch_attend(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                      const csa_kv_t* entries, int32_t m_prime, float sm_scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (csa_status st = check_attend_common(Q, q, q_dtype, H, entries, m_prime, out)) return st;
+  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, entries->rows);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
+  csa::AttendArgs a{};
+  a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.H = H;
+  a.ent = to_store(*entries);
+  a.m = m_prime;
+  a.dense = 1;
+  a.idx = nullptr;
+  a.k = 0;
+  a.window = 0;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return hip_status(csa::launch_attend(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

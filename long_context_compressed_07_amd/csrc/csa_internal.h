@@ -1,0 +1,114 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel translation units.
+// Not installed; the public interface is include/csa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+// A cache-row store as seen by kernels (plain values; device pointers).
+struct Store {
+  const void* c;
+  const void* r;
+  const float* scale;
+  const int64_t* pos0;
+  int dtype;        // csa_dtype of c; r is bf16 unless dtype == CSA_F32 (then fp32)
+  int d_c, d_r;
+  int64_t rows;     // rows per sequence
+  int64_t ld_c, ld_r;
+};
+
+struct OutStore {
+  void* c;
+  void* r;
+  float* scale;
+  int dtype;
+  int d_c, d_r;
+  int64_t rows;
+  int64_t ld_c, ld_r;
+};
+
+struct Queries {
+  const int32_t* seq;
+  const int64_t* pos;
+  int nq;
+};
+
+// ---- compress ----------------------------------------------------------------------------
+struct CompressArgs {
+  const void* x;
+  const void* g;
+  int in_dtype;
+  const float* bias;
+  int m;
+  int B;
+  int64_t T;
+  int d_c, d_r;
+  const float* hidden;
+  const float* w_x;
+  const float* w_g;
+  int d_model;
+  OutStore out;
+  float* raw_x_out;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+// ---- index ---------------------------------------------------------------------------------
+struct IndexArgs {
+  Queries Q;
+  const void* q_i;
+  const float* q_i_scale;
+  int dtype;            // of q_i and k_i
+  const float* w;
+  int H_I, d_I;
+  const void* k_i;
+  const float* k_i_scale;
+  int B;
+  int64_t N;
+  int m;
+  float* scores;
+  int64_t ld_scores;
+};
+hipError_t launch_index(const IndexArgs& a, hipStream_t s);
+
+// ---- top-k ---------------------------------------------------------------------------------
+struct TopkArgs {
+  Queries Q;
+  const float* scores;
+  int64_t ld_scores;
+  int64_t N;
+  int m;
+  int k;
+  int32_t* idx;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t topk_workspace(int nq, int64_t N, int k);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// ---- attention -----------------------------------------------------------------------------
+struct AttendArgs {
+  Queries Q;
+  const void* q;
+  int q_dtype;
+  int H;
+  Store ent;
+  int m;
+  int dense;            // 1: HCA, every visible entry is a key; 0: CSA, the k slots of idx
+  const int32_t* idx;   // [nq][k] selected entries (CSA); unused when dense or k == 0
+  int k;
+  Store raw;            // raw.c == NULL or window == 0: no window
+  int window;
+  float sm_scale;
+  float* out;
+  float* lse;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t attend_workspace(int nq, int H, int d_c, int64_t max_keys);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,110 @@
+"""The C-ABI library: it loads without a GPU, exports every symbol include/csa.h declares, and its
+host-side validation rejects bad arguments before enqueuing anything (no GPU needed for these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_compressed_07_amd import lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "csa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:csa_status|size_t|const char\*|int32_t)\s+(\w+)\s*\(",
+                                 text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libcsa.so not built")
+    return lib.load()
+
+
+def test_header_declares_the_five_ops():
+    fns = declared_functions()
+    for name in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend"):
+        assert name in fns
+    assert set(fns) == set(lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.csa_abi_version() == 1
+    assert L.csa_status_str(0) == b"ok"
+    assert L.csa_status_str(3) == b"workspace too small"
+
+
+def _q(nq=1):
+    # Fake device addresses: validation fails before any of them is dereferenced.
+    return lib.Queries(0x1000, 0x2000, nq)
+
+
+def test_topk_validation(L):
+    Q = _q()
+    assert L.csa_topk(ctypes.byref(Q), 0x3000, 10, 10, 4, 0, 0x4000, None, 0, None) == 1   # k = 0
+    assert L.csa_topk(ctypes.byref(Q), 0x3000, 5, 10, 4, 3, 0x4000, None, 0, None) == 1    # ld < N
+    assert L.csa_topk(None, 0x3000, 10, 10, 4, 3, 0x4000, None, 0, None) == 1              # null Q
+    bad = lib.Queries(None, 0x2000, 1)
+    assert L.csa_topk(ctypes.byref(bad), 0x3000, 10, 10, 4, 3, 0x4000, None, 0, None) == 1
+    assert b"seq" in L.csa_last_error()
+
+
+def test_index_validation(L):
+    Q = _q()
+    # mismatched dtypes
+    assert L.csa_index(ctypes.byref(Q), 0x10, None, 1, 0x20, 8, 64, 0x30, None, 2, 1, 100, 4,
+                       0x40, 100, None) == 1
+    # fp8 without scales
+    assert L.csa_index(ctypes.byref(Q), 0x10, None, 2, 0x20, 8, 64, 0x30, None, 2, 1, 100, 4,
+                       0x40, 100, None) == 1
+    # huge H_I * d_I
+    assert L.csa_index(ctypes.byref(Q), 0x10, None, 0, 0x20, 512, 512, 0x30, None, 0, 1, 100, 4,
+                       0x40, 100, None) == 2
+
+
+def _kv(**kw):
+    base = dict(c=0x100, r=0x200, scale=None, pos0=None, dtype_c=1, d_c=512, d_r=64, rows=10,
+                ld_c=576, ld_r=576)
+    base.update(kw)
+    return lib.KV(**base)
+
+
+def test_attend_validation(L):
+    Q = _q()
+    ent = _kv()
+    raw = _kv()
+    args = lambda e, r, k=4, w=8, q_dt=1: (ctypes.byref(Q), 0x500, q_dt, 64, ctypes.byref(e), 4,
+                                           0x600, k, ctypes.byref(r), w, 0.1, 0x700, None, None,
+                                           0, None)
+    assert L.csa_attend(*args(_kv(scale=0x999), raw)) == 1          # scale on a bf16 store
+    assert L.csa_attend(*args(_kv(dtype_c=2), raw)) == 1            # fp8 store without scale
+    assert L.csa_attend(*args(ent, _kv(d_r=0, r=None))) == 1        # raw dims differ
+    assert L.csa_attend(*args(ent, raw, k=-1)) == 1
+    assert L.csa_attend(*args(ent, raw, q_dt=2)) == 1               # fp8 queries unsupported
+    assert L.csa_attend(*args(_kv(ld_c=100), raw)) == 1             # ld below width
+    assert L.csa_attend(*args(_kv(d_c=2048, ld_c=4096, ld_r=4096), raw)) == 2
+
+
+def test_compress_validation(L):
+    out = lib.KVOut(0x100, 0x200, None, 1, 512, 64, 25, 576, 576)
+    # rows must be T / m
+    assert L.csa_compress(0x10, 0x20, 1, 0x30, 4, 1, 99, 512, 64, None, None, None, 0,
+                          ctypes.byref(lib.KVOut(0x100, 0x200, None, 1, 512, 64, 25, 576, 576)),
+                          None, None) == 1
+    # misaligned x
+    assert L.csa_compress(0x11, 0x20, 1, 0x30, 4, 1, 100, 512, 64, None, None, None, 0,
+                          ctypes.byref(out), None, None) == 2
+    # projection mode with x given
+    assert L.csa_compress(0x10, None, 0, 0x30, 4, 1, 100, 512, 64, 0x40, 0x50, 0x60, 256,
+                          ctypes.byref(out), 0x70, None) == 1
+    # projection mode into an fp8 store is unsupported
+    out8 = lib.KVOut(0x100, 0x200, 0x300, 2, 512, 64, 25, 512, 64)
+    assert L.csa_compress(None, None, 0, 0x30, 4, 1, 100, 512, 64, 0x40, 0x50, 0x60, 256,
+                          ctypes.byref(out8), 0x70, None) == 2

@@ -1,0 +1,132 @@
+"""GPU parity: libcsa (through its C ABI) against the fp64 oracle on seeded inputs.
+
+Scaled-down versions of the five workloads (sizes the oracle finishes in seconds, spanning several
+tiles with ragged tails), each in the workload's own inputs and in a "sharp" variant whose
+attention logits have unit scale, plus edge cases and run-to-run determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_compressed_07_amd import lib
+from long_context_compressed_07_amd.configs import SMALL, SEED_BASE
+from long_context_compressed_07_amd.inputs import make_inputs
+from long_context_compressed_07_amd.layer import Step
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.load()
+
+
+def _run(wl, sharp, seed):
+    host = make_inputs(wl, seed, sharp=sharp)
+    step = Step(wl, host, sm_scale=1.0 if sharp else None)
+    step.run()
+    torch.cuda.synchronize()
+    return host, step
+
+
+def _cfg_seed(cfg):
+    return SEED_BASE[cfg]
+
+
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C4", "C5"])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_csa_layer_small(cfg, sharp):
+    wl = SMALL[cfg]
+    print(f"[parity] {cfg} {wl.name} sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, _cfg_seed(cfg))
+    if wl.compress_on_path:
+        parity.check_compress(wl, host, step)
+    stats = {}
+    parity.check_csa(wl, host, step, stats=stats)
+    if wl.kind == "hybrid_decode":
+        parity.check_hca(wl, host, step, stats=stats)
+    print(stats)
+
+
+@pytest.mark.parametrize("sharp", [False, True])
+def test_hca_prefill_small(sharp):
+    wl = SMALL["C3"]
+    print(f"[parity] C3 {wl.name} sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, _cfg_seed("C3"))
+    parity.check_compress(wl, host, step)
+    stats = {}
+    parity.check_hca(wl, host, step, stats=stats)
+    print(stats)
+
+
+def test_hca_prefill_every_position():
+    # Queries at every position of a short context: n_vis runs from 0 (empty key set) upwards.
+    wl = SMALL["C3"].replace(T=128 * 6 + 50, nq=128 * 6 + 50, H=64)
+    print("[parity] hca every position", flush=True)
+    host, step = _run(wl, False, 11)
+    parity.check_hca(wl, host, step)
+
+
+def test_csa_prefill_ragged_and_small_k():
+    # k larger than most n_vis (padding), a window wider than the early prefixes, T % m != 0.
+    wl = SMALL["C2"].replace(T=4 * 150 + 3, nq=4 * 150 + 3, k=200, window=64)
+    print("[parity] csa prefill ragged", flush=True)
+    host, step = _run(wl, False, 12)
+    parity.check_compress(wl, host, step)
+    parity.check_csa(wl, host, step)
+
+
+def test_csa_window_one_and_k_one():
+    wl = SMALL["C2"].replace(T=4 * 100 + 1, nq=4 * 100 + 1, k=1, window=1)
+    print("[parity] csa k=1 window=1", flush=True)
+    host, step = _run(wl, True, 13)
+    parity.check_csa(wl, host, step)
+
+
+def test_attend_skips_empty_slots():
+    # Selection slots holding -1 in the middle of a row are skipped by csa_attend.
+    wl = SMALL["C4"]
+    print("[parity] attend with -1 holes", flush=True)
+    host, step = _run(wl, False, 14)
+    idx = step.idx.clone()
+    idx[:, 1::3] = -1
+    step.attend(idx)
+    torch.cuda.synchronize()
+    step.idx = idx  # the oracle reads the same holes
+    from oracle import csa_oracle as orc
+    from long_context_compressed_07_amd.inputs import query_positions
+    seq, pos = query_positions(wl)
+    out = step.out.cpu().numpy()
+    for qi in range(seq.size):
+        b = int(seq[qi])
+        o, _ = orc.csa_attend_one(parity.dec(host["q"][qi], "bf16"),
+                                  parity._entry_store(wl, host, step, b), idx[qi].cpu().numpy(),
+                                  parity._raw_store(wl, host, step, b), int(pos[qi]), wl.window,
+                                  step.sm_scale)
+        assert parity.rel_err(out[qi], o) <= 2e-2
+
+
+def test_no_queries_and_no_entries():
+    wl = SMALL["C2"].replace(T=3, nq=0, k=8, window=4)   # T < m: no entries, no queries
+    host = make_inputs(wl, 15)
+    step = Step(wl, host)
+    step.run()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C5"])
+def test_deterministic(cfg):
+    wl = SMALL[cfg]
+    print(f"[parity] determinism {cfg}", flush=True)
+    host, s1 = _run(wl, False, 16)
+    a = [t.clone() for t in parity.outputs(s1)]
+    s1.run()
+    torch.cuda.synchronize()
+    b = parity.outputs(s1)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y)
