@@ -1,0 +1,407 @@
+// MFMA attention kernel for csa_attend / hca_attend on gfx950 (bf16 or fp8 cache rows of
+// d_c = 512 latent + d_r = 64 RoPE dims, bf16 queries, heads in groups of 32).
+//
+// Method: deepseek.csdn.net "一文搞懂 DeepSeek" V4 改进一 (CSA: selected compressed rows plus the
+// raw window, MQA with one KV shared by every head; HCA: dense over the m'-compressed rows) and the
+// MLA section (key row = [latent; RoPE key], value row = latent); yudonglee.me "DeepSeek-V4 详解"
+// 2.2 Step 4 and 2.3 Step 2. The jaylab-temp.pages.dev report (其他技术细节) gives the fp8 latent +
+// bf16 RoPE cache row.
+//
+// Layout of the work. A workgroup is 4 wavefronts and serves one query: HGW groups of 32 heads x
+// KSW splits of that query's key list (HGW * KSW = 4). Keys are staged tile by tile (32 * KSW
+// keys) into LDS as fp16 rows [key][576 + 16 pad], converted exactly from bf16 or from
+// (fp8 code x row scale); every wave then works on its own 32 keys of the tile:
+//   S^T[32 keys x 32 heads] = K_tile . Q^T       36 x mfma_f32_32x32x16_f16, K from LDS
+//                                                 (ds_read_b128), Q^T held in registers
+//   online softmax per head                       each lane owns one head (column of S^T), so
+//                                                 the row max / sum are lane-local plus one
+//                                                 exchange with lane ^ 32; the running max is
+//                                                 only moved when a tile exceeds it by 2^8
+//   O^T[512 x 32 heads] += V^T . P^T              32 x mfma, V^T fragments read transposed from
+//                                                 the same LDS rows (ds_read_tr16_b64), P^T is
+//                                                 the softmax output already in registers
+// The KSW key splits of a head group are merged through LDS at the end (log-sum-exp merge); with
+// n_split > 1 workgroups per query, partial (O, m, l) go to the workspace and combine_kernel
+// merges them.
+//
+// Precision: products in fp16 are exact for these inputs (bf16 and scaled fp8 values lie inside
+// fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
+// rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
+#include "attend_keys.h"
+
+namespace csa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) _Float16 lds_half;
+
+// Transposed LDS read (gfx950 ds_read_tr16_b64): within each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes 4 j + i / 4, j = 0..3.
+__device__ __forceinline__ half4 read_tr16(const lds_half* p) {
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+  return __builtin_bit_cast(half4, v);
+}
+
+constexpr int kDC = 512;                 // latent (value) dims
+constexpr int kDR = 64;                  // RoPE dims
+constexpr int kD = kDC + kDR;            // key dims
+constexpr int kChunks = kD / 8;          // 16-byte fp16 chunks per key row
+constexpr int kRowH = kD + 16;           // LDS row stride in halfs (pad keeps reads conflict-free)
+constexpr int kKSteps = kD / 16;         // k-steps of the S^T contraction
+constexpr int kMT = kDC / 32;            // 32-dim output tiles
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;            // log2 headroom before the running max is moved
+
+struct MfmaPlan {
+  int ksw;            // key splits inside a workgroup
+  int head_groups;    // workgroups per query along heads (each covers 32 * 4 / ksw heads)
+  int n_split;        // workgroups per query along keys
+  float* ws_o;        // [nq][n_split][H][kDC] partial outputs (unnormalised), n_split > 1
+  float* ws_ml;       // [nq][n_split][H][2] partial (max in log2 units, sum)
+};
+
+__device__ __forceinline__ half8 cvt8_bf16(uint4 v) {
+  half8 h;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
+    h[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xffff0000u);
+  }
+  return h;
+}
+
+__device__ __forceinline__ half8 cvt8_e4m3(uint2 v, float s) {
+  half8 h;
+  const int w0 = (int)v.x, w1 = (int)v.y;
+  h[0] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w0, 0) * s);
+  h[1] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w0, 1) * s);
+  h[2] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w0, 2) * s);
+  h[3] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w0, 3) * s);
+  h[4] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w1, 0) * s);
+  h[5] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w1, 1) * s);
+  h[6] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w1, 2) * s);
+  h[7] = (_Float16)(__builtin_amdgcn_cvt_f32_fp8(w1, 3) * s);
+  return h;
+}
+
+// Stage the rows of one tile (32 * KSW keys) into LDS as fp16. s_key holds, per tile key, the
+// store (bit 30) and row, or -1 for an empty slot (written as zeros).
+template <int KVT, int KSW>
+__device__ __forceinline__ void stage_tile(const AttendArgs& a, int64_t b, const int* s_key,
+                                           _Float16* tile) {
+  constexpr int kTasks = 32 * KSW * kChunks;
+#pragma unroll 1
+  for (int t = threadIdx.x; t < kTasks; t += 256) {
+    const int r = t / kChunks;
+    const int c = t - r * kChunks;
+    const int code = s_key[r];
+    half8 h;
+    if (code < 0) {
+      h = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+      const Store& st = (code >> 30) ? a.raw : a.ent;
+      const int64_t row = b * st.rows + (code & 0x3fffffff);
+      if (c < kDC / 8) {
+        if (KVT == CSA_BF16) {
+          const uint16_t* p = static_cast<const uint16_t*>(st.c) + row * st.ld_c + c * 8;
+          h = cvt8_bf16(*reinterpret_cast<const uint4*>(p));
+        } else {
+          const uint8_t* p = static_cast<const uint8_t*>(st.c) + row * st.ld_c + c * 8;
+          h = cvt8_e4m3(*reinterpret_cast<const uint2*>(p), st.scale[row]);
+        }
+      } else {
+        const uint16_t* p = static_cast<const uint16_t*>(st.r) + row * st.ld_r + (c - kDC / 8) * 8;
+        h = cvt8_bf16(*reinterpret_cast<const uint4*>(p));
+      }
+    }
+    *reinterpret_cast<half8*>(tile + r * kRowH + c * 8) = h;
+  }
+}
+
+template <int KVT, int KSW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
+  constexpr int HGW = 4 / KSW;
+  constexpr int kTileBytes = 32 * KSW * kRowH * 2;
+  constexpr int kMergeBytes = KSW > 1 ? (KSW / 2) * HGW * (kMT * 16 + 2) * 64 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char lds[kTileBytes > kMergeBytes ? kTileBytes
+                                                                             : kMergeBytes];
+  __shared__ int s_key[32 * KSW];
+  _Float16* tile = reinterpret_cast<_Float16*>(lds);
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hgw = w % HGW;
+  const int ks = w / HGW;
+  const int hi = lane >> 5;                       // lane half
+  const int per_q = plan.head_groups * plan.n_split;
+  const int qi = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qi * per_q;
+  const int hgrp = rem / plan.n_split;
+  const int split = rem - hgrp * plan.n_split;
+  const int h0 = (hgrp * HGW + hgw) * 32;
+  const int head = h0 + (lane & 31);
+
+  const KeyList kl = make_key_list(a, qi);
+  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
+  const int64_t kb = (int64_t)split * per_split;
+  const int64_t ke = kb + per_split < kl.total ? kb + per_split : kl.total;
+
+  // Q^T operand fragments: head `head`, dims 16 s + 8 hi + [0, 8).
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + head) * kD;
+  half8 qb[kKSteps];
+#pragma unroll
+  for (int s = 0; s < kKSteps; ++s)
+    qb[s] = cvt8_bf16(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hi));
+
+  floatx16 o[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) o[mt] = floatx16{};
+  float m_run = -INFINITY;   // running max of the scaled logits (log2 units), per head
+  float l_run = 0.f;         // running sum of this lane's half of the keys
+  const float cscale = a.sm_scale * kLog2e;
+
+  const _Float16* wtile = tile + (32 * ks) * kRowH;        // this wave's 32 keys
+  for (int64_t t0 = kb; t0 < ke; t0 += 32 * KSW) {
+    if (threadIdx.x < 32 * KSW) {
+      const int64_t kk = t0 + threadIdx.x;
+      int code = -1;
+      if (kk < ke) {
+        int src;
+        const int64_t row = key_row(a, kl, kk, src);
+        if (row >= 0) code = (int)row | (src << 30);
+      }
+      s_key[threadIdx.x] = code;
+    }
+    __syncthreads();
+    stage_tile<KVT, KSW>(a, kl.b, s_key, tile);
+    __syncthreads();
+
+    // S^T = K . Q^T for this wave's 32 keys.
+    floatx16 acc = floatx16{};
+    const _Float16* arow = wtile + (lane & 31) * kRowH + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+      const half8 av = *reinterpret_cast<const half8*>(arow + 16 * s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qb[s], acc, 0, 0, 0);
+    }
+    // Scale, mask empty slots, tile max per head.
+    float x[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 32 * ks + 8 * (i >> 2) + 4 * hi + (i & 3);
+      x[i] = s_key[key] >= 0 ? acc[i] * cscale : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy rescale: the running max moves only when some head of the wave gains more than
+    // 2^kLazy. Until the first finite max the accumulators are zero and the max is just set.
+    // A real rescale is rare; on that path the Q^T fragments are reloaded afterwards, so their
+    // registers are free while the accumulators pass through VGPRs.
+    if (__any(m_run == -INFINITY)) {
+      m_run = m_run == -INFINITY ? tmax : m_run;
+    }
+    if (__any(tmax > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) o[mt] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        qb[s] = cvt8_bf16(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hi));
+    }
+    // P^T in fp16, already in the B-operand layout of the next contraction: k-step s of lane
+    // half hi covers keys 16 s + 4 hi + [0,4) and 16 s + 8 + 4 hi + [0,4).
+    half8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_run);
+      const _Float16 ph = (_Float16)p;
+      l_run += (float)ph;
+      pb[i >> 3][i & 7] = ph;
+    }
+    // O^T += V^T . P^T; V^T fragments come transposed from the fp16 rows.
+    const int g = lane >> 4;
+    const int la = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      const int col = 32 * mt + 16 * (g & 1) + 4 * (la & 3);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int r0 = 16 * s + 4 * hi + (la >> 2);
+        const lds_half* base = (const lds_half*)wtile;
+        const half4 v0 = read_tr16(base + r0 * kRowH + col);
+        const half4 v1 = read_tr16(base + (r0 + 8) * kRowH + col);
+        const half8 av = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[s], o[mt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Both lane halves hold the same head; their sums cover different keys.
+  l_run += __shfl_xor(l_run, 32);
+
+  // Merge the KSW key splits of each head group through LDS (lane-local log-sum-exp merge).
+  if (KSW > 1) {
+    float* xo = reinterpret_cast<float*>(lds);      // per slot: [kMT*16 + 2][64] floats
+    for (int span = KSW / 2; span >= 1; span >>= 1) {
+      // waves with ks in [span, 2 span) send to ks - span.
+      const bool sender = ks >= span && ks < 2 * span;
+      const bool receiver = ks < span;
+      float* slot = xo + (size_t)((ks % span) * HGW + hgw) * (kMT * 16 + 2) * 64;
+      if (sender) {
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) slot[(mt * 16 + i) * 64 + lane] = o[mt][i];
+        slot[(kMT * 16) * 64 + lane] = m_run;
+        slot[(kMT * 16 + 1) * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (receiver) {
+        const float m2 = slot[(kMT * 16) * 64 + lane];
+        const float l2 = slot[(kMT * 16 + 1) * 64 + lane];
+        const float mm = fmaxf(m_run, m2);
+        const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
+        const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mm);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            o[mt][i] = o[mt][i] * a1 + slot[(mt * 16 + i) * 64 + lane] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_run = mm;
+      }
+      __syncthreads();
+    }
+  }
+  if (ks != 0) return;
+
+  // Output rows: lane owns head `head`, dims 32 mt + 8 j + 4 hi + [0, 4).
+  if (plan.n_split == 1) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    float* orow = a.out + ((int64_t)qi * a.H + head) * kDC;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 v = make_float4(o[mt][4 * j] * inv, o[mt][4 * j + 1] * inv,
+                               o[mt][4 * j + 2] * inv, o[mt][4 * j + 3] * inv);
+        *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) = v;
+      }
+    if (a.lse != nullptr && hi == 0)
+      a.lse[(int64_t)qi * a.H + head] =
+          l_run > 0.f ? (m_run + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  } else {
+    const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
+    float* orow = plan.ws_o + pidx * kDC;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
+            make_float4(o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]);
+    if (hi == 0) {
+      plan.ws_ml[pidx * 2] = m_run;
+      plan.ws_ml[pidx * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Log-sum-exp merge of n_split partials: one block per (query, head), one thread per 4 dims.
+__global__ void __launch_bounds__(128) combine_kernel(AttendArgs a, MfmaPlan plan) {
+  const int qi = blockIdx.x / a.H;
+  const int head = blockIdx.x - qi * a.H;
+  float mx = -INFINITY;
+  for (int s = 0; s < plan.n_split; ++s)
+    mx = fmaxf(mx, plan.ws_ml[(((int64_t)qi * plan.n_split + s) * a.H + head) * 2]);
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int d0 = threadIdx.x * 4;
+  for (int s = 0; s < plan.n_split; ++s) {
+    const int64_t pidx = ((int64_t)qi * plan.n_split + s) * a.H + head;
+    const float m = plan.ws_ml[pidx * 2];
+    if (m == -INFINITY) continue;
+    const float wgt = exp2f(m - mx);
+    lsum += wgt * plan.ws_ml[pidx * 2 + 1];
+    const float4 v = *reinterpret_cast<const float4*>(plan.ws_o + pidx * kDC + d0);
+    acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  *reinterpret_cast<float4*>(a.out + ((int64_t)qi * a.H + head) * kDC + d0) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (a.lse != nullptr && threadIdx.x == 0)
+    a.lse[(int64_t)qi * a.H + head] =
+        lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+}
+
+MfmaPlan make_plan(int nq, int H, int64_t max_keys) {
+  MfmaPlan p{};
+  const int groups32 = H / 32;
+  if ((int64_t)nq * ((groups32 + 3) / 4) >= 512 && groups32 % 4 == 0) {
+    p.ksw = 1;                    // prefill, 128 heads: 4 head groups share each tile
+    p.head_groups = groups32 / 4;
+    p.n_split = 1;
+  } else if ((int64_t)nq * (groups32 / 2) >= 512 && groups32 % 2 == 0) {
+    p.ksw = 2;                    // prefill, 64 heads: 2 head groups x 2 key halves
+    p.head_groups = groups32 / 2;
+    p.n_split = 1;
+  } else {
+    p.ksw = 4;                    // decode: one head group per workgroup, 4 key quarters
+    p.head_groups = groups32;
+    const int64_t wgs = (int64_t)nq * groups32;
+    int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
+    const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
+    p.n_split = (int)(ns < cap ? ns : cap);
+  }
+  return p;
+}
+
+}  // namespace
+
+bool attend_mfma_supported(const AttendArgs& a) {
+  return a.q_dtype == CSA_BF16 && (a.ent.dtype == CSA_BF16 || a.ent.dtype == CSA_E4M3) &&
+         a.ent.d_c == kDC && a.ent.d_r == kDR && a.H % 32 == 0 &&
+         (a.ent.ld_c % 8 == 0) && (a.ent.ld_r % 8 == 0) &&
+         (a.dense || a.window == 0 || (a.raw.ld_c % 8 == 0 && a.raw.ld_r % 8 == 0)) &&
+         a.ent.rows < (1 << 30) && (a.dense || a.raw.rows < (1 << 30));
+}
+
+size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
+  const MfmaPlan p = make_plan(nq, H, max_keys);
+  if (p.n_split <= 1) return 0;
+  return (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float);
+}
+
+hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
+  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys);
+  if (p.n_split > 1) {
+    p.ws_o = static_cast<float*>(a.ws);
+    p.ws_ml = p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC;
+  }
+  const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
+  const bool fp8 = a.ent.dtype == CSA_E4M3;
+  switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
+    case 2: attend_mfma_kernel<CSA_BF16, 1><<<grid, 256, 0, s>>>(a, p); break;
+    case 3: attend_mfma_kernel<CSA_E4M3, 1><<<grid, 256, 0, s>>>(a, p); break;
+    case 4: attend_mfma_kernel<CSA_BF16, 2><<<grid, 256, 0, s>>>(a, p); break;
+    case 5: attend_mfma_kernel<CSA_E4M3, 2><<<grid, 256, 0, s>>>(a, p); break;
+    case 8: attend_mfma_kernel<CSA_BF16, 4><<<grid, 256, 0, s>>>(a, p); break;
+    default: attend_mfma_kernel<CSA_E4M3, 4><<<grid, 256, 0, s>>>(a, p); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split <= 1) return e;
+  combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kDC / 4, 0, s>>>(a, p);
+  return hipGetLastError();
+}
+
+}  // namespace csa

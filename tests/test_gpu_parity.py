@@ -130,3 +130,35 @@ def test_deterministic(cfg):
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
                            y.view(torch.uint8) if y.dtype != torch.uint8 else y)
+
+
+def test_hca_prefill_128_heads_many_queries():
+    # >= 512 queries of 128 heads: four 32-head groups share every staged key tile.
+    wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=640, H=128)
+    print("[parity] hca 128 heads x 640 queries", flush=True)
+    host, step = _run(wl, True, 17)
+    parity.check_hca(wl, host, step)
+
+
+def test_hca_few_queries_many_entries_split():
+    # Few queries over many entries: several workgroups per query along the key list, merged by
+    # the log-sum-exp combine kernel.
+    wl = SMALL["C3"].replace(m=16, T=16 * 2300 + 5, nq=3, H=128)
+    print("[parity] hca key splits", flush=True)
+    for sharp in (False, True):
+        host, step = _run(wl, sharp, 18)
+        parity.check_hca(wl, host, step)
+
+
+def test_attend_mfma_matches_generic_kernel(monkeypatch):
+    # The MFMA kernel against the fp32 reference kernel on identical inputs (fp8 decode).
+    wl = SMALL["C5"]
+    host, step = _run(wl, True, 19)
+    fast = (step.out.clone(), step.hca_out.clone())
+    monkeypatch.setenv("CSA_ATTEND_KERNEL", "generic")
+    step.attend()
+    step.hca()
+    torch.cuda.synchronize()
+    for f, g in zip(fast, (step.out, step.hca_out)):
+        err = (f - g).abs().max().item() / g.abs().max().item()
+        assert err < 2e-3, err
