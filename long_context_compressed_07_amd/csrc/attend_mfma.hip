@@ -13,10 +13,16 @@
 // (fp8 code x row scale); every wave then works on its own 32 keys of the tile:
 //   S^T[32 keys x 32 heads] = K_tile . Q^T       36 x mfma_f32_32x32x16_f16, K from LDS
 //                                                 (ds_read_b128), Q^T held in registers
-//   online softmax per head                       each lane owns one head (column of S^T), so
+//   softmax per head                              each lane owns one head (column of S^T), so
 //                                                 the row max / sum are lane-local plus one
-//                                                 exchange with lane ^ 32; the running max is
-//                                                 only moved when a tile exceeds it by 2^8
+//                                                 exchange with lane ^ 32. The reference max of
+//                                                 a head is fixed at its first non-empty tile;
+//                                                 later tiles may reach 2^15 above it (fp16 P
+//                                                 range), so the accumulators are never rescaled
+//                                                 inside the loop. A head that would exceed the
+//                                                 range flags its workgroup, and fixup_kernel
+//                                                 recomputes the flagged queries with the fp32
+//                                                 reference code.
 //   O^T[512 x 32 heads] += V^T . P^T              32 x mfma, V^T fragments read transposed from
 //                                                 the same LDS rows (ds_read_tr16_b64), P^T is
 //                                                 the softmax output already in registers
@@ -27,7 +33,7 @@
 // Precision: products in fp16 are exact for these inputs (bf16 and scaled fp8 values lie inside
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
 // rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
-#include "attend_keys.h"
+#include "attend_generic.h"
 
 namespace csa {
 namespace {
@@ -54,7 +60,7 @@ constexpr int kRowH = kD + 16;           // LDS row stride in halfs (pad keeps r
 constexpr int kKSteps = kD / 16;         // k-steps of the S^T contraction
 constexpr int kMT = kDC / 32;            // 32-dim output tiles
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;            // log2 headroom before the running max is moved
+constexpr float kRange = 15.0f;          // log2 headroom of P above the reference max (fp16)
 
 struct MfmaPlan {
   int ksw;            // key splits inside a workgroup
@@ -62,6 +68,7 @@ struct MfmaPlan {
   int n_split;        // workgroups per query along keys
   float* ws_o;        // [nq][n_split][H][kDC] partial outputs (unnormalised), n_split > 1
   float* ws_ml;       // [nq][n_split][H][2] partial (max in log2 units, sum)
+  int* flags;         // [nq][head_groups][n_split] 1 = a head left the fp16 range of P
 };
 
 __device__ __forceinline__ half8 cvt8_bf16(uint4 v) {
@@ -132,7 +139,9 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   __shared__ __attribute__((aligned(16))) char lds[kTileBytes > kMergeBytes ? kTileBytes
                                                                              : kMergeBytes];
   __shared__ int s_key[32 * KSW];
+  __shared__ int s_flag;
   _Float16* tile = reinterpret_cast<_Float16*>(lds);
+  if (threadIdx.x == 0) s_flag = 0;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -162,8 +171,9 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   floatx16 o[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) o[mt] = floatx16{};
-  float m_run = -INFINITY;   // running max of the scaled logits (log2 units), per head
+  float m_run = -INFINITY;   // reference max of the scaled logits (log2 units), per head
   float l_run = 0.f;         // running sum of this lane's half of the keys
+  bool overflow = false;
   const float cscale = a.sm_scale * kLog2e;
 
   const _Float16* wtile = tile + (32 * ks) * kRowH;        // this wave's 32 keys
@@ -190,40 +200,26 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
       const half8 av = *reinterpret_cast<const half8*>(arow + 16 * s);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qb[s], acc, 0, 0, 0);
     }
-    // Scale, mask empty slots, tile max per head.
-    float x[16];
+    // Scale, mask empty slots, tile max per head (lane-local over 16 keys, then lane ^ 32).
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 32 * ks + 8 * (i >> 2) + 4 * hi + (i & 3);
-      x[i] = s_key[key] >= 0 ? acc[i] * cscale : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
+      acc[i] = s_key[key] >= 0 ? acc[i] * cscale : -INFINITY;
+      tmax = fmaxf(tmax, acc[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // Lazy rescale: the running max moves only when some head of the wave gains more than
-    // 2^kLazy. Until the first finite max the accumulators are zero and the max is just set.
-    // A real rescale is rare; on that path the Q^T fragments are reloaded afterwards, so their
-    // registers are free while the accumulators pass through VGPRs.
-    if (__any(m_run == -INFINITY)) {
-      m_run = m_run == -INFINITY ? tmax : m_run;
-    }
-    if (__any(tmax > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) o[mt] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        qb[s] = cvt8_bf16(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hi));
-    }
+    // The reference max is set by the first non-empty tile (the accumulators are still zero
+    // then); afterwards it never moves and P may reach 2^kRange. A head that would exceed that
+    // marks the workgroup for the fp32 fixup pass.
+    m_run = m_run == -INFINITY ? tmax : m_run;
+    overflow |= tmax > m_run + kRange;
     // P^T in fp16, already in the B-operand layout of the next contraction: k-step s of lane
     // half hi covers keys 16 s + 4 hi + [0,4) and 16 s + 8 + 4 hi + [0,4).
     half8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_run);
+      const float p = acc[i] == -INFINITY ? 0.f : exp2f(fminf(acc[i] - m_run, kRange));
       const _Float16 ph = (_Float16)p;
       l_run += (float)ph;
       pb[i >> 3][i & 7] = ph;
@@ -249,6 +245,7 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
 
   // Both lane halves hold the same head; their sums cover different keys.
   l_run += __shfl_xor(l_run, 32);
+  if (__any(overflow)) atomicOr(&s_flag, 1);
 
   // Merge the KSW key splits of each head group through LDS (lane-local log-sum-exp merge).
   if (KSW > 1) {
@@ -274,16 +271,20 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
         const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
         const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mm);
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
+        for (int mt = 0; mt < kMT; ++mt) {
+          floatx16 other;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            o[mt][i] = o[mt][i] * a1 + slot[(mt * 16 + i) * 64 + lane] * a2;
+          for (int i = 0; i < 16; ++i) other[i] = slot[(mt * 16 + i) * 64 + lane];
+          o[mt] = o[mt] * a1 + other * a2;
+        }
         l_run = l_run * a1 + l2 * a2;
         m_run = mm;
       }
       __syncthreads();
     }
   }
+  __syncthreads();
+  if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
   if (ks != 0) return;
 
   // Output rows: lane owns head `head`, dims 32 mt + 8 j + 4 hi + [0, 4).
@@ -344,6 +345,24 @@ __global__ void __launch_bounds__(128) combine_kernel(AttendArgs a, MfmaPlan pla
         lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
+// Recompute, with the fp32 reference code, every query one of whose workgroups flagged a head
+// whose logits left the fp16 range of P. Nearly always a no-op scan of the flags.
+__global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPlan plan) {
+  __shared__ float smem[generic_smem_bytes(kD) / sizeof(float)];
+  __shared__ int s_any;
+  const int per_q = plan.head_groups * plan.n_split;
+  for (int qi = blockIdx.x; qi < a.Q.nq; qi += gridDim.x) {
+    if (threadIdx.x == 0) s_any = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < per_q; i += kGenThreads)
+      if (plan.flags[(int64_t)qi * per_q + i]) s_any = 1;
+    __syncthreads();
+    if (s_any)
+      for (int h = 0; h < a.H; ++h) attend_generic_one(a, qi, h, smem);
+    __syncthreads();
+  }
+}
+
 MfmaPlan make_plan(int nq, int H, int64_t max_keys) {
   MfmaPlan p{};
   const int groups32 = H / 32;
@@ -376,18 +395,23 @@ bool attend_mfma_supported(const AttendArgs& a) {
          a.ent.rows < (1 << 30) && (a.dense || a.raw.rows < (1 << 30));
 }
 
+// Workspace: partial outputs when a query spans several workgroups, then one flag per workgroup.
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
   const MfmaPlan p = make_plan(nq, H, max_keys);
-  if (p.n_split <= 1) return 0;
-  return (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float);
+  const size_t partial =
+      p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float) : 0;
+  return partial + (size_t)nq * p.head_groups * p.n_split * sizeof(int);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
   MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys);
+  size_t off = 0;
   if (p.n_split > 1) {
     p.ws_o = static_cast<float*>(a.ws);
     p.ws_ml = p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC;
+    off = (size_t)a.Q.nq * p.n_split * a.H * (kDC + 2) * sizeof(float);
   }
+  p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + off);
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   const bool fp8 = a.ent.dtype == CSA_E4M3;
   switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
@@ -399,8 +423,13 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
     default: attend_mfma_kernel<CSA_E4M3, 4><<<grid, 256, 0, s>>>(a, p); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split <= 1) return e;
-  combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kDC / 4, 0, s>>>(a, p);
+  if (e != hipSuccess) return e;
+  if (p.n_split > 1) {
+    combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kDC / 4, 0, s>>>(a, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int fx = a.Q.nq < 1024 ? a.Q.nq : 1024;
+  fixup_kernel<<<fx, kGenThreads, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

@@ -45,8 +45,12 @@ __global__ void __launch_bounds__(256) index_generic_kernel(IndexArgs a, int til
 
 }  // namespace
 
+bool index_fast(const IndexArgs& a, hipStream_t s, hipError_t* err);
+
 hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
   if (a.Q.nq == 0 || a.N == 0) return hipSuccess;
+  hipError_t err;
+  if (index_fast(a, s, &err)) return err;
   const int tiles = (int)((a.N + 255) / 256);
   const size_t shm = sizeof(float) * ((size_t)a.H_I * a.d_I + a.H_I);
   index_generic_kernel<<<(unsigned)((int64_t)tiles * a.Q.nq), 256, shm, s>>>(a, tiles);

@@ -8,6 +8,8 @@
 // most-significant-digit radix select (4 passes of 8 bits, LDS histograms) finds the k-th largest
 // key K and how many entries equal to K are still needed; a final in-order pass keeps every key
 // > K and the lowest-index keys == K, compacted with wavefront ballots and a block scan.
+#include <atomic>
+
 #include "common.h"
 
 namespace csa {
@@ -41,7 +43,10 @@ __device__ __forceinline__ int block_excl_scan(bool flag, int* s_wave, int& tota
   return before + in_wave;
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_block_kernel(TopkArgs a) {
+// One workgroup per query row. When the row fits (cache_cap keys), its keys are copied once into
+// dynamic LDS and every pass reads LDS; otherwise the passes re-read the scores.
+__global__ void __launch_bounds__(kTopkThreads) topk_block_kernel(TopkArgs a, int cache_cap) {
+  extern __shared__ uint32_t s_keys[];
   __shared__ int s_hist[256];
   __shared__ int s_wave[kTopkThreads / kWave];
   __shared__ int s_sel[2];
@@ -54,6 +59,11 @@ __global__ void __launch_bounds__(kTopkThreads) topk_block_kernel(TopkArgs a) {
     for (int i = tid; i < a.k; i += kTopkThreads) out[i] = i < nv ? i : -1;
     return;
   }
+  const bool cached = nv <= cache_cap;
+  if (cached) {
+    for (int64_t j = tid; j < nv; j += kTopkThreads) s_keys[j] = score_key(row[j]);
+  }
+  auto key_at = [&](int64_t j) -> uint32_t { return cached ? s_keys[j] : score_key(row[j]); };
   uint32_t prefix = 0, pmask = 0;
   int remaining = a.k;
   for (int pass = 0; pass < 4; ++pass) {
@@ -61,7 +71,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_block_kernel(TopkArgs a) {
     for (int i = tid; i < 256; i += kTopkThreads) s_hist[i] = 0;
     __syncthreads();
     for (int64_t j = tid; j < nv; j += kTopkThreads) {
-      const uint32_t key = score_key(row[j]);
+      const uint32_t key = key_at(j);
       if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
     }
     __syncthreads();
@@ -84,7 +94,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_block_kernel(TopkArgs a) {
   int emitted = 0, eq_seen = 0;
   for (int64_t c0 = 0; c0 < nv; c0 += kTopkThreads) {
     const int64_t j = c0 + tid;
-    const uint32_t key = j < nv ? score_key(row[j]) : 0u;
+    const uint32_t key = j < nv ? key_at(j) : 0u;
     const bool gt = j < nv && key > prefix;
     const bool eq = j < nv && key == prefix;
     int eq_total, take_total;
@@ -104,7 +114,22 @@ size_t topk_workspace(int /*nq*/, int64_t /*N*/, int /*k*/) { return 0; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.Q.nq == 0) return hipSuccess;
-  topk_block_kernel<<<a.Q.nq, kTopkThreads, 0, s>>>(a);
+  constexpr int kMaxCache = 32768;                 // keys (128 KiB of LDS)
+  // Dynamic LDS above 64 KiB needs a per-device opt-in; remember it per device (thread-safe).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_block_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxCache * (int)sizeof(uint32_t));
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  const int cap = a.N < kMaxCache ? (int)a.N : kMaxCache;
+  topk_block_kernel<<<a.Q.nq, kTopkThreads, (size_t)cap * sizeof(uint32_t), s>>>(a, cap);
   return hipGetLastError();
 }
 

@@ -144,8 +144,10 @@ def run(wl, host: dict, cores: int, budget_s: float, seed: int = 0) -> dict:
         if decode:
             sample = np.arange(nq)
         else:
-            # Probe the per-query cost, then size the sample to the time budget.
-            probe = rng.choice(nq, size=min(nq, cores), replace=False)
+            # Probe the per-query cost (after one untimed round), then size the sample to the
+            # time budget.
+            list(ex.map(_query, rng.choice(nq, size=min(nq, cores), replace=False)))
+            probe = rng.choice(nq, size=min(nq, 4 * cores), replace=False)
             t = time.perf_counter()
             list(ex.map(_query, probe))
             t_probe = (time.perf_counter() - t) / len(probe) * cores
