@@ -96,38 +96,71 @@ __device__ __forceinline__ half8 cvt8_e4m3(uint2 v, float s) {
   return h;
 }
 
-// Stage the rows of one tile (32 * KSW keys) into LDS as fp16. s_key holds, per tile key, the
-// store (bit 30) and row, or -1 for an empty slot (written as zeros).
-template <int KVT, int KSW>
-__device__ __forceinline__ void stage_tile(const AttendArgs& a, int64_t b, const int* s_key,
-                                           _Float16* tile) {
-  constexpr int kTasks = 32 * KSW * kChunks;
-#pragma unroll 1
-  for (int t = threadIdx.x; t < kTasks; t += 256) {
-    const int r = t / kChunks;
-    const int c = t - r * kChunks;
-    const int code = s_key[r];
-    half8 h;
-    if (code < 0) {
-      h = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    } else {
-      const Store& st = (code >> 30) ? a.raw : a.ent;
-      const int64_t row = b * st.rows + (code & 0x3fffffff);
-      if (c < kDC / 8) {
-        if (KVT == CSA_BF16) {
-          const uint16_t* p = static_cast<const uint16_t*>(st.c) + row * st.ld_c + c * 8;
-          h = cvt8_bf16(*reinterpret_cast<const uint4*>(p));
-        } else {
-          const uint8_t* p = static_cast<const uint8_t*>(st.c) + row * st.ld_c + c * 8;
-          h = cvt8_e4m3(*reinterpret_cast<const uint2*>(p), st.scale[row]);
-        }
+// Staging of a key tile (32 * KSW keys) into LDS as fp16, in batches of 32 keys. In a batch,
+// thread t owns key row t / 8 and its 16-byte chunks 9 (t % 8) .. 9 (t % 8) + 8 (of the 72 chunks
+// of a 576-dim row: 64 latent chunks, then 8 RoPE chunks), so it needs one row address and nine
+// loads, all in flight at once. batch_load only issues the loads; batch_store converts and writes.
+// s_key holds, per tile key, the store (bit 30) and row, or -1 for an empty slot (zeros).
+constexpr int kBatch = kChunks / 8;   // 9 chunks per thread
+
+struct Batch {
+  uint4 v[kBatch];
+  float sc;
+};
+
+template <int KVT>
+__device__ __forceinline__ void batch_load(const AttendArgs& a, int64_t b, const int* s_key,
+                                           int bi, Batch& B) {
+  const int r = 32 * bi + (threadIdx.x >> 3);
+  const int c0 = kBatch * (threadIdx.x & 7);
+  const int code = s_key[r];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) B.v[j] = make_uint4(0u, 0u, 0u, 0u);
+  B.sc = 0.f;
+  if (code < 0) return;
+  const Store& st = (code >> 30) ? a.raw : a.ent;
+  const int64_t row = b * st.rows + (code & 0x3fffffff);
+  const char* crow = static_cast<const char*>(st.c) + row * st.ld_c * (KVT == CSA_BF16 ? 2 : 1);
+  const char* rrow = static_cast<const char*>(st.r) + row * st.ld_r * 2;
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int c = c0 + j;
+    if (c < kDC / 8) {
+      if (KVT == CSA_BF16) {
+        B.v[j] = *reinterpret_cast<const uint4*>(crow + c * 16);
       } else {
-        const uint16_t* p = static_cast<const uint16_t*>(st.r) + row * st.ld_r + (c - kDC / 8) * 8;
-        h = cvt8_bf16(*reinterpret_cast<const uint4*>(p));
+        const uint2 u = *reinterpret_cast<const uint2*>(crow + c * 8);
+        B.v[j].x = u.x;
+        B.v[j].y = u.y;
       }
+    } else {
+      B.v[j] = *reinterpret_cast<const uint4*>(rrow + (c - kDC / 8) * 16);
     }
+  }
+  if (KVT == CSA_E4M3) B.sc = st.scale[row];
+}
+
+template <int KVT>
+__device__ __forceinline__ void batch_store(const Batch& B, int bi, _Float16* tile) {
+  const int r = 32 * bi + (threadIdx.x >> 3);
+  const int c0 = kBatch * (threadIdx.x & 7);
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int c = c0 + j;
+    const half8 h = (KVT == CSA_E4M3 && c < kDC / 8)
+                        ? cvt8_e4m3(make_uint2(B.v[j].x, B.v[j].y), B.sc)
+                        : cvt8_bf16(B.v[j]);
     *reinterpret_cast<half8*>(tile + r * kRowH + c * 8) = h;
   }
+}
+
+// Code of key kk of the query's key list for s_key: row | store << 30, or -1.
+__device__ __forceinline__ int key_code(const AttendArgs& a, const KeyList& kl, int64_t kk,
+                                        int64_t ke) {
+  if (kk >= ke) return -1;
+  int src;
+  const int64_t row = key_row(a, kl, kk, src);
+  return row >= 0 ? (int)row | (src << 30) : -1;
 }
 
 template <int KVT, int KSW>
@@ -138,7 +171,7 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   constexpr int kMergeBytes = KSW > 1 ? (KSW / 2) * HGW * (kMT * 16 + 2) * 64 * 4 : 0;
   __shared__ __attribute__((aligned(16))) char lds[kTileBytes > kMergeBytes ? kTileBytes
                                                                              : kMergeBytes];
-  __shared__ int s_key[32 * KSW];
+  __shared__ int s_key[2][32 * KSW];
   __shared__ int s_flag;
   _Float16* tile = reinterpret_cast<_Float16*>(lds);
   if (threadIdx.x == 0) s_flag = 0;
@@ -177,20 +210,31 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   const float cscale = a.sm_scale * kLog2e;
 
   const _Float16* wtile = tile + (32 * ks) * kRowH;        // this wave's 32 keys
-  for (int64_t t0 = kb; t0 < ke; t0 += 32 * KSW) {
-    if (threadIdx.x < 32 * KSW) {
-      const int64_t kk = t0 + threadIdx.x;
-      int code = -1;
-      if (kk < ke) {
-        int src;
-        const int64_t row = key_row(a, kl, kk, src);
-        if (row >= 0) code = (int)row | (src << 30);
-      }
-      s_key[threadIdx.x] = code;
+  constexpr int TK = 32 * KSW;                              // keys per tile
+  // Prologue: codes of tiles 0 and 1, tile 0 staged.
+  if (threadIdx.x < TK) {
+    s_key[0][threadIdx.x] = key_code(a, kl, kb + threadIdx.x, ke);
+    s_key[1][threadIdx.x] = key_code(a, kl, kb + TK + threadIdx.x, ke);
+  }
+  __syncthreads();
+  if (kb < ke) {
+#pragma unroll
+    for (int bi = 0; bi < KSW; ++bi) {
+      Batch B;
+      batch_load<KVT>(a, kl.b, s_key[0], bi, B);
+      batch_store<KVT>(B, bi, tile);
     }
-    __syncthreads();
-    stage_tile<KVT, KSW>(a, kl.b, s_key, tile);
-    __syncthreads();
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int64_t t0 = kb; t0 < ke; t0 += TK) {
+    const bool has_next = t0 + TK < ke;
+    // Prefetch: the first 32 keys of the next tile (registers) and the codes of the tile after.
+    Batch pre;
+    if (has_next) batch_load<KVT>(a, kl.b, s_key[cur ^ 1], 0, pre);
+    int code2 = -1;
+    if (threadIdx.x < TK) code2 = key_code(a, kl, t0 + 2 * TK + threadIdx.x, ke);
+    const int* keys = s_key[cur];
 
     // S^T = K . Q^T for this wave's 32 keys.
     floatx16 acc = floatx16{};
@@ -205,7 +249,7 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 32 * ks + 8 * (i >> 2) + 4 * hi + (i & 3);
-      acc[i] = s_key[key] >= 0 ? acc[i] * cscale : -INFINITY;
+      acc[i] = keys[key] >= 0 ? acc[i] * cscale : -INFINITY;
       tmax = fmaxf(tmax, acc[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -240,7 +284,19 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[s], o[mt], 0, 0, 0);
       }
     }
+    __syncthreads();   // every wave is done with this tile and its codes
+    if (has_next) {
+      batch_store<KVT>(pre, 0, tile);
+#pragma unroll
+      for (int bi = 1; bi < KSW; ++bi) {
+        Batch B;
+        batch_load<KVT>(a, kl.b, s_key[cur ^ 1], bi, B);
+        batch_store<KVT>(B, bi, tile);
+      }
+    }
+    if (threadIdx.x < TK) s_key[cur][threadIdx.x] = code2;
     __syncthreads();
+    cur ^= 1;
   }
 
   // Both lane halves hold the same head; their sums cover different keys.
