@@ -136,6 +136,8 @@ csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scor
   if (csa_status st = check_queries(Q)) return st;
   if (k < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
   if (Q->nq > 0 && (scores == nullptr || idx == nullptr)) return fail(CSA_EINVAL, "null scores/idx");
+  if (!csa::topk_supported(N, k))
+    return fail(CSA_EUNSUPPORTED, "rows longer than 8192 need k <= 2048 and N * k <= 2^28");
   const size_t need = csa::topk_workspace(Q->nq, N, k);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
   csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, ld_scores, N, m, k, idx, ws, ws_bytes};

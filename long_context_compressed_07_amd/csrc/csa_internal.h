@@ -87,6 +87,7 @@ struct TopkArgs {
   size_t ws_bytes;
 };
 size_t topk_workspace(int nq, int64_t N, int k);
+bool topk_supported(int64_t N, int k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // ---- attention -----------------------------------------------------------------------------

@@ -162,3 +162,30 @@ def test_attend_mfma_matches_generic_kernel(monkeypatch):
     for f, g in zip(fast, (step.out, step.hca_out)):
         err = (f - g).abs().max().item() / g.abs().max().item()
         assert err < 2e-3, err
+
+
+@pytest.mark.parametrize("N,k", [(40000, 1024), (40000, 2048), (20000, 1), (9000, 700),
+                                 (8192, 1024), (5000, 96)])
+def test_topk_exact_with_ties_and_long_rows(N, k):
+    # Top-k on identical fp32 scores is integer work: bit-exact against the oracle, including
+    # heavy ties (coarse score values, -0.0 vs +0.0) and rows longer than one chunk.
+    from oracle import csa_oracle as orc
+    rng = np.random.default_rng(N + k)
+    nq, m = 6, 4
+    pos = np.array([0, 4 * 50 - 1, 4 * min(N, k) + 2, 4 * N - 5, 4 * N + 100, 4 * (N // 2)],
+                   dtype=np.int64)
+    seq = np.zeros(nq, dtype=np.int32)
+    sc = np.round(rng.standard_normal((nq, N)) * 4) / 4
+    sc[1, ::7] = -0.0
+    sc[2, :] = 0.0
+    scores = torch.tensor(sc, dtype=torch.float32, device="cuda")
+    idx = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+    lib.csa_topk(torch.tensor(seq, device="cuda"), torch.tensor(pos, device="cuda"), scores,
+                 idx, N, m, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    s64 = scores.cpu().numpy().astype(np.float64)
+    for q in range(nq):
+        nv = orc.n_visible(int(pos[q]), m, N)
+        want, _ = orc.topk(s64[q], nv, k)
+        assert (got[q] == want).all(), (q, nv)
