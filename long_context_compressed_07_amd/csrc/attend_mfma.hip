@@ -34,6 +34,7 @@
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
 // rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
 #include "attend_generic.h"
+#include "attend_plan.h"
 
 namespace csa {
 namespace {
@@ -62,14 +63,7 @@ constexpr int kMT = kDC / 32;            // 32-dim output tiles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRange = 15.0f;          // log2 headroom of P above the reference max (fp16)
 
-struct MfmaPlan {
-  int ksw;            // key splits inside a workgroup
-  int head_groups;    // workgroups per query along heads (each covers 32 * 4 / ksw heads)
-  int n_split;        // workgroups per query along keys
-  float* ws_o;        // [nq][n_split][H][kDC] partial outputs (unnormalised), n_split > 1
-  float* ws_ml;       // [nq][n_split][H][2] partial (max in log2 units, sum)
-  int* flags;         // [nq][head_groups][n_split] 1 = a head left the fp16 range of P
-};
+using MfmaPlan = AttnPlan;
 
 __device__ __forceinline__ half8 cvt8_bf16(uint4 v) {
   half8 h;
@@ -419,25 +413,38 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
   }
 }
 
-MfmaPlan make_plan(int nq, int H, int64_t max_keys) {
+// Work decomposition. Many queries (prefill): one workgroup per query and head group, 4 head
+// groups sharing each staged tile (ksw 1) or 2 head groups x 2 key halves (ksw 2). Few queries
+// (decode): also split each query's keys over workgroups (n_split) to fill the chip, merged by
+// combine_kernel. bf16 caches take the DMA kernel (ksw 1 or 2); fp8 caches, and head counts that
+// are an odd multiple of 32, take the fp16-staging kernel (ksw up to 4, one 32-head group each).
+MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
   MfmaPlan p{};
   const int groups32 = H / 32;
-  if ((int64_t)nq * ((groups32 + 3) / 4) >= 512 && groups32 % 4 == 0) {
-    p.ksw = 1;                    // prefill, 128 heads: 4 head groups share each tile
+  const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
+  auto splits_for = [&](int64_t wgs_per_split) {
+    const int64_t wgs = (int64_t)nq * wgs_per_split;
+    const int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
+    return (int)(ns < cap ? ns : cap);
+  };
+  if (groups32 % 4 == 0 && (int64_t)nq * (groups32 / 4) >= 512) {
+    p.ksw = 1;
     p.head_groups = groups32 / 4;
     p.n_split = 1;
-  } else if ((int64_t)nq * (groups32 / 2) >= 512 && groups32 % 2 == 0) {
-    p.ksw = 2;                    // prefill, 64 heads: 2 head groups x 2 key halves
+  } else if (groups32 % 2 == 0 && (int64_t)nq * (groups32 / 2) >= 512) {
+    p.ksw = 2;
     p.head_groups = groups32 / 2;
     p.n_split = 1;
+  } else if (bf16 && groups32 % 2 == 0) {
+    p.ksw = 2;
+    p.head_groups = groups32 / 2;
+    p.n_split = splits_for(p.head_groups);
   } else {
-    p.ksw = 4;                    // decode: one head group per workgroup, 4 key quarters
+    p.ksw = 4;
     p.head_groups = groups32;
-    const int64_t wgs = (int64_t)nq * groups32;
-    int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-    const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
-    p.n_split = (int)(ns < cap ? ns : cap);
+    p.n_split = splits_for(p.head_groups);
   }
+  p.bf16_dma = bf16 && p.ksw <= 2;
   return p;
 }
 
@@ -453,14 +460,17 @@ bool attend_mfma_supported(const AttendArgs& a) {
 
 // Workspace: partial outputs when a query spans several workgroups, then one flag per workgroup.
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
-  const MfmaPlan p = make_plan(nq, H, max_keys);
+  // The larger of the two plans (the dtype is not part of the workspace query).
+  const MfmaPlan pa = make_plan(nq, H, max_keys, true), pb = make_plan(nq, H, max_keys, false);
+  const MfmaPlan& p = (int64_t)pa.head_groups * pa.n_split > (int64_t)pb.head_groups * pb.n_split
+                          ? pa : pb;
   const size_t partial =
       p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float) : 0;
   return partial + (size_t)nq * p.head_groups * p.n_split * sizeof(int);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys);
+  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, a.ent.dtype == CSA_BF16);
   size_t off = 0;
   if (p.n_split > 1) {
     p.ws_o = static_cast<float*>(a.ws);
@@ -470,7 +480,10 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + off);
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   const bool fp8 = a.ent.dtype == CSA_E4M3;
-  switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
+  if (p.bf16_dma) {
+    hipError_t e = launch_attend_bf16(a, p, s);
+    if (e != hipSuccess) return e;
+  } else switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
     case 2: attend_mfma_kernel<CSA_BF16, 1><<<grid, 256, 0, s>>>(a, p); break;
     case 3: attend_mfma_kernel<CSA_E4M3, 1><<<grid, 256, 0, s>>>(a, p); break;
     case 4: attend_mfma_kernel<CSA_BF16, 2><<<grid, 256, 0, s>>>(a, p); break;
