@@ -1,25 +1,37 @@
 // MFMA attention for bf16 caches (csa_attend / hca_attend; 512 latent + 64 RoPE dims per row,
-// bf16 queries, heads in groups of 32): the prefill path.
+// bf16 queries, heads in groups of 64 or 128 per workgroup): the prefill path.
 //
 // Method: deepseek.csdn.net "一文搞懂 DeepSeek" V4 改进一 (CSA: selected compressed rows plus the
 // raw window, MQA with one KV shared by every head; HCA: dense over the m'-compressed rows) and the
 // MLA section (key row = [latent; RoPE key], value row = latent); yudonglee.me "DeepSeek-V4 详解"
 // 2.2 Step 4 and 2.3 Step 2.
 //
-// A workgroup is 4 waves and serves one query: HGW groups of 32 heads x KSW splits of its key list
-// (HGW * KSW = 4). Key rows reach LDS by DMA (global_load_lds, 16 bytes per lane, no registers):
-// tile t + 1 streams into the second buffer while tile t is computed, so each tile costs one
-// barrier. Rows stay bf16 and unpadded, split into a latent region ([rows][1024 B]) and a RoPE
-// region ([rows][128 B]) so that one DMA instruction moves one row's latent (a wave-uniform row
+// A workgroup is 4 waves and serves R = 32 RG heads of one query (RG = 2 or 4 row groups of 32
+// heads). Key rows reach LDS by DMA (global_load_lds, 16 bytes per lane, no registers) in tiles of
+// TK = 128 / RG rows, double-buffered: tile t + 1 streams in while tile t is computed. Each tile is
+// computed in two phases split differently over the waves:
+//   QK   wave w takes row group w % RG and key block w / RG (32 keys):
+//        S^T[32 keys x 32 heads] = K . Q^T, 36 x mfma_f32_32x32x16_bf16 with Q^T held in
+//        registers; each lane owns one head's column, so the softmax is lane-local. P (fp16) goes
+//        to LDS in exactly the register layout the PV phase reads back.
+//   PV   wave w owns the value dims [128 w, 128 w + 128) of all R heads:
+//        O^T[128 dims x R heads] += V^T . P^T, 32 x mfma_f32_32x32x16_f16 per tile; V^T fragments
+//        come from transposed LDS reads (ds_read_b64_tr_b16) and each feeds RG MFMAs.
+// Splitting the output dims keeps O^T at 64 RG accumulator registers per lane and leaves the
+// vector registers for loads in flight. Nothing has to be merged across waves at the end.
+//
+// Numerics. Keys and queries stay bf16 (products exact in fp32). V converts to fp16 in registers
+// (exact in fp16's normal range) and P is fp16 (relative rounding 2^-11). The softmax takes a fixed
+// per-head reference: the maximum logit of the first tile that has a key, so no running rescale is
+// needed. A later logit about 16 (log2 units) above it overflows P's fp16, and a value outside
+// fp16's range overflows V; either turns the output non-finite, which flags the workgroup, and the
+// fixup pass then recomputes that query in fp32.
+//
+// LDS tile layout: rows stay unpadded, split into a latent region ([rows][1024 B]) and a RoPE
+// region ([rows][128 B]), so one DMA instruction moves one row's latent (a wave-uniform row
 // address). 16-byte chunk c of row r sits at chunk position c ^ f(r), f(r) = 2 (r & 3) + (r >> 2 & 1),
 // which keeps the K-fragment reads (8 consecutive rows, one chunk) and the transposed V reads
-// (4 consecutive rows, 2 adjacent chunks) free of bank conflicts. Per wave and 32-key tile:
-//   S^T[32 keys x 32 heads] = K . Q^T      36 x mfma_f32_32x32x16_bf16 (Q^T in registers)
-//   softmax per head                        lane-local (each lane owns one head's column); the
-//                                           reference max is fixed at the first non-empty tile
-//   O^T[512 x 32 heads] += V^T . P^T        P = P_hi + P_lo, both bf16 (P_lo = bf16(p - P_hi)):
-//                                           2 x 32 mfma, relative error of P about 2^-16
-// Products of bf16 values are exact in the fp32 accumulators, so only P is rounded.
+// (4 consecutive rows, 2 adjacent chunks) free of bank conflicts.
 #include "attend_generic.h"
 #include "attend_plan.h"
 
@@ -27,6 +39,7 @@ namespace csa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
@@ -35,18 +48,47 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kDC = 512;
 constexpr int kDR = 64;
 constexpr int kD = kDC + kDR;
-constexpr int kChunks = kD / 8;          // 72 chunks of 16 bytes per row
 constexpr int kRowB = kD * 2;            // 1152 bytes per staged row
-constexpr int kKSteps = kD / 16;
-constexpr int kMT = kDC / 32;
+constexpr int kKSteps = kD / 16;         // QK k-steps
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRange = 60.0f;          // log2 headroom of P above the reference max (bf16 range)
 
 __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// outstanding global loads (a __syncthreads() fence would also wait for the DMA of the next
+// tile, which must stay in flight across the barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most N vector memory operations are outstanding and
+// leaves the other counters unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8).
+template <int N>
+constexpr int kVmcntDma = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ int lds_addr(const char* p) {
+  return (int)(uintptr_t)(const lds_char*)p;
+}
+
+// 8 bf16 values (4 words, low half first) -> 8 fp16 values, round to nearest even (exact for
+// values in fp16's normal range; larger magnitudes become infinite and are caught downstream).
+__device__ __forceinline__ f16x8 bf16x8_to_f16(uint32_t w0, uint32_t w1, uint32_t w2,
+                                               uint32_t w3) {
+  const uint32_t w[4] = {w0, w1, w2, w3};
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
+    r[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xffff0000u);
+  }
+  return r;
+}
 
 __device__ __forceinline__ int key_code(const AttendArgs& a, const KeyList& kl, int64_t kk,
                                         int64_t ke) {
@@ -56,27 +98,50 @@ __device__ __forceinline__ int key_code(const AttendArgs& a, const KeyList& kl, 
   return row >= 0 ? (int)row | (src << 30) : -1;
 }
 
+// Row addressing of the two stores for one sequence, computed once per workgroup (kept as plain
+// scalars: a runtime-indexed array would live in scratch memory).
+struct RowBases {
+  const char* c0;          // latent rows of sequence b in the entry store
+  const char* c1;          // ... in the raw window store
+  const char* r0;          // RoPE rows, entry store
+  const char* r1;          // RoPE rows, raw window store
+  uint32_t ldc0, ldc1, ldr0, ldr1;   // row strides in bytes
+  const char* zero;        // a 16-byte zero chunk (source for empty slots)
+};
+
+__device__ __forceinline__ RowBases row_bases(const AttendArgs& a, int64_t b) {
+  RowBases rb;
+  rb.c0 = static_cast<const char*>(a.ent.c) + b * a.ent.rows * a.ent.ld_c * 2;
+  rb.r0 = static_cast<const char*>(a.ent.r) + b * a.ent.rows * a.ent.ld_r * 2;
+  rb.ldc0 = (uint32_t)(a.ent.ld_c * 2);
+  rb.ldr0 = (uint32_t)(a.ent.ld_r * 2);
+  const bool win = a.raw.c != nullptr;
+  rb.c1 = win ? static_cast<const char*>(a.raw.c) + b * a.raw.rows * a.raw.ld_c * 2 : rb.c0;
+  rb.r1 = win ? static_cast<const char*>(a.raw.r) + b * a.raw.rows * a.raw.ld_r * 2 : rb.r0;
+  rb.ldc1 = win ? (uint32_t)(a.raw.ld_c * 2) : rb.ldc0;
+  rb.ldr1 = win ? (uint32_t)(a.raw.ld_r * 2) : rb.ldr0;
+  rb.zero = reinterpret_cast<const char*>(&kZeroChunk);
+  return rb;
+}
+
 // Issue the DMA of one tile (TK rows) into buf = [latent region TK x 1024 B][RoPE region TK x 128 B].
 // Latent: one instruction per row (wave w takes rows w, w + 4, ...), lane l fetching chunk
-// l ^ f(row). RoPE: one instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk
-// (l & 7) ^ f(row). Empty slots read a zero chunk.
+// l ^ f(row); the row's code is wave-uniform, so its address is scalar arithmetic. RoPE: one
+// instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk (l & 7) ^ f(row). Empty slots
+// read a zero chunk.
 template <int TK>
-__device__ __forceinline__ void dma_tile(const AttendArgs& a, int64_t b, const int* codes,
-                                         char* buf) {
+__device__ __forceinline__ void dma_tile(const RowBases& rb, const int* codes, char* buf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int code[TK / 4];
-#pragma unroll
-  for (int j = 0; j < TK / 4; ++j) code[j] = codes[4 * j + w];
+  const int mine = lane < TK / 4 ? codes[4 * lane + w] : -1;   // lane j: code of row 4 j + w
 #pragma unroll
   for (int j = 0; j < TK / 4; ++j) {
     const int r = 4 * j + w;
-    const int cd = __builtin_amdgcn_readfirstlane(code[j]);
-    const void* src = &kZeroChunk;
+    const int cd = __builtin_amdgcn_readlane(mine, j);
+    const char* src = rb.zero;
     if (cd >= 0) {
-      const Store& st = (cd >> 30) ? a.raw : a.ent;
-      const uint16_t* crow = static_cast<const uint16_t*>(st.c) +
-                             (b * st.rows + (cd & 0x3fffffff)) * st.ld_c;
-      src = crow + 8 * (lane ^ swz(r));
+      const bool raw = cd >> 30;
+      src = (raw ? rb.c1 : rb.c0) + (uint64_t)(uint32_t)(cd & 0x3fffffff) * (raw ? rb.ldc1 : rb.ldc0) +
+            16 * (lane ^ swz(r));
     }
     __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + 1024 * r), 16, 0, 0);
   }
@@ -85,12 +150,11 @@ __device__ __forceinline__ void dma_tile(const AttendArgs& a, int64_t b, const i
   for (int j = w; j < TK / 8; j += 4) {
     const int r = 8 * j + (lane >> 3);
     const int cd = codes[r];
-    const void* src = &kZeroChunk;
+    const char* src = rb.zero;
     if (cd >= 0) {
-      const Store& st = (cd >> 30) ? a.raw : a.ent;
-      const uint16_t* rrow = static_cast<const uint16_t*>(st.r) +
-                             (b * st.rows + (cd & 0x3fffffff)) * st.ld_r;
-      src = rrow + 8 * ((lane & 7) ^ swz(r));
+      const bool raw = cd >> 30;
+      src = (raw ? rb.r1 : rb.r0) + (uint64_t)(uint32_t)(cd & 0x3fffffff) * (raw ? rb.ldr1 : rb.ldr0) +
+            16 * ((lane & 7) ^ swz(r));
     }
     __builtin_amdgcn_global_load_lds(src, (lds_char*)(rbuf + 1024 * j), 16, 0, 0);
   }
@@ -98,255 +162,420 @@ __device__ __forceinline__ void dma_tile(const AttendArgs& a, int64_t b, const i
 
 // Raw list entry for key kk (the selection slot, or the row for window / dense keys), fetched
 // early; key_code_of() turns it into a code later, so the load's latency overlaps a whole tile.
-__device__ __forceinline__ int64_t key_prefetch(const AttendArgs& a, const KeyList& kl,
-                                                int64_t kk, int64_t ke) {
+__device__ __forceinline__ int key_prefetch(const AttendArgs& a, const KeyList& kl, int64_t kk,
+                                            int64_t ke) {
   if (kk >= ke) return -1;
-  if (kk < kl.n_sel && kl.sel != nullptr) return (int64_t)kl.sel[kk];
-  return kk;
+  if (kk < kl.n_sel && kl.sel != nullptr) return kl.sel[kk];
+  return 0;
 }
 
-__device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int64_t raw,
-                                           int64_t ke) {
+__device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int raw, int64_t ke) {
   if (kk >= ke || raw < 0) return -1;
-  if (kk < kl.n_sel) return (int)raw;                            // entry row (store 0)
+  if (kk < kl.n_sel) return kl.sel != nullptr ? raw : (int)kk;          // entry row (store 0)
   return (int)(kl.wlo + (kk - kl.n_sel) - kl.raw_base) | (1 << 30);   // raw-window row
 }
 
-template <int KSW>
+// S^T[32 keys x 32 heads] = K . Q^T over the 36 k-steps of a 576-dim row, as one instruction
+// block: 4 K-fragment reads stay in flight ahead of the MFMA chain (5 rotating register quads, so a
+// quad is rewritten only after the MFMA that read it and one more have issued). Every read is
+// waited for inside the block, and the trailing s_nop covers the wait states before VALU code may
+// read the accumulator. lb[t]: LDS address of latent k-step t (k-step s reads lb[s & 3] +
+// 128 (s >> 2)); rb[t]: LDS address of RoPE k-step 32 + t.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int (&lb)[4],
+                                             const int (&rb)[4]) {
+  floatx16 acc;
+  v4i t0, t1, t2, t3, t4;
+  asm volatile(
+      "ds_read_b128 %1, %42\n"
+      "ds_read_b128 %2, %43\n"
+      "ds_read_b128 %3, %44\n"
+      "ds_read_b128 %4, %45\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %6, 0\n"
+      "ds_read_b128 %5, %42 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %7, %0\n"
+      "ds_read_b128 %1, %43 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %8, %0\n"
+      "ds_read_b128 %2, %44 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %9, %0\n"
+      "ds_read_b128 %3, %45 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %10, %0\n"
+      "ds_read_b128 %4, %42 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %11, %0\n"
+      "ds_read_b128 %5, %43 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %12, %0\n"
+      "ds_read_b128 %1, %44 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %13, %0\n"
+      "ds_read_b128 %2, %45 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %14, %0\n"
+      "ds_read_b128 %3, %42 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %15, %0\n"
+      "ds_read_b128 %4, %43 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %16, %0\n"
+      "ds_read_b128 %5, %44 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %17, %0\n"
+      "ds_read_b128 %1, %45 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %18, %0\n"
+      "ds_read_b128 %2, %42 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %19, %0\n"
+      "ds_read_b128 %3, %43 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %20, %0\n"
+      "ds_read_b128 %4, %44 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %21, %0\n"
+      "ds_read_b128 %5, %45 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %22, %0\n"
+      "ds_read_b128 %1, %42 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %23, %0\n"
+      "ds_read_b128 %2, %43 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %24, %0\n"
+      "ds_read_b128 %3, %44 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %25, %0\n"
+      "ds_read_b128 %4, %45 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %26, %0\n"
+      "ds_read_b128 %5, %42 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %27, %0\n"
+      "ds_read_b128 %1, %43 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
+      "ds_read_b128 %2, %44 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %29, %0\n"
+      "ds_read_b128 %3, %45 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %30, %0\n"
+      "ds_read_b128 %4, %42 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %31, %0\n"
+      "ds_read_b128 %5, %43 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %32, %0\n"
+      "ds_read_b128 %1, %44 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %33, %0\n"
+      "ds_read_b128 %2, %45 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %34, %0\n"
+      "ds_read_b128 %3, %46\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %35, %0\n"
+      "ds_read_b128 %4, %47\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %36, %0\n"
+      "ds_read_b128 %5, %48\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %37, %0\n"
+      "ds_read_b128 %1, %49\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %38, %0\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %39, %0\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %40, %0\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %41, %0\n"
+      "s_nop 7\n s_nop 7\n s_nop 4\n"
+      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
+      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]),
+        "v"(rb[1]), "v"(rb[2]), "v"(rb[3]));
+  return acc;
+}
+
+template <int RG, int NBUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
-  constexpr int HGW = 4 / KSW;
-  constexpr int TK = 32 * KSW;
+  constexpr int KB = 4 / RG;            // 32-key blocks per tile
+  constexpr int TK = 32 * KB;           // keys per tile
+  constexpr int kAhead = NBUF - 1;      // tiles in flight ahead of the one being computed
+  constexpr int kSlots = NBUF + 1;      // key-code slots: tiles t .. t + NBUF
+  constexpr int kDmaOps = TK / 4 + TK / 32;   // DMA instructions per wave and tile
+  constexpr int R = 32 * RG;            // heads per workgroup
   constexpr int kBufB = TK * kRowB;
-  constexpr int kMergeB = KSW > 1 ? (KSW / 2) * HGW * (kMT * 16 + 2) * 64 * 4 : 0;
-  constexpr int kLdsB = 2 * kBufB > kMergeB ? 2 * kBufB : kMergeB;
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsB];
-  __shared__ int s_code[3][TK];
+  constexpr int kPSteps = TK / 16;      // PV k-steps per tile
+  // Two distinct arrays (not halves of one): every access below names its buffer statically, so
+  // the compiler can tell that reading one buffer does not wait for the DMA into the other.
+  // NBUF tile buffers: the DMA of tile t + NBUF - 1 is issued while tile t is computed.
+  __shared__ __attribute__((aligned(1024))) char kv[NBUF][kBufB];
+  __shared__ __attribute__((aligned(16))) char s_p[kPSteps * RG * 1024];
+  __shared__ int s_code[kSlots][TK];
+  __shared__ int s_has_key[kSlots];     // per code slot: the tile holds at least one key
+  __shared__ int s_full[kSlots];        // per code slot: every key of the tile is present
+  __shared__ float s_ref[KB][R];
+  __shared__ float s_l[KB][R];
   __shared__ int s_flag;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int hgw = w % HGW;
-  const int ks = w / HGW;
+  const int rg = w % RG;                // QK: row group
+  const int kb = w / RG;                // QK: key block of the tile
   const int hi = lane >> 5;
   const int per_q = plan.head_groups * plan.n_split;
   const int qi = blockIdx.x / per_q;
   const int rem = blockIdx.x - qi * per_q;
   const int hgrp = rem / plan.n_split;
   const int split = rem - hgrp * plan.n_split;
-  const int head = (hgrp * HGW + hgw) * 32 + (lane & 31);
+  const int hbase = hgrp * R;
+  const int qrow_i = 32 * rg + (lane & 31);           // QK: this lane's head within the group
   if (threadIdx.x == 0) s_flag = 0;
 
   const KeyList kl = make_key_list(a, qi);
   const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
-  const int64_t kb = (int64_t)split * per_split;
-  const int64_t ke = kb + per_split < kl.total ? kb + per_split : kl.total;
+  const int64_t k0 = (int64_t)split * per_split;
+  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
+  const RowBases rbases = row_bases(a, kl.b);
 
-  // Q^T fragments (bf16, as stored): head `head`, dims 16 s + 8 hi + [0, 8).
-  bf16x8 qb[kKSteps];
+  // Q^T fragments (bf16, as stored): head hbase + qrow_i, dims 16 s + 8 hi + [0, 8).
+  v4i qb[kKSteps];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + head) * kD;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + qrow_i) * kD;
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s)
-      qb[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hi));
+      qb[s] = *reinterpret_cast<const v4i*>(qrow + 16 * s + 8 * hi);
   }
-  floatx16 o[kMT];
+  floatx16 o[4][RG];
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) o[mt] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < RG; ++r) o[mt][r] = floatx16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  bool have_ref = false;
   bool overflow = false;
   const float cscale = a.sm_scale * kLog2e;
 
-  // Prologue: codes of tiles 0 and 1; tile 0 in flight.
-  if (threadIdx.x < TK) {
-    s_code[0][threadIdx.x] = key_code(a, kl, kb + threadIdx.x, ke);
-    s_code[1][threadIdx.x] = key_code(a, kl, kb + TK + threadIdx.x, ke);
+  // Prologue: key codes of tiles 0 .. NBUF - 1; tiles 0 .. NBUF - 2 in flight, tile 0 landed.
+  // Codes are written by wave 0 (TK <= 64 lanes), which also records whether each tile has a key
+  // and whether it is full.
+  if (threadIdx.x < 64) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      const int c = threadIdx.x < TK ? key_code(a, kl, k0 + j * TK + threadIdx.x, ke) : -1;
+      if (threadIdx.x < TK) s_code[j][threadIdx.x] = c;
+      const bool h = __any(c >= 0);
+      const bool f = __all(c >= 0 || threadIdx.x >= TK);
+      if (threadIdx.x == 0) {
+        s_has_key[j] = h;
+        s_full[j] = f;
+      }
+    }
   }
   __syncthreads();
-  if (kb < ke) dma_tile<TK>(a, kl.b, s_code[0], lds);
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (k0 + j * TK < ke) dma_tile<TK>(rbases, s_code[j], kv[j]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  int it = 0;
-  for (int64_t t0 = kb; t0 < ke; t0 += TK, ++it) {
-    const int cb = it & 1;
-    const int* codes = s_code[it % 3];
-    // The list entries of the tile after next are fetched first (their wait comes at the end of
-    // the iteration), then the next tile's rows stream into the other buffer.
-    const int64_t kk2 = t0 + 2 * TK + threadIdx.x;
-    int64_t raw2 = -1;
-    if (threadIdx.x < TK) raw2 = key_prefetch(a, kl, kk2, ke);
-    if (t0 + TK < ke) dma_tile<TK>(a, kl.b, s_code[(it + 1) % 3], lds + (cb ^ 1) * kBufB);
+  // PV addressing. V^T fragment of dim tile mt (32 dims) and k-step s (16 keys): lane (group g,
+  // la) reads rows r0 = 16 s + 4 hi + la / 4 (and r0 + 8), dims d = 32 mt + 16 (g & 1) + 4 (la & 3).
+  // f(r0) = 2 (la / 4) + hi for every s, and chunk (4 mt + c0) ^ f = 4 (mt ^ f2) + (c0 ^ (f & 3)),
+  // so the address is a per-lane base (one for even, one for odd mt) plus compile-time offsets.
+  // The key order inside a k-step matches the S^T accumulator layout of the QK phase.
+  int v_even, v_odd;
+  {
+    const int g = lane >> 4, la = lane & 15;
+    const int f = 2 * (la >> 2) + hi;
+    const int c0 = 2 * (g & 1) + ((la & 3) >> 1);
+    const int f2 = f >> 2;
+    const int base = (4 * hi + (la >> 2)) * 1024 + 16 * (c0 ^ (f & 3)) + 8 * (la & 1) + 256 * w;
+    v_even = base + 64 * f2;
+    v_odd = base - 64 * f2;
+  }
 
-    const char* cbuf = lds + cb * kBufB;                 // latent region of this tile
-    const char* wlat = cbuf + (32 * ks) * 1024;          // this wave's 32 rows
-    const char* wrope = cbuf + TK * 1024 + (32 * ks) * 128;
-    // S^T = K . Q^T: latent k-steps 0..31 (chunk 2 s + hi), RoPE k-steps 32..35.
-    floatx16 acc = floatx16{};
+  // One tile: compute from `cbuf` while the next tile streams into `nbuf`.
+  // One tile: compute from `cbuf` while tile t + kAhead streams into `nbuf`.
+  auto tile = [&](const char* __restrict__ cbuf, char* __restrict__ nbuf, int64_t t0, int it) {
+    const int slot = it % kSlots;
+    const int* codes = s_code[slot];
+    // The list entries of tile t + kAhead + 1 are fetched first (their wait comes at the end of the
+    // tile), then tile t + kAhead streams into its buffer.
+    const int64_t kk2 = t0 + (kAhead + 1) * TK + threadIdx.x;
+    int raw2 = -1;
+    if (threadIdx.x < TK) raw2 = key_prefetch(a, kl, kk2, ke);
+    const bool dma_now = t0 + kAhead * TK < ke;
+    if (dma_now) dma_tile<TK>(rbases, s_code[(it + kAhead) % kSlots], nbuf);
+
+    // ---- QK: S^T = K . Q^T for key block kb; latent k-steps 0..31 (chunk 2 s + hi), RoPE 32..35.
+    floatx16 acc;
     {
       // Chunk 2 s + hi of row r sits at (2 s + hi) ^ f = 2 (s ^ f1) + (hi ^ f0): for s = 4 q + t
-      // that is byte 128 q + 32 (t ^ f1) + 16 (hi ^ f0), i.e. four per-lane bases (one per t)
-      // plus compile-time offsets.
+      // that is byte 128 q + 32 (t ^ f1) + 16 (hi ^ f0): four per-lane bases (one per t) plus
+      // compile-time offsets.
       const int r = lane & 31;
       const int f = swz(r);
       const int h16 = 16 * (hi ^ (f & 1));
-      const char* lb[4];
-      const char* rb[4];
+      const int lat = lds_addr(cbuf) + (32 * kb + r) * 1024 + h16;
+      const int rope = lds_addr(cbuf) + TK * 1024 + (32 * kb + r) * 128 + h16;
+      int lb[4], rb[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        lb[t] = wlat + r * 1024 + 32 * (t ^ (f >> 1)) + h16;
-        rb[t] = wrope + r * 128 + 32 * (t ^ (f >> 1)) + h16;
+        lb[t] = lat + 32 * (t ^ (f >> 1));
+        rb[t] = rope + 32 * (t ^ (f >> 1));
       }
-      // Four K fragments in flight ahead of the MFMA that consumes them.
-      constexpr int kAhead = 4;
-      bf16x8 kf[kAhead];
-#pragma unroll
-      for (int s = 0; s < kAhead; ++s)
-        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(lb[s & 3] + 128 * (s >> 2)));
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const bf16x8 av = kf[s % kAhead];
-        const int sn = s + kAhead;
-        if (sn < kKSteps) {
-          const char* src = sn < kDC / 16 ? lb[sn & 3] + 128 * (sn >> 2) : rb[sn & 3];
-          kf[s % kAhead] = as_bf16x8(*reinterpret_cast<const uint4*>(src));
-        }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[s], acc, 0, 0, 0);
-      }
+      acc = qk_chain(qb, lb, rb);
     }
 
-    float tmax = -INFINITY;
+    if (!s_full[slot]) {            // empty slots (a partial tile, -1 selections): no logit
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * ks + 8 * (i >> 2) + 4 * hi + (i & 3);
-      acc[i] = codes[key] >= 0 ? acc[i] * cscale : -INFINITY;
-      tmax = fmaxf(tmax, acc[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+        acc[i] = codes[key] >= 0 ? acc[i] : -INFINITY;
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    m_run = m_run == -INFINITY ? tmax : m_run;
-    overflow |= tmax > m_run + kRange;
-    // P^T = P_hi + P_lo in bf16, in the B-operand layout: k-step s of lane half hi covers keys
-    // 16 s + 4 hi + [0,4) and 16 s + 8 + 4 hi + [0,4).
-    bf16x8 ph[2], pl[2];
+    // Reference maximum (scaled logits, log2 units), set at the first tile that holds a key. Every
+    // head of the query sees the same keys, so the condition is uniform across the workgroup.
+    if (!have_ref && s_has_key[slot]) {
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = acc[i] == -INFINITY ? 0.f : exp2f(fminf(acc[i] - m_run, kRange));
-      l_run += p;
-      const __bf16 h = (__bf16)p;
-      ph[i >> 3][i & 7] = h;
-      pl[i >> 3][i & 7] = (__bf16)(p - (float)h);
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[i] * cscale);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (KB > 1) {
+        if (hi == 0) s_ref[kb][qrow_i] = tmax;
+        lds_barrier();
+        float mx = s_ref[0][qrow_i];
+#pragma unroll
+        for (int j = 1; j < KB; ++j) mx = fmaxf(mx, s_ref[j][qrow_i]);
+        tmax = mx;
+      }
+      m_ref = tmax;
+      have_ref = true;
     }
-    // O^T += V^T . P^T; V^T fragments read transposed from the bf16 rows. Lane (group g, la)
-    // reads rows r0 = 16 s + 4 hi + la / 4 (and r0 + 8), dims d = 32 mt + 16 (g & 1) + 4 (la & 3):
-    // f(r0) = 2 (la / 4) + hi for every s, and chunk (4 mt + c0) ^ f = 4 (mt ^ f2) + (c0 ^ (f & 3)),
-    // so the address is a per-lane base (one for even, one for odd mt) plus compile-time offsets.
+    // Logits more than 2^16 above the reference overflow P's fp16 and reach O as inf/NaN, which
+    // the final check flags; no per-tile test is needed.
+    const float nm = have_ref ? -m_ref : 0.f;   // no reference yet: the tile is empty, P = 0
+    // P^T in the B-operand layout of the PV MFMA: k-step s of lane half hi holds keys
+    // 16 s + 4 hi + [0,4) and 16 s + 8 + 4 hi + [0,4) of this key block.
     {
-      const int g = lane >> 4, la = lane & 15;
-      const int f = 2 * (la >> 2) + hi;
-      const int c0 = 2 * (g & 1) + ((la & 3) >> 1);
-      const int within = 8 * (la & 1);
-      const int f2 = f >> 2;
-      const char* base = wlat + (4 * hi + (la >> 2)) * 1024 + 16 * (c0 ^ (f & 3)) + within;
-      const char* be = base + 64 * f2;          // even mt: 4 mt ^ 4 f2 = 4 mt + 4 f2
-      const char* bo = base - 64 * f2;          // odd mt: 4 mt - 4 f2
+      f16x8 ph[2];
 #pragma unroll
-      for (int mt = 0; mt < kMT; mt += 4) {
-        bf16x8 av[4][2];
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], cscale, nm));   // exp2(-inf) = 0
+        l_run += p;
+        ph[i >> 3][i & 7] = (_Float16)p;
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+      for (int s = 0; s < 2; ++s)
+        *reinterpret_cast<f16x8*>(s_p + (((2 * kb + s) * RG + rg) * 64 + lane) * 16) = ph[s];
+    }
+    lds_barrier();   // P of the whole tile is in LDS
+
+    // ---- PV: O^T[dims 128 w + 32 mt, heads 32 r] += V^T . P^T over the tile's k-steps.
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const char* b0 = ((mt + u) & 1 ? bo : be) + 64 * (mt + u) + 16384 * s;
-            const uint2 v0 = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const lds_char*)b0));
-            const uint2 v1 = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (lds_short4*)(const lds_char*)(b0 + 8 * 1024)));
-            av[u][s] = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-          }
+    for (int ks = 0; ks < kPSteps; ++ks) {
+      f16x8 pf[RG];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+      for (int r = 0; r < RG; ++r)
+        pf[r] = *reinterpret_cast<const f16x8*>(s_p + ((ks * RG + r) * 64 + lane) * 16);
+      const int koff = (ks >> 1) * 32 * 1024 + (ks & 1) * 16384;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[mt + u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u][s], ph[s], o[mt + u], 0, 0, 0);
+      for (int mt = 0; mt < 4; ++mt) {
+        const char* b0 = cbuf + ((mt & 1) ? v_odd : v_even) + 64 * mt + koff;
+        const uint2 x0 = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const lds_char*)b0));
+        const uint2 x1 = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (lds_short4*)(const lds_char*)(b0 + 8 * 1024)));
+        const f16x8 vf = bf16x8_to_f16(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[mt + u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u][s], pl[s], o[mt + u], 0, 0, 0);
-        }
+        for (int r = 0; r < RG; ++r)
+          o[mt][r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[r], o[mt][r], 0, 0, 0);
       }
     }
-    if (threadIdx.x < TK) s_code[(it + 2) % 3][threadIdx.x] = key_code_of(kl, kk2, raw2, ke);
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's DMA of the next tile has landed
-    __syncthreads();                 // every wave is done with this tile; next tile complete
-  }
+    if (threadIdx.x < 64) {
+      const int c2 = threadIdx.x < TK ? key_code_of(kl, kk2, raw2, ke) : -1;
+      const int slot2 = (it + kAhead + 1) % kSlots;
+      if (threadIdx.x < TK) s_code[slot2][threadIdx.x] = c2;
+      const bool h2 = __any(c2 >= 0);
+      const bool f2 = __all(c2 >= 0 || threadIdx.x >= TK);
+      if (threadIdx.x == 0) {
+        s_has_key[slot2] = h2;
+        s_full[slot2] = f2;
+      }
+    }
+    // This wave's DMA of tile t + 1 has landed once at most the kDmaOps instructions of tile
+    // t + kAhead are outstanding (vector memory operations complete in order).
+    if (kAhead > 1 && dma_now)
+      __builtin_amdgcn_s_waitcnt(kVmcntDma<kDmaOps>);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();                   // every wave is done with this tile and with s_p
+  };
+  int it = 0;
+  for (int64_t t0 = k0; t0 < ke; t0 += TK, ++it)
+    tile(kv[it % NBUF], kv[(it + kAhead) % NBUF], t0, it);
 
+  // Row sums of each key block and the reference maxima go through LDS to the PV layout.
   l_run += __shfl_xor(l_run, 32);
-  if (__any(overflow)) atomicOr(&s_flag, 1);
-
-  // Merge the KSW key splits of each head group through LDS (lane-local log-sum-exp merge).
-  if (KSW > 1) {
-    float* xo = reinterpret_cast<float*>(lds);
-    for (int span = KSW / 2; span >= 1; span >>= 1) {
-      const bool sender = ks >= span && ks < 2 * span;
-      const bool receiver = ks < span;
-      float* slot = xo + (size_t)((ks % span) * HGW + hgw) * (kMT * 16 + 2) * 64;
-      if (sender) {
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) slot[(mt * 16 + i) * 64 + lane] = o[mt][i];
-        slot[(kMT * 16) * 64 + lane] = m_run;
-        slot[(kMT * 16 + 1) * 64 + lane] = l_run;
-      }
-      __syncthreads();
-      if (receiver) {
-        const float m2 = slot[(kMT * 16) * 64 + lane];
-        const float l2 = slot[(kMT * 16 + 1) * 64 + lane];
-        const float mm = fmaxf(m_run, m2);
-        const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
-        const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mm);
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          floatx16 other;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) other[i] = slot[(mt * 16 + i) * 64 + lane];
-          o[mt] = o[mt] * a1 + other * a2;
-        }
-        l_run = l_run * a1 + l2 * a2;
-        m_run = mm;
-      }
-      __syncthreads();
-    }
+  if (hi == 0) {
+    s_l[kb][qrow_i] = l_run;
+    if (kb == 0) s_ref[0][qrow_i] = m_ref;
   }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][r][i]);
+  if (__any(overflow)) atomicOr(&s_flag, 1);
   __syncthreads();
   if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
-  if (ks != 0) return;
 
-  if (plan.n_split == 1) {
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float* orow = a.out + ((int64_t)qi * a.H + head) * kDC;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+  for (int r = 0; r < RG; ++r) {
+    const int hrow = 32 * r + (lane & 31);
+    float l = s_l[0][hrow];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-            make_float4(o[mt][4 * j] * inv, o[mt][4 * j + 1] * inv, o[mt][4 * j + 2] * inv,
-                        o[mt][4 * j + 3] * inv);
-    if (a.lse != nullptr && hi == 0)
-      a.lse[(int64_t)qi * a.H + head] =
-          l_run > 0.f ? (m_run + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
-  } else {
-    const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
-    float* orow = plan.ws_o + pidx * kDC;
+    for (int j = 1; j < KB; ++j) l += s_l[j][hrow];
+    const float m = s_ref[0][hrow];
+    const int head = hbase + hrow;
+    if (plan.n_split == 1) {
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* orow = a.out + ((int64_t)qi * a.H + head) * kDC + 128 * w;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-            make_float4(o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]);
-    if (hi == 0) {
-      plan.ws_ml[pidx * 2] = m_run;
-      plan.ws_ml[pidx * 2 + 1] = l_run;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
+              make_float4(o[mt][r][4 * j] * inv, o[mt][r][4 * j + 1] * inv,
+                          o[mt][r][4 * j + 2] * inv, o[mt][r][4 * j + 3] * inv);
+      if (a.lse != nullptr && w == 0 && hi == 0)
+        a.lse[(int64_t)qi * a.H + head] =
+            l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
+    } else {
+      const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
+      float* orow = plan.ws_o + pidx * kDC + 128 * w;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
+              make_float4(o[mt][r][4 * j], o[mt][r][4 * j + 1], o[mt][r][4 * j + 2],
+                          o[mt][r][4 * j + 3]);
+      if (w == 0 && hi == 0) {
+        plan.ws_ml[pidx * 2] = m;
+        plan.ws_ml[pidx * 2 + 1] = l;
+      }
     }
   }
 }
@@ -355,10 +584,10 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
 
 hipError_t launch_attend_bf16(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
-  if (p.ksw == 1)
-    attend_bf16_kernel<1><<<grid, 256, 0, s>>>(a, p);
+  if (p.rg == 4)
+    attend_bf16_kernel<4, 3><<<grid, 256, 0, s>>>(a, p);
   else
-    attend_bf16_kernel<2><<<grid, 256, 0, s>>>(a, p);
+    attend_bf16_kernel<2, 2><<<grid, 256, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@
 // Precision: products in fp16 are exact for these inputs (bf16 and scaled fp8 values lie inside
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
 // rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
+#include <algorithm>
+
 #include "attend_generic.h"
 #include "attend_plan.h"
 
@@ -413,11 +415,12 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
   }
 }
 
-// Work decomposition. Many queries (prefill): one workgroup per query and head group, 4 head
-// groups sharing each staged tile (ksw 1) or 2 head groups x 2 key halves (ksw 2). Few queries
-// (decode): also split each query's keys over workgroups (n_split) to fill the chip, merged by
-// combine_kernel. bf16 caches take the DMA kernel (ksw 1 or 2); fp8 caches, and head counts that
-// are an odd multiple of 32, take the fp16-staging kernel (ksw up to 4, one 32-head group each).
+// Work decomposition. bf16 caches with a multiple of 64 heads take the DMA kernel
+// (attend_bf16.hip): one workgroup per query and group of 64 or 128 heads. Everything else takes
+// the fp16-staging kernel here: many queries (prefill) give one workgroup per query and head group,
+// 4 head groups sharing each staged tile (ksw 1) or 2 head groups x 2 key halves (ksw 2); few
+// queries (decode) take ksw 4, one 32-head group each. When there are too few workgroups to fill
+// the chip, each query's keys are also split over workgroups (n_split), merged by combine_kernel.
 MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
   MfmaPlan p{};
   const int groups32 = H / 32;
@@ -427,6 +430,13 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
     const int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
     return (int)(ns < cap ? ns : cap);
   };
+  if (bf16 && groups32 % 2 == 0) {
+    p.bf16_dma = 1;
+    p.rg = groups32 % 4 == 0 ? 4 : 2;
+    p.head_groups = groups32 / p.rg;
+    p.n_split = splits_for(p.head_groups);
+    return p;
+  }
   if (groups32 % 4 == 0 && (int64_t)nq * (groups32 / 4) >= 512) {
     p.ksw = 1;
     p.head_groups = groups32 / 4;
@@ -435,16 +445,11 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
     p.ksw = 2;
     p.head_groups = groups32 / 2;
     p.n_split = 1;
-  } else if (bf16 && groups32 % 2 == 0) {
-    p.ksw = 2;
-    p.head_groups = groups32 / 2;
-    p.n_split = splits_for(p.head_groups);
   } else {
     p.ksw = 4;
     p.head_groups = groups32;
     p.n_split = splits_for(p.head_groups);
   }
-  p.bf16_dma = bf16 && p.ksw <= 2;
   return p;
 }
 
@@ -459,25 +464,26 @@ bool attend_mfma_supported(const AttendArgs& a) {
 }
 
 // Workspace: partial outputs when a query spans several workgroups, then one flag per workgroup.
+// The dtype is not part of the workspace query, so this covers both plans.
+static size_t plan_partial_bytes(const MfmaPlan& p, int nq, int H) {
+  return p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float) : 0;
+}
+static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
+  return (size_t)nq * p.head_groups * p.n_split * sizeof(int);
+}
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
-  // The larger of the two plans (the dtype is not part of the workspace query).
   const MfmaPlan pa = make_plan(nq, H, max_keys, true), pb = make_plan(nq, H, max_keys, false);
-  const MfmaPlan& p = (int64_t)pa.head_groups * pa.n_split > (int64_t)pb.head_groups * pb.n_split
-                          ? pa : pb;
-  const size_t partial =
-      p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float) : 0;
-  return partial + (size_t)nq * p.head_groups * p.n_split * sizeof(int);
+  const size_t part = std::max(plan_partial_bytes(pa, nq, H), plan_partial_bytes(pb, nq, H));
+  return part + std::max(plan_flag_bytes(pa, nq), plan_flag_bytes(pb, nq));
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
   MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, a.ent.dtype == CSA_BF16);
-  size_t off = 0;
   if (p.n_split > 1) {
     p.ws_o = static_cast<float*>(a.ws);
     p.ws_ml = p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC;
-    off = (size_t)a.Q.nq * p.n_split * a.H * (kDC + 2) * sizeof(float);
   }
-  p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + off);
+  p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + plan_partial_bytes(p, a.Q.nq, a.H));
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   const bool fp8 = a.ent.dtype == CSA_E4M3;
   if (p.bf16_dma) {

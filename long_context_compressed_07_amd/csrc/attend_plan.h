@@ -7,8 +7,9 @@
 namespace csa {
 
 struct AttnPlan {
-  int ksw;            // key splits inside a workgroup (4 waves = 4 / ksw head groups x ksw)
-  int head_groups;    // workgroups per query along heads (each covers 128 / ksw heads)
+  int ksw;            // fp16-staging kernel: key splits inside a workgroup (4 / ksw head groups)
+  int rg;             // bf16 kernel: 32-head row groups per workgroup (2 or 4)
+  int head_groups;    // workgroups per query along heads
   int n_split;        // workgroups per query along keys
   int bf16_dma;       // 1: bf16 rows staged by DMA (attend_bf16.hip); 0: fp16 staging
   float* ws_o;        // [nq][n_split][H][512] partial outputs (unnormalised), n_split > 1
