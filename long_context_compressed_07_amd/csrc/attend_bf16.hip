@@ -52,7 +52,8 @@ constexpr int kRowB = kD * 2;            // 1152 bytes per staged row
 constexpr int kKSteps = kD / 16;         // QK k-steps
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+// Source of empty key slots: one zero row, so any lane offset within a row stays inside it.
+__device__ const uint4 kZeroRow[kRowB / 16] = {};
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
@@ -106,7 +107,6 @@ struct RowBases {
   const char* r0;          // RoPE rows, entry store
   const char* r1;          // RoPE rows, raw window store
   uint32_t ldc0, ldc1, ldr0, ldr1;   // row strides in bytes
-  const char* zero;        // a 16-byte zero chunk (source for empty slots)
 };
 
 __device__ __forceinline__ RowBases row_bases(const AttendArgs& a, int64_t b) {
@@ -120,53 +120,67 @@ __device__ __forceinline__ RowBases row_bases(const AttendArgs& a, int64_t b) {
   rb.r1 = win ? static_cast<const char*>(a.raw.r) + b * a.raw.rows * a.raw.ld_r * 2 : rb.r0;
   rb.ldc1 = win ? (uint32_t)(a.raw.ld_c * 2) : rb.ldc0;
   rb.ldr1 = win ? (uint32_t)(a.raw.ld_r * 2) : rb.ldr0;
-  rb.zero = reinterpret_cast<const char*>(&kZeroChunk);
   return rb;
 }
 
+// Global addresses of one key's latent and RoPE parts (a zero row for an empty slot).
+struct KeyAddr {
+  const char* lat;
+  const char* rope;
+};
+
+__device__ __forceinline__ KeyAddr key_addr(const RowBases& rb, int code) {
+  KeyAddr k;
+  if (code < 0) {
+    k.lat = k.rope = reinterpret_cast<const char*>(kZeroRow);
+  } else {
+    const bool raw = code >> 30;
+    const uint64_t row = (uint32_t)(code & 0x3fffffff);
+    k.lat = (raw ? rb.c1 : rb.c0) + row * (raw ? rb.ldc1 : rb.ldc0);
+    k.rope = (raw ? rb.r1 : rb.r0) + row * (raw ? rb.ldr1 : rb.ldr0);
+  }
+  return k;
+}
+
 // Issue the DMA of one tile (TK rows) into buf = [latent region TK x 1024 B][RoPE region TK x 128 B].
-// Latent: one instruction per row (wave w takes rows w, w + 4, ...), lane l fetching chunk
-// l ^ f(row); the row's code is wave-uniform, so its address is scalar arithmetic. RoPE: one
-// instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk (l & 7) ^ f(row). Empty slots
-// read a zero chunk.
+// addr[r] holds the global addresses of row r. Latent: one instruction per row (wave w takes rows
+// w, w + 4, ...): the row address is a scalar base and lane l adds 16 (l ^ f(row)). RoPE: one
+// instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk (l & 7) ^ f(row).
 template <int TK>
-__device__ __forceinline__ void dma_tile(const RowBases& rb, const int* codes, char* buf) {
+__device__ __forceinline__ void dma_tile(const KeyAddr* addr, char* buf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int mine = lane < TK / 4 ? codes[4 * lane + w] : -1;   // lane j: code of row 4 j + w
+  // Lane j holds the latent address of row 4 j + w; rows of one wave have f(row) in {f(w), f(w + 4)}.
+  const char* mine = lane < TK / 4 ? addr[4 * lane + w].lat : nullptr;
+  const uint32_t off0 = 16 * (lane ^ swz(w)), off1 = 16 * (lane ^ swz(w + 4));
 #pragma unroll
   for (int j = 0; j < TK / 4; ++j) {
     const int r = 4 * j + w;
-    const int cd = __builtin_amdgcn_readlane(mine, j);
-    const char* src = rb.zero;
-    if (cd >= 0) {
-      const bool raw = cd >> 30;
-      src = (raw ? rb.c1 : rb.c0) + (uint64_t)(uint32_t)(cd & 0x3fffffff) * (raw ? rb.ldc1 : rb.ldc0) +
-            16 * (lane ^ swz(r));
-    }
+    const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                               (int)(uint32_t)(uintptr_t)mine, j)) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                               (int)(uint32_t)((uintptr_t)mine >> 32), j) << 32);
+    const char* src = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
     __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + 1024 * r), 16, 0, 0);
   }
   char* rbuf = buf + TK * 1024;
 #pragma unroll
   for (int j = w; j < TK / 8; j += 4) {
     const int r = 8 * j + (lane >> 3);
-    const int cd = codes[r];
-    const char* src = rb.zero;
-    if (cd >= 0) {
-      const bool raw = cd >> 30;
-      src = (raw ? rb.r1 : rb.r0) + (uint64_t)(uint32_t)(cd & 0x3fffffff) * (raw ? rb.ldr1 : rb.ldr0) +
-            16 * ((lane & 7) ^ swz(r));
-    }
+    const char* src = addr[r].rope + 16 * ((lane & 7) ^ swz(r));
     __builtin_amdgcn_global_load_lds(src, (lds_char*)(rbuf + 1024 * j), 16, 0, 0);
   }
 }
 
-// Raw list entry for key kk (the selection slot, or the row for window / dense keys), fetched
-// early; key_code_of() turns it into a code later, so the load's latency overlaps a whole tile.
-__device__ __forceinline__ int key_prefetch(const AttendArgs& a, const KeyList& kl, int64_t kk,
-                                            int64_t ke) {
-  if (kk >= ke) return -1;
-  if (kk < kl.n_sel && kl.sel != nullptr) return kl.sel[kk];
-  return 0;
+// Selection slots of one tile (TK keys from kk0) copied by DMA into LDS (wave 0, lane j ->
+// dst[j]); keys outside the selection read a zero instead. Copying by DMA keeps the loop free of
+// register loads, so its waits can be exact counts of DMA instructions.
+template <int TK>
+__device__ __forceinline__ void dma_sel(const KeyList& kl, int64_t kk0, int64_t ke, int* dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t kk = kk0 + lane;
+  const void* src = (lane < TK && kk < ke && kk < kl.n_sel) ? (const void*)(kl.sel + kk)
+                                                           : (const void*)kZeroRow;
+  __builtin_amdgcn_global_load_lds(src, (lds_char*)dst, 4, 0, 0);
 }
 
 __device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int raw, int64_t ke) {
@@ -177,16 +191,249 @@ __device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int ra
 
 // S^T[32 keys x 32 heads] = K . Q^T over the 36 k-steps of a 576-dim row, as one instruction
 // block: 4 K-fragment reads stay in flight ahead of the MFMA chain (5 rotating register quads, so a
-// quad is rewritten only after the MFMA that read it and one more have issued). Every read is
-// waited for inside the block, and the trailing s_nop covers the wait states before VALU code may
-// read the accumulator. lb[t]: LDS address of latent k-step t (k-step s reads lb[s & 3] +
-// 128 (s >> 2)); rb[t]: LDS address of RoPE k-step 32 + t.
+// quad is rewritten only after the MFMA that read it and one more have issued). lb[t]: LDS address
+// of latent k-step t (k-step s reads lb[s & 3] + 128 (s >> 2)); rb[t]: LDS address of RoPE k-step
+// 32 + t. With QA the 32 latent Q^T fragments are read from accumulation registers (MFMA takes its
+// B operand from either register file). With NV > 0 the block also fetches the tile's NV
+// transposed V^T fragments for the PV phase (two ds_read_b64_tr_b16 each, from the per-lane bases
+// ve / vo for even / odd dim tiles), issued under the last MFMAs. Every LDS read is waited for
+// inside the block (lgkmcnt never exceeds 15 outstanding), and the trailing s_nop covers the wait
+// states before VALU code may read the accumulator.
+//
+// The DMA of a later tile is issued between the MFMAs (so the wave never stalls on the load path
+// while the matrix unit idles): the selection slots (4 bytes per lane), then this wave's latent
+// rows and RoPE row groups (TileDma). These write LDS only; the caller waits for them by count.
+// The block sets M0; no M0 value of the compiler's is live across it (the loop issues no other
+// DMA).
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+template <int NLAT, int NROPE>
+struct TileDma {
+  const char* sel;          // per-lane source of the selection slots
+  const char* lat[NLAT];    // per-lane sources of this wave's latent rows
+  const char* rope[NROPE];  // per-lane sources of this wave's RoPE row groups
+  int m0_rows;              // LDS address of this wave's first latent row in the target buffer
+  int m0_sel;               // LDS address of the selection slot
+};
+
+template <bool QA, int NV, int NLAT, int NROPE, int TK>
 __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int (&lb)[4],
-                                             const int (&rb)[4]) {
+                                             const int (&rb)[4], int ve, int vo,
+                                             v2i (&vr)[NV > 0 ? 2 * NV : 1],
+                                             const TileDma<NLAT, NROPE>& dma) {
   floatx16 acc;
   v4i t0, t1, t2, t3, t4;
-  asm volatile(
+  if constexpr (QA && NV == 16 && NLAT == 16 && NROPE == 2 && TK == 64) {
+    asm volatile(
+      "ds_read_b128 %1, %74\n"
+      "ds_read_b128 %2, %75\n"
+      "ds_read_b128 %3, %76\n"
+      "ds_read_b128 %4, %77\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %38, 0\n"
+      "ds_read_b128 %5, %74 offset:128\n"
+      "s_mov_b32 m0, %104\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %84, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %39, %0\n"
+      "ds_read_b128 %1, %75 offset:128\n"
+      "s_add_u32 m0, %103, 0\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %85, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %40, %0\n"
+      "ds_read_b128 %2, %76 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %41, %0\n"
+      "ds_read_b128 %3, %77 offset:128\n"
+      "s_add_u32 m0, %103, 4096\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %86, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %42, %0\n"
+      "ds_read_b128 %4, %74 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %43, %0\n"
+      "ds_read_b128 %5, %75 offset:256\n"
+      "s_add_u32 m0, %103, 8192\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %87, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %44, %0\n"
+      "ds_read_b128 %1, %76 offset:256\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %45, %0\n"
+      "ds_read_b128 %2, %77 offset:256\n"
+      "s_add_u32 m0, %103, 12288\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %88, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %46, %0\n"
+      "ds_read_b128 %3, %74 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %47, %0\n"
+      "ds_read_b128 %4, %75 offset:384\n"
+      "s_add_u32 m0, %103, 16384\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %89, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %48, %0\n"
+      "ds_read_b128 %5, %76 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %49, %0\n"
+      "ds_read_b128 %1, %77 offset:384\n"
+      "s_add_u32 m0, %103, 20480\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %90, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %50, %0\n"
+      "ds_read_b128 %2, %74 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %51, %0\n"
+      "ds_read_b128 %3, %75 offset:512\n"
+      "s_add_u32 m0, %103, 24576\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %91, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %52, %0\n"
+      "ds_read_b128 %4, %76 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %53, %0\n"
+      "ds_read_b128 %5, %77 offset:512\n"
+      "s_add_u32 m0, %103, 28672\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %92, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %54, %0\n"
+      "ds_read_b128 %1, %74 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %55, %0\n"
+      "ds_read_b128 %2, %75 offset:640\n"
+      "s_add_u32 m0, %103, 32768\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %93, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %56, %0\n"
+      "ds_read_b128 %3, %76 offset:640\n"
+      "s_add_u32 m0, %103, 36864\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %94, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %57, %0\n"
+      "ds_read_b128 %4, %77 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %58, %0\n"
+      "ds_read_b128 %5, %74 offset:768\n"
+      "s_add_u32 m0, %103, 40960\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %95, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %59, %0\n"
+      "ds_read_b128 %1, %75 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %60, %0\n"
+      "ds_read_b128 %2, %76 offset:768\n"
+      "s_add_u32 m0, %103, 45056\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %96, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %61, %0\n"
+      "ds_read_b128 %3, %77 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %62, %0\n"
+      "ds_read_b128 %4, %74 offset:896\n"
+      "s_add_u32 m0, %103, 49152\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %97, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %63, %0\n"
+      "ds_read_b128 %5, %75 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %64, %0\n"
+      "ds_read_b128 %1, %76 offset:896\n"
+      "s_add_u32 m0, %103, 53248\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %98, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %65, %0\n"
+      "ds_read_b128 %2, %77 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %66, %0\n"
+      "ds_read_b128 %3, %78\n"
+      "s_add_u32 m0, %103, 57344\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %99, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %67, %0\n"
+      "ds_read_b128 %4, %79\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %68, %0\n"
+      "ds_read_b128 %5, %80\n"
+      "s_add_u32 m0, %103, 61440\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %100, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %69, %0\n"
+      "ds_read_b128 %1, %81\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %70, %0\n"
+      "s_add_u32 m0, %103, 65536\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %101, off\n"
+      "ds_read_b64_tr_b16 %6, %82 offset:0\n"
+      "ds_read_b64_tr_b16 %7, %82 offset:8192\n"
+      "ds_read_b64_tr_b16 %8, %83 offset:64\n"
+      "ds_read_b64_tr_b16 %9, %83 offset:8256\n"
+      "ds_read_b64_tr_b16 %10, %82 offset:128\n"
+      "ds_read_b64_tr_b16 %11, %82 offset:8320\n"
+      "s_waitcnt lgkmcnt(8)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %71, %0\n"
+      "ds_read_b64_tr_b16 %12, %83 offset:192\n"
+      "ds_read_b64_tr_b16 %13, %83 offset:8384\n"
+      "ds_read_b64_tr_b16 %14, %82 offset:16384\n"
+      "ds_read_b64_tr_b16 %15, %82 offset:24576\n"
+      "ds_read_b64_tr_b16 %16, %83 offset:16448\n"
+      "ds_read_b64_tr_b16 %17, %83 offset:24640\n"
+      "s_waitcnt lgkmcnt(13)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %72, %0\n"
+      "s_add_u32 m0, %103, 69632\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %102, off\n"
+      "ds_read_b64_tr_b16 %18, %82 offset:16512\n"
+      "ds_read_b64_tr_b16 %19, %82 offset:24704\n"
+      "s_waitcnt lgkmcnt(14)\n"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %73, %0\n"
+      "ds_read_b64_tr_b16 %20, %83 offset:16576\n"
+      "ds_read_b64_tr_b16 %21, %83 offset:24768\n"
+      "ds_read_b64_tr_b16 %22, %82 offset:32768\n"
+      "ds_read_b64_tr_b16 %23, %82 offset:40960\n"
+      "ds_read_b64_tr_b16 %24, %83 offset:32832\n"
+      "ds_read_b64_tr_b16 %25, %83 offset:41024\n"
+      "ds_read_b64_tr_b16 %26, %82 offset:32896\n"
+      "ds_read_b64_tr_b16 %27, %82 offset:41088\n"
+      "ds_read_b64_tr_b16 %28, %83 offset:32960\n"
+      "ds_read_b64_tr_b16 %29, %83 offset:41152\n"
+      "ds_read_b64_tr_b16 %30, %82 offset:49152\n"
+      "ds_read_b64_tr_b16 %31, %82 offset:57344\n"
+      "ds_read_b64_tr_b16 %32, %83 offset:49216\n"
+      "ds_read_b64_tr_b16 %33, %83 offset:57408\n"
+      "ds_read_b64_tr_b16 %34, %82 offset:49280\n"
+      "ds_read_b64_tr_b16 %35, %82 offset:57472\n"
+      "ds_read_b64_tr_b16 %36, %83 offset:49344\n"
+      "ds_read_b64_tr_b16 %37, %83 offset:57536\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 4\n"
+                 : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]), "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]), "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
+                 : "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "a"(q[4]), "a"(q[5]), "a"(q[6]), "a"(q[7]), "a"(q[8]), "a"(q[9]), "a"(q[10]), "a"(q[11]), "a"(q[12]), "a"(q[13]), "a"(q[14]), "a"(q[15]), "a"(q[16]), "a"(q[17]), "a"(q[18]), "a"(q[19]), "a"(q[20]), "a"(q[21]), "a"(q[22]), "a"(q[23]), "a"(q[24]), "a"(q[25]), "a"(q[26]), "a"(q[27]), "a"(q[28]), "a"(q[29]), "a"(q[30]), "a"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]),
+                   "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]),
+                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "v"(dma.lat[0]), "v"(dma.lat[1]), "v"(dma.lat[2]), "v"(dma.lat[3]), "v"(dma.lat[4]), "v"(dma.lat[5]), "v"(dma.lat[6]), "v"(dma.lat[7]), "v"(dma.lat[8]), "v"(dma.lat[9]), "v"(dma.lat[10]), "v"(dma.lat[11]), "v"(dma.lat[12]), "v"(dma.lat[13]), "v"(dma.lat[14]), "v"(dma.lat[15]), "v"(dma.rope[0]), "v"(dma.rope[1]), "s"(dma.m0_rows), "s"(dma.m0_sel)
+                 : "m0");
+  } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {
+    asm volatile(
       "ds_read_b128 %1, %42\n"
       "ds_read_b128 %2, %43\n"
       "ds_read_b128 %3, %44\n"
@@ -194,6 +441,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %6, 0\n"
       "ds_read_b128 %5, %42 offset:128\n"
+      "s_mov_b32 m0, %63\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %52, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %7, %0\n"
       "ds_read_b128 %1, %43 offset:128\n"
@@ -203,6 +453,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %9, %0\n"
       "ds_read_b128 %3, %45 offset:128\n"
+      "s_add_u32 m0, %62, 0\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %53, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %10, %0\n"
       "ds_read_b128 %4, %42 offset:256\n"
@@ -215,6 +468,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %13, %0\n"
       "ds_read_b128 %2, %45 offset:256\n"
+      "s_add_u32 m0, %62, 4096\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %54, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %14, %0\n"
       "ds_read_b128 %3, %42 offset:384\n"
@@ -224,6 +480,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %16, %0\n"
       "ds_read_b128 %5, %44 offset:384\n"
+      "s_add_u32 m0, %62, 8192\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %55, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %17, %0\n"
       "ds_read_b128 %1, %45 offset:384\n"
@@ -236,6 +495,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %20, %0\n"
       "ds_read_b128 %4, %44 offset:512\n"
+      "s_add_u32 m0, %62, 12288\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %56, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %21, %0\n"
       "ds_read_b128 %5, %45 offset:512\n"
@@ -248,6 +510,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %24, %0\n"
       "ds_read_b128 %3, %44 offset:640\n"
+      "s_add_u32 m0, %62, 16384\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %57, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %25, %0\n"
       "ds_read_b128 %4, %45 offset:640\n"
@@ -257,6 +522,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %27, %0\n"
       "ds_read_b128 %1, %43 offset:768\n"
+      "s_add_u32 m0, %62, 20480\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %58, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
       "ds_read_b128 %2, %44 offset:768\n"
@@ -269,6 +537,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %31, %0\n"
       "ds_read_b128 %5, %43 offset:896\n"
+      "s_add_u32 m0, %62, 24576\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %59, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %32, %0\n"
       "ds_read_b128 %1, %44 offset:896\n"
@@ -278,6 +549,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %34, %0\n"
       "ds_read_b128 %3, %46\n"
+      "s_add_u32 m0, %62, 28672\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %60, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %35, %0\n"
       "ds_read_b128 %4, %47\n"
@@ -289,17 +563,95 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "ds_read_b128 %1, %49\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %38, %0\n"
+      "s_add_u32 m0, %62, 32768\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %61, off\n"
       "s_waitcnt lgkmcnt(2)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %39, %0\n"
       "s_waitcnt lgkmcnt(1)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %40, %0\n"
       "s_waitcnt lgkmcnt(0)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %41, %0\n"
-      "s_nop 7\n s_nop 7\n s_nop 4\n"
-      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
-      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]),
-        "v"(rb[1]), "v"(rb[2]), "v"(rb[3]));
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 4\n"
+                 : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]),
+                   "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]),
+                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "v"(dma.lat[0]), "v"(dma.lat[1]), "v"(dma.lat[2]), "v"(dma.lat[3]), "v"(dma.lat[4]), "v"(dma.lat[5]), "v"(dma.lat[6]), "v"(dma.lat[7]), "v"(dma.rope[0]), "s"(dma.m0_rows), "s"(dma.m0_sel)
+                 : "m0");
+  } else {
+    static_assert(QA && NV == 16, "unsupported configuration");
+  }
   return acc;
+}
+
+// Q^T fragments of one head (bf16, as stored): fragment s holds dims 16 s + 8 hi + [0, 8). With QA
+// the 32 latent fragments are loaded straight into accumulation registers, in one block that
+// waits for its loads.
+template <bool QA>
+__device__ __forceinline__ void load_q(const uint16_t* qrow, int hi, v4i (&q)[kKSteps]) {
+  const uint16_t* p = qrow + 8 * hi;
+  if constexpr (QA) {
+    asm volatile(
+        "global_load_dwordx4 %0, %32, off offset:0\n"
+        "global_load_dwordx4 %1, %32, off offset:32\n"
+        "global_load_dwordx4 %2, %32, off offset:64\n"
+        "global_load_dwordx4 %3, %32, off offset:96\n"
+        "global_load_dwordx4 %4, %32, off offset:128\n"
+        "global_load_dwordx4 %5, %32, off offset:160\n"
+        "global_load_dwordx4 %6, %32, off offset:192\n"
+        "global_load_dwordx4 %7, %32, off offset:224\n"
+        "global_load_dwordx4 %8, %32, off offset:256\n"
+        "global_load_dwordx4 %9, %32, off offset:288\n"
+        "global_load_dwordx4 %10, %32, off offset:320\n"
+        "global_load_dwordx4 %11, %32, off offset:352\n"
+        "global_load_dwordx4 %12, %32, off offset:384\n"
+        "global_load_dwordx4 %13, %32, off offset:416\n"
+        "global_load_dwordx4 %14, %32, off offset:448\n"
+        "global_load_dwordx4 %15, %32, off offset:480\n"
+        "global_load_dwordx4 %16, %32, off offset:512\n"
+        "global_load_dwordx4 %17, %32, off offset:544\n"
+        "global_load_dwordx4 %18, %32, off offset:576\n"
+        "global_load_dwordx4 %19, %32, off offset:608\n"
+        "global_load_dwordx4 %20, %32, off offset:640\n"
+        "global_load_dwordx4 %21, %32, off offset:672\n"
+        "global_load_dwordx4 %22, %32, off offset:704\n"
+        "global_load_dwordx4 %23, %32, off offset:736\n"
+        "global_load_dwordx4 %24, %32, off offset:768\n"
+        "global_load_dwordx4 %25, %32, off offset:800\n"
+        "global_load_dwordx4 %26, %32, off offset:832\n"
+        "global_load_dwordx4 %27, %32, off offset:864\n"
+        "global_load_dwordx4 %28, %32, off offset:896\n"
+        "global_load_dwordx4 %29, %32, off offset:928\n"
+        "global_load_dwordx4 %30, %32, off offset:960\n"
+        "global_load_dwordx4 %31, %32, off offset:992\n"
+        "s_waitcnt vmcnt(0)\n"
+        : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]), "=a"(q[7]), "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]), "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]), "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]), "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
+        : "v"(p));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 32; ++s) q[s] = *reinterpret_cast<const v4i*>(p + 16 * s);
+  }
+#pragma unroll
+  for (int s = 32; s < kKSteps; ++s) q[s] = *reinterpret_cast<const v4i*>(p + 16 * s);
+}
+
+// The P^T fragments of one tile (8 of them: k-step ks and row group r at index ks * RG + r), read
+// from the exchange buffer in one block that waits for its reads.
+__device__ __forceinline__ void load_p8(int addr, v4i (&p)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n"
+      "ds_read_b128 %1, %8 offset:1024\n"
+      "ds_read_b128 %2, %8 offset:2048\n"
+      "ds_read_b128 %3, %8 offset:3072\n"
+      "ds_read_b128 %4, %8 offset:4096\n"
+      "ds_read_b128 %5, %8 offset:5120\n"
+      "ds_read_b128 %6, %8 offset:6144\n"
+      "ds_read_b128 %7, %8 offset:7168\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]), "=v"(p[7])
+      : "v"(addr));
 }
 
 template <int RG, int NBUF>
@@ -309,7 +661,7 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int TK = 32 * KB;           // keys per tile
   constexpr int kAhead = NBUF - 1;      // tiles in flight ahead of the one being computed
   constexpr int kSlots = NBUF + 1;      // key-code slots: tiles t .. t + NBUF
-  constexpr int kDmaOps = TK / 4 + TK / 32;   // DMA instructions per wave and tile
+  constexpr int kDmaOps = TK / 4 + TK / 32;   // tile DMA instructions per wave and tile
   constexpr int R = 32 * RG;            // heads per workgroup
   constexpr int kBufB = TK * kRowB;
   constexpr int kPSteps = TK / 16;      // PV k-steps per tile
@@ -319,8 +671,10 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
   __shared__ __attribute__((aligned(1024))) char kv[NBUF][kBufB];
   __shared__ __attribute__((aligned(16))) char s_p[kPSteps * RG * 1024];
   __shared__ int s_code[kSlots][TK];
+  __shared__ KeyAddr s_addr[kSlots][TK];   // global addresses of each key's row parts
   __shared__ int s_has_key[kSlots];     // per code slot: the tile holds at least one key
   __shared__ int s_full[kSlots];        // per code slot: every key of the tile is present
+  __shared__ int s_sel[2][64];          // selection slots of tiles t + kAhead + 1, t + kAhead + 2
   __shared__ float s_ref[KB][R];
   __shared__ float s_l[KB][R];
   __shared__ int s_flag;
@@ -346,14 +700,14 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
   const RowBases rbases = row_bases(a, kl.b);
 
   // Q^T fragments (bf16, as stored): head hbase + qrow_i, dims 16 s + 8 hi + [0, 8).
+  // Q^T of this lane's head; with two row groups its latent part lives in accumulation registers
+  // (O takes the other half), which leaves the vector registers to the loop's loads in flight.
+  constexpr bool kQA = RG == 2;
+  // With the vector registers freed, the QK block also fetches the tile's V^T fragments.
+  constexpr int kNV = RG == 2 ? 4 * kPSteps : 0;
   v4i qb[kKSteps];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + qrow_i) * kD;
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s)
-      qb[s] = *reinterpret_cast<const v4i*>(qrow + 16 * s + 8 * hi);
-  }
+  load_q<kQA>(static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + qrow_i) * kD, hi,
+              qb);
   floatx16 o[4][RG];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -371,7 +725,10 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
       const int c = threadIdx.x < TK ? key_code(a, kl, k0 + j * TK + threadIdx.x, ke) : -1;
-      if (threadIdx.x < TK) s_code[j][threadIdx.x] = c;
+      if (threadIdx.x < TK) {
+        s_code[j][threadIdx.x] = c;
+        s_addr[j][threadIdx.x] = key_addr(rbases, c);
+      }
       const bool h = __any(c >= 0);
       const bool f = __all(c >= 0 || threadIdx.x >= TK);
       if (threadIdx.x == 0) {
@@ -381,9 +738,13 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
     }
   }
   __syncthreads();
+  const bool sel_dma = kl.sel != nullptr;   // CSA: selection slots come from idx
+  if (sel_dma && threadIdx.x < 64) dma_sel<TK>(kl, k0 + (kAhead + 1) * TK, ke, s_sel[(kAhead + 1) & 1]);
+  // Every tile issues exactly kDmaOps DMA instructions per wave (tiles past the end copy the zero
+  // row), so the count of outstanding loads is the same on every path and the waits below stay
+  // exact.
 #pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (k0 + j * TK < ke) dma_tile<TK>(rbases, s_code[j], kv[j]);
+  for (int j = 0; j < kAhead; ++j) dma_tile<TK>(s_addr[j], kv[j]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -405,17 +766,44 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
 
   // One tile: compute from `cbuf` while the next tile streams into `nbuf`.
   // One tile: compute from `cbuf` while tile t + kAhead streams into `nbuf`.
-  auto tile = [&](const char* __restrict__ cbuf, char* __restrict__ nbuf, int64_t t0, int it) {
+  // The buffers are restrict-qualified so that the compiler knows that reading the current tile or
+  // the P exchange never has to wait for the DMA into `nbuf`.
+  auto tile = [&](const char* __restrict__ cbuf, char* __restrict__ nbuf, char* __restrict__ pbuf,
+                  int64_t t0, int it) {
     const int slot = it % kSlots;
     const int* codes = s_code[slot];
-    // The list entries of tile t + kAhead + 1 are fetched first (their wait comes at the end of the
-    // tile), then tile t + kAhead streams into its buffer.
-    const int64_t kk2 = t0 + (kAhead + 1) * TK + threadIdx.x;
-    int raw2 = -1;
-    if (threadIdx.x < TK) raw2 = key_prefetch(a, kl, kk2, ke);
-    const bool dma_now = t0 + kAhead * TK < ke;
-    if (dma_now) dma_tile<TK>(rbases, s_code[(it + kAhead) % kSlots], nbuf);
+    // DMA issued from inside the QK block: the selection slots of tile t + kAhead + 2 (every wave
+    // copies the same values), then this wave's rows of tile t + kAhead. Per wave and tile that is
+    // 1 + kDmaOps instructions, in this order.
+    TileDma<TK / 4, TK / 32> dma;
+    {
+      const int64_t kk = t0 + (kAhead + 2) * TK + lane;
+      dma.sel = (sel_dma && lane < TK && kk < ke && kk < kl.n_sel)
+                    ? reinterpret_cast<const char*>(kl.sel + kk)
+                    : reinterpret_cast<const char*>(kZeroRow);
+      const KeyAddr* ad = s_addr[(it + kAhead) % kSlots];
+      const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
+      const uint32_t off0 = 16 * (lane ^ swz(w)), off1 = 16 * (lane ^ swz(w + 4));
+#pragma unroll
+      for (int j = 0; j < TK / 4; ++j) {
+        const uint64_t base =
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uintptr_t)mine, j)) |
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uintptr_t)mine >> 32), j)
+             << 32);
+        dma.lat[j] = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < TK / 32; ++jj) {
+        const int r = 8 * (w + 4 * jj) + (lane >> 3);
+        dma.rope[jj] = ad[r].rope + 16 * ((lane & 7) ^ swz(r));
+      }
+      // Wave-uniform LDS targets, made scalar for the block's M0 writes.
+      dma.m0_rows = __builtin_amdgcn_readfirstlane(lds_addr(nbuf) + 1024 * w);
+      dma.m0_sel = __builtin_amdgcn_readfirstlane(
+          lds_addr(reinterpret_cast<const char*>(s_sel[(it + kAhead + 2) & 1])));
+    }
 
+    v2i vraw[kNV > 0 ? 2 * kNV : 1];   // the tile's V^T fragments, fetched by the QK block
     // ---- QK: S^T = K . Q^T for key block kb; latent k-steps 0..31 (chunk 2 s + hi), RoPE 32..35.
     floatx16 acc;
     {
@@ -433,7 +821,8 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
         lb[t] = lat + 32 * (t ^ (f >> 1));
         rb[t] = rope + 32 * (t ^ (f >> 1));
       }
-      acc = qk_chain(qb, lb, rb);
+      acc = qk_chain<kQA, kNV, TK / 4, TK / 32, TK>(qb, lb, rb, lds_addr(cbuf) + v_even,
+                                                    lds_addr(cbuf) + v_odd, vraw, dma);
     }
 
     if (!s_full[slot]) {            // empty slots (a partial tile, -1 selections): no logit
@@ -476,26 +865,33 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        *reinterpret_cast<f16x8*>(s_p + (((2 * kb + s) * RG + rg) * 64 + lane) * 16) = ph[s];
+        *reinterpret_cast<f16x8*>(pbuf + (((2 * kb + s) * RG + rg) * 64 + lane) * 16) = ph[s];
     }
     lds_barrier();   // P of the whole tile is in LDS
 
     // ---- PV: O^T[dims 128 w + 32 mt, heads 32 r] += V^T . P^T over the tile's k-steps.
+    static_assert(kPSteps * RG == 8, "eight P fragments per tile");
+    v4i pall[8];
+    load_p8(lds_addr(pbuf) + lane * 16, pall);
 #pragma unroll
     for (int ks = 0; ks < kPSteps; ++ks) {
       f16x8 pf[RG];
 #pragma unroll
-      for (int r = 0; r < RG; ++r)
-        pf[r] = *reinterpret_cast<const f16x8*>(s_p + ((ks * RG + r) * 64 + lane) * 16);
+      for (int r = 0; r < RG; ++r) pf[r] = __builtin_bit_cast(f16x8, pall[ks * RG + r]);
       const int koff = (ks >> 1) * 32 * 1024 + (ks & 1) * 16384;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const char* b0 = cbuf + ((mt & 1) ? v_odd : v_even) + 64 * mt + koff;
-        const uint2 x0 = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const lds_char*)b0));
-        const uint2 x1 = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                       (lds_short4*)(const lds_char*)(b0 + 8 * 1024)));
+        uint2 x0, x1;
+        if constexpr (kNV > 0) {
+          x0 = __builtin_bit_cast(uint2, vraw[2 * (4 * ks + mt)]);
+          x1 = __builtin_bit_cast(uint2, vraw[2 * (4 * ks + mt) + 1]);
+        } else {
+          const char* b0 = cbuf + ((mt & 1) ? v_odd : v_even) + 64 * mt + koff;
+          x0 = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(const lds_char*)b0));
+          x1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (lds_short4*)(const lds_char*)(b0 + 8 * 1024)));
+        }
         const f16x8 vf = bf16x8_to_f16(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
         for (int r = 0; r < RG; ++r)
@@ -503,9 +899,16 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
       }
     }
     if (threadIdx.x < 64) {
+      // Codes of tile t + kAhead + 1 (its selection slots landed with the DMA of tile t + kAhead - 1,
+      // which this wave has waited for).
+      const int64_t kk2 = t0 + (kAhead + 1) * TK + threadIdx.x;
+      const int raw2 = sel_dma ? s_sel[(it + kAhead + 1) & 1][threadIdx.x] : 0;
       const int c2 = threadIdx.x < TK ? key_code_of(kl, kk2, raw2, ke) : -1;
       const int slot2 = (it + kAhead + 1) % kSlots;
-      if (threadIdx.x < TK) s_code[slot2][threadIdx.x] = c2;
+      if (threadIdx.x < TK) {
+        s_code[slot2][threadIdx.x] = c2;
+        s_addr[slot2][threadIdx.x] = key_addr(rbases, c2);
+      }
       const bool h2 = __any(c2 >= 0);
       const bool f2 = __all(c2 >= 0 || threadIdx.x >= TK);
       if (threadIdx.x == 0) {
@@ -513,17 +916,16 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
         s_full[slot2] = f2;
       }
     }
-    // This wave's DMA of tile t + 1 has landed once at most the kDmaOps instructions of tile
-    // t + kAhead are outstanding (vector memory operations complete in order).
-    if (kAhead > 1 && dma_now)
-      __builtin_amdgcn_s_waitcnt(kVmcntDma<kDmaOps>);
-    else
-      __builtin_amdgcn_s_waitcnt(0);
+    // This wave's DMA of tile t + 1 (and the selection slots issued with it) has landed once at most
+    // the DMA instructions issued in the last kAhead - 1 tiles are outstanding (vector memory
+    // operations complete in order).
+    __builtin_amdgcn_s_waitcnt(kVmcntDma<(kAhead - 1) * (kDmaOps + 1)>);
     lds_barrier();                   // every wave is done with this tile and with s_p
   };
   int it = 0;
   for (int64_t t0 = k0; t0 < ke; t0 += TK, ++it)
-    tile(kv[it % NBUF], kv[(it + kAhead) % NBUF], t0, it);
+    tile(kv[it % NBUF], kv[(it + kAhead) % NBUF], s_p, t0, it);
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA may land in LDS after the workgroup has finished
 
   // Row sums of each key block and the reference maxima go through LDS to the PV layout.
   l_run += __shfl_xor(l_run, 32);
