@@ -202,7 +202,8 @@ __device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int ra
 //
 // The DMA of a later tile is issued between the MFMAs (so the wave never stalls on the load path
 // while the matrix unit idles): the selection slots (4 bytes per lane), then this wave's latent
-// rows and RoPE row groups (TileDma). These write LDS only; the caller waits for them by count.
+// rows (scalar row base + per-lane offset) and RoPE row groups (TileDma). These write LDS only;
+// the caller waits for them by count.
 // The block sets M0; no M0 value of the compiler's is live across it (the loop issues no other
 // DMA).
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -211,7 +212,8 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 template <int NLAT, int NROPE>
 struct TileDma {
   const char* sel;          // per-lane source of the selection slots
-  const char* lat[NLAT];    // per-lane sources of this wave's latent rows
+  const char* lat[NLAT];    // wave-uniform row addresses of this wave's latent rows
+  uint32_t off[2];          // per-lane byte offsets within a row: rows 4 j + w for even / odd j
   const char* rope[NROPE];  // per-lane sources of this wave's RoPE row groups
   int m0_rows;              // LDS address of this wave's first latent row in the target buffer
   int m0_sel;               // LDS address of the selection slot
@@ -233,155 +235,155 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %38, 0\n"
       "ds_read_b128 %5, %74 offset:128\n"
-      "s_mov_b32 m0, %104\n"
+      "s_mov_b32 m0, %106\n"
       "s_nop 0\n"
       "global_load_lds_dword %84, off\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %39, %0\n"
       "ds_read_b128 %1, %75 offset:128\n"
-      "s_add_u32 m0, %103, 0\n"
+      "s_add_u32 m0, %105, 0\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %85, off\n"
+      "global_load_lds_dwordx4 %101, %85\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %40, %0\n"
       "ds_read_b128 %2, %76 offset:128\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %41, %0\n"
       "ds_read_b128 %3, %77 offset:128\n"
-      "s_add_u32 m0, %103, 4096\n"
+      "s_add_u32 m0, %105, 4096\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, off\n"
+      "global_load_lds_dwordx4 %102, %86\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %42, %0\n"
       "ds_read_b128 %4, %74 offset:256\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %43, %0\n"
       "ds_read_b128 %5, %75 offset:256\n"
-      "s_add_u32 m0, %103, 8192\n"
+      "s_add_u32 m0, %105, 8192\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %87, off\n"
+      "global_load_lds_dwordx4 %101, %87\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %44, %0\n"
       "ds_read_b128 %1, %76 offset:256\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %45, %0\n"
       "ds_read_b128 %2, %77 offset:256\n"
-      "s_add_u32 m0, %103, 12288\n"
+      "s_add_u32 m0, %105, 12288\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %88, off\n"
+      "global_load_lds_dwordx4 %102, %88\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %46, %0\n"
       "ds_read_b128 %3, %74 offset:384\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %47, %0\n"
       "ds_read_b128 %4, %75 offset:384\n"
-      "s_add_u32 m0, %103, 16384\n"
+      "s_add_u32 m0, %105, 16384\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, off\n"
+      "global_load_lds_dwordx4 %101, %89\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %48, %0\n"
       "ds_read_b128 %5, %76 offset:384\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %49, %0\n"
       "ds_read_b128 %1, %77 offset:384\n"
-      "s_add_u32 m0, %103, 20480\n"
+      "s_add_u32 m0, %105, 20480\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %90, off\n"
+      "global_load_lds_dwordx4 %102, %90\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %50, %0\n"
       "ds_read_b128 %2, %74 offset:512\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %51, %0\n"
       "ds_read_b128 %3, %75 offset:512\n"
-      "s_add_u32 m0, %103, 24576\n"
+      "s_add_u32 m0, %105, 24576\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %91, off\n"
+      "global_load_lds_dwordx4 %101, %91\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %52, %0\n"
       "ds_read_b128 %4, %76 offset:512\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %53, %0\n"
       "ds_read_b128 %5, %77 offset:512\n"
-      "s_add_u32 m0, %103, 28672\n"
+      "s_add_u32 m0, %105, 28672\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %92, off\n"
+      "global_load_lds_dwordx4 %102, %92\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %54, %0\n"
       "ds_read_b128 %1, %74 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %55, %0\n"
       "ds_read_b128 %2, %75 offset:640\n"
-      "s_add_u32 m0, %103, 32768\n"
+      "s_add_u32 m0, %105, 32768\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %93, off\n"
+      "global_load_lds_dwordx4 %101, %93\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %56, %0\n"
       "ds_read_b128 %3, %76 offset:640\n"
-      "s_add_u32 m0, %103, 36864\n"
+      "s_add_u32 m0, %105, 36864\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %94, off\n"
+      "global_load_lds_dwordx4 %102, %94\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %57, %0\n"
       "ds_read_b128 %4, %77 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %58, %0\n"
       "ds_read_b128 %5, %74 offset:768\n"
-      "s_add_u32 m0, %103, 40960\n"
+      "s_add_u32 m0, %105, 40960\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %95, off\n"
+      "global_load_lds_dwordx4 %101, %95\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %59, %0\n"
       "ds_read_b128 %1, %75 offset:768\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %60, %0\n"
       "ds_read_b128 %2, %76 offset:768\n"
-      "s_add_u32 m0, %103, 45056\n"
+      "s_add_u32 m0, %105, 45056\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %96, off\n"
+      "global_load_lds_dwordx4 %102, %96\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %61, %0\n"
       "ds_read_b128 %3, %77 offset:768\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %62, %0\n"
       "ds_read_b128 %4, %74 offset:896\n"
-      "s_add_u32 m0, %103, 49152\n"
+      "s_add_u32 m0, %105, 49152\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %97, off\n"
+      "global_load_lds_dwordx4 %101, %97\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %63, %0\n"
       "ds_read_b128 %5, %75 offset:896\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %64, %0\n"
       "ds_read_b128 %1, %76 offset:896\n"
-      "s_add_u32 m0, %103, 53248\n"
+      "s_add_u32 m0, %105, 53248\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %98, off\n"
+      "global_load_lds_dwordx4 %102, %98\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %65, %0\n"
       "ds_read_b128 %2, %77 offset:896\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %66, %0\n"
       "ds_read_b128 %3, %78\n"
-      "s_add_u32 m0, %103, 57344\n"
+      "s_add_u32 m0, %105, 57344\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %99, off\n"
+      "global_load_lds_dwordx4 %101, %99\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %67, %0\n"
       "ds_read_b128 %4, %79\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %68, %0\n"
       "ds_read_b128 %5, %80\n"
-      "s_add_u32 m0, %103, 61440\n"
+      "s_add_u32 m0, %105, 61440\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %100, off\n"
+      "global_load_lds_dwordx4 %102, %100\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %69, %0\n"
       "ds_read_b128 %1, %81\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %70, %0\n"
-      "s_add_u32 m0, %103, 65536\n"
+      "s_add_u32 m0, %105, 65536\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %101, off\n"
+      "global_load_lds_dwordx4 %103, off\n"
       "ds_read_b64_tr_b16 %6, %82 offset:0\n"
       "ds_read_b64_tr_b16 %7, %82 offset:8192\n"
       "ds_read_b64_tr_b16 %8, %83 offset:64\n"
@@ -398,9 +400,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "ds_read_b64_tr_b16 %17, %83 offset:24640\n"
       "s_waitcnt lgkmcnt(13)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %72, %0\n"
-      "s_add_u32 m0, %103, 69632\n"
+      "s_add_u32 m0, %105, 69632\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %102, off\n"
+      "global_load_lds_dwordx4 %104, off\n"
       "ds_read_b64_tr_b16 %18, %82 offset:16512\n"
       "ds_read_b64_tr_b16 %19, %82 offset:24704\n"
       "s_waitcnt lgkmcnt(14)\n"
@@ -430,7 +432,7 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
                  : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]), "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]), "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
                  : "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "a"(q[4]), "a"(q[5]), "a"(q[6]), "a"(q[7]), "a"(q[8]), "a"(q[9]), "a"(q[10]), "a"(q[11]), "a"(q[12]), "a"(q[13]), "a"(q[14]), "a"(q[15]), "a"(q[16]), "a"(q[17]), "a"(q[18]), "a"(q[19]), "a"(q[20]), "a"(q[21]), "a"(q[22]), "a"(q[23]), "a"(q[24]), "a"(q[25]), "a"(q[26]), "a"(q[27]), "a"(q[28]), "a"(q[29]), "a"(q[30]), "a"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]),
                    "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]),
-                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "v"(dma.lat[0]), "v"(dma.lat[1]), "v"(dma.lat[2]), "v"(dma.lat[3]), "v"(dma.lat[4]), "v"(dma.lat[5]), "v"(dma.lat[6]), "v"(dma.lat[7]), "v"(dma.lat[8]), "v"(dma.lat[9]), "v"(dma.lat[10]), "v"(dma.lat[11]), "v"(dma.lat[12]), "v"(dma.lat[13]), "v"(dma.lat[14]), "v"(dma.lat[15]), "v"(dma.rope[0]), "v"(dma.rope[1]), "s"(dma.m0_rows), "s"(dma.m0_sel)
+                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "s"(dma.lat[0]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "s"(dma.lat[8]), "s"(dma.lat[9]), "s"(dma.lat[10]), "s"(dma.lat[11]), "s"(dma.lat[12]), "s"(dma.lat[13]), "s"(dma.lat[14]), "s"(dma.lat[15]), "v"(dma.off[0]), "v"(dma.off[1]), "v"(dma.rope[0]), "v"(dma.rope[1]), "s"(dma.m0_rows), "s"(dma.m0_sel)
                  : "m0");
   } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {
     asm volatile(
@@ -441,7 +443,7 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %6, 0\n"
       "ds_read_b128 %5, %42 offset:128\n"
-      "s_mov_b32 m0, %63\n"
+      "s_mov_b32 m0, %65\n"
       "s_nop 0\n"
       "global_load_lds_dword %52, off\n"
       "s_waitcnt lgkmcnt(3)\n"
@@ -453,9 +455,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %9, %0\n"
       "ds_read_b128 %3, %45 offset:128\n"
-      "s_add_u32 m0, %62, 0\n"
+      "s_add_u32 m0, %64, 0\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %53, off\n"
+      "global_load_lds_dwordx4 %61, %53\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %10, %0\n"
       "ds_read_b128 %4, %42 offset:256\n"
@@ -468,9 +470,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %13, %0\n"
       "ds_read_b128 %2, %45 offset:256\n"
-      "s_add_u32 m0, %62, 4096\n"
+      "s_add_u32 m0, %64, 4096\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %54, off\n"
+      "global_load_lds_dwordx4 %62, %54\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %14, %0\n"
       "ds_read_b128 %3, %42 offset:384\n"
@@ -480,9 +482,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %16, %0\n"
       "ds_read_b128 %5, %44 offset:384\n"
-      "s_add_u32 m0, %62, 8192\n"
+      "s_add_u32 m0, %64, 8192\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %55, off\n"
+      "global_load_lds_dwordx4 %61, %55\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %17, %0\n"
       "ds_read_b128 %1, %45 offset:384\n"
@@ -495,9 +497,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %20, %0\n"
       "ds_read_b128 %4, %44 offset:512\n"
-      "s_add_u32 m0, %62, 12288\n"
+      "s_add_u32 m0, %64, 12288\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %56, off\n"
+      "global_load_lds_dwordx4 %62, %56\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %21, %0\n"
       "ds_read_b128 %5, %45 offset:512\n"
@@ -510,9 +512,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %24, %0\n"
       "ds_read_b128 %3, %44 offset:640\n"
-      "s_add_u32 m0, %62, 16384\n"
+      "s_add_u32 m0, %64, 16384\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %57, off\n"
+      "global_load_lds_dwordx4 %61, %57\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %25, %0\n"
       "ds_read_b128 %4, %45 offset:640\n"
@@ -522,9 +524,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %27, %0\n"
       "ds_read_b128 %1, %43 offset:768\n"
-      "s_add_u32 m0, %62, 20480\n"
+      "s_add_u32 m0, %64, 20480\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %58, off\n"
+      "global_load_lds_dwordx4 %62, %58\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
       "ds_read_b128 %2, %44 offset:768\n"
@@ -537,9 +539,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %1, %31, %0\n"
       "ds_read_b128 %5, %43 offset:896\n"
-      "s_add_u32 m0, %62, 24576\n"
+      "s_add_u32 m0, %64, 24576\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %59, off\n"
+      "global_load_lds_dwordx4 %61, %59\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %32, %0\n"
       "ds_read_b128 %1, %44 offset:896\n"
@@ -549,9 +551,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %34, %0\n"
       "ds_read_b128 %3, %46\n"
-      "s_add_u32 m0, %62, 28672\n"
+      "s_add_u32 m0, %64, 28672\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %60, off\n"
+      "global_load_lds_dwordx4 %62, %60\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %5, %35, %0\n"
       "ds_read_b128 %4, %47\n"
@@ -563,9 +565,9 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
       "ds_read_b128 %1, %49\n"
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %3, %38, %0\n"
-      "s_add_u32 m0, %62, 32768\n"
+      "s_add_u32 m0, %64, 32768\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %61, off\n"
+      "global_load_lds_dwordx4 %63, off\n"
       "s_waitcnt lgkmcnt(2)\n"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %39, %0\n"
       "s_waitcnt lgkmcnt(1)\n"
@@ -578,7 +580,7 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
                  : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
                  : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]),
                    "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]),
-                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "v"(dma.lat[0]), "v"(dma.lat[1]), "v"(dma.lat[2]), "v"(dma.lat[3]), "v"(dma.lat[4]), "v"(dma.lat[5]), "v"(dma.lat[6]), "v"(dma.lat[7]), "v"(dma.rope[0]), "s"(dma.m0_rows), "s"(dma.m0_sel)
+                   "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "s"(dma.lat[0]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "v"(dma.off[0]), "v"(dma.off[1]), "v"(dma.rope[0]), "s"(dma.m0_rows), "s"(dma.m0_sel)
                  : "m0");
   } else {
     static_assert(QA && NV == 16, "unsupported configuration");
@@ -651,6 +653,18 @@ __device__ __forceinline__ void load_p8(int addr, v4i (&p)[8]) {
       "ds_read_b128 %7, %8 offset:7168\n"
       "s_waitcnt lgkmcnt(0)\n"
       : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]), "=v"(p[7])
+      : "v"(addr));
+}
+
+// Four P^T fragments (consecutive 1 KB slots from addr), read in one block that waits for them.
+__device__ __forceinline__ void load_p4(int addr, v4i (&p)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n"
+      "ds_read_b128 %1, %4 offset:1024\n"
+      "ds_read_b128 %2, %4 offset:2048\n"
+      "ds_read_b128 %3, %4 offset:3072\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3])
       : "v"(addr));
 }
 
@@ -783,14 +797,15 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
                     : reinterpret_cast<const char*>(kZeroRow);
       const KeyAddr* ad = s_addr[(it + kAhead) % kSlots];
       const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
-      const uint32_t off0 = 16 * (lane ^ swz(w)), off1 = 16 * (lane ^ swz(w + 4));
+      dma.off[0] = 16 * (lane ^ swz(w));
+      dma.off[1] = 16 * (lane ^ swz(w + 4));
 #pragma unroll
       for (int j = 0; j < TK / 4; ++j) {
         const uint64_t base =
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uintptr_t)mine, j)) |
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uintptr_t)mine >> 32), j)
              << 32);
-        dma.lat[j] = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
+        dma.lat[j] = reinterpret_cast<const char*>(base);
       }
 #pragma unroll
       for (int jj = 0; jj < TK / 32; ++jj) {
@@ -871,13 +886,17 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
 
     // ---- PV: O^T[dims 128 w + 32 mt, heads 32 r] += V^T . P^T over the tile's k-steps.
     static_assert(kPSteps * RG == 8, "eight P fragments per tile");
-    v4i pall[8];
-    load_p8(lds_addr(pbuf) + lane * 16, pall);
+    // 64-head groups read all eight P^T fragments at once; 128-head groups (short of vector
+    // registers) read the four of each k-step.
+    v4i pall[RG == 2 ? 8 : 4];
+    if constexpr (RG == 2) load_p8(lds_addr(pbuf) + lane * 16, pall);
 #pragma unroll
     for (int ks = 0; ks < kPSteps; ++ks) {
+      if constexpr (RG == 4) load_p4(lds_addr(pbuf) + lane * 16 + 4096 * ks, pall);
       f16x8 pf[RG];
 #pragma unroll
-      for (int r = 0; r < RG; ++r) pf[r] = __builtin_bit_cast(f16x8, pall[ks * RG + r]);
+      for (int r = 0; r < RG; ++r)
+        pf[r] = __builtin_bit_cast(f16x8, pall[(RG == 2 ? ks * RG : 0) + r]);
       const int koff = (ks >> 1) * 32 * 1024 + (ks & 1) * 16384;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
