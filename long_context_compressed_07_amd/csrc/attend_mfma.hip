@@ -416,25 +416,36 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
 }
 
 // Work decomposition. bf16 caches with a multiple of 64 heads take the DMA kernel
-// (attend_bf16.hip): one workgroup per query and group of 64 or 128 heads. Everything else takes
-// the fp16-staging kernel here: many queries (prefill) give one workgroup per query and head group,
-// 4 head groups sharing each staged tile (ksw 1) or 2 head groups x 2 key halves (ksw 2); few
-// queries (decode) take ksw 4, one 32-head group each. When there are too few workgroups to fill
-// the chip, each query's keys are also split over workgroups (n_split), merged by combine_kernel.
-MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
+// (attend_bf16.hip): one workgroup per query and group of 64 or 128 heads. fp8 caches with a
+// multiple of 128 heads take the fp8 DMA kernel (attend_fp8.hip): one workgroup per query and
+// group of 128 heads. Everything else takes the fp16-staging kernel here: many queries (prefill)
+// give one workgroup per query and head group, 4 head groups sharing each staged tile (ksw 1) or
+// 2 head groups x 2 key halves (ksw 2); few queries (decode) take ksw 4, one 32-head group each.
+// When there are too few workgroups to fill the chip, each query's keys are also split over
+// workgroups (n_split), merged by combine_kernel.
+enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
+
+MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
   MfmaPlan p{};
   const int groups32 = H / 32;
   const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
-  auto splits_for = [&](int64_t wgs_per_split) {
+  auto splits_for = [&](int64_t wgs_per_split, int64_t cap_) {
     const int64_t wgs = (int64_t)nq * wgs_per_split;
     const int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-    return (int)(ns < cap ? ns : cap);
+    return (int)(ns < cap_ ? ns : cap_);
   };
-  if (bf16 && groups32 % 2 == 0) {
+  if (kind == kPlanBf16 && groups32 % 2 == 0) {
     p.bf16_dma = 1;
     p.rg = groups32 % 4 == 0 ? 4 : 2;
     p.head_groups = groups32 / p.rg;
-    p.n_split = splits_for(p.head_groups);
+    p.n_split = splits_for(p.head_groups, cap);
+    return p;
+  }
+  if (kind == kPlanF8 && groups32 % 4 == 0) {
+    p.f8_dma = 1;
+    p.rg = 4;
+    p.head_groups = groups32 / 4;
+    p.n_split = splits_for(p.head_groups, max_keys / 128 > 1 ? max_keys / 128 : 1);
     return p;
   }
   if (groups32 % 4 == 0 && (int64_t)nq * (groups32 / 4) >= 512) {
@@ -448,9 +459,21 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, bool bf16) {
   } else {
     p.ksw = 4;
     p.head_groups = groups32;
-    p.n_split = splits_for(p.head_groups);
+    p.n_split = splits_for(p.head_groups, cap);
   }
   return p;
+}
+
+// Which kernel a call takes.
+int plan_kind(const AttendArgs& a) {
+  const bool win = !a.dense && a.window > 0 && a.raw.c != nullptr;
+  if (a.ent.dtype == CSA_BF16 && (!win || a.raw.dtype == CSA_BF16)) return kPlanBf16;
+  if (a.ent.dtype == CSA_E4M3 && (!win || a.raw.dtype == CSA_E4M3) && a.ent.ld_c % 16 == 0 &&
+      (!win || a.raw.ld_c % 16 == 0) &&
+      (reinterpret_cast<uintptr_t>(a.ent.c) & 15) == 0 &&
+      (!win || (reinterpret_cast<uintptr_t>(a.raw.c) & 15) == 0))
+    return kPlanF8;
+  return kPlanStaging;
 }
 
 }  // namespace
@@ -472,13 +495,18 @@ static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
   return (size_t)nq * p.head_groups * p.n_split * sizeof(int);
 }
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
-  const MfmaPlan pa = make_plan(nq, H, max_keys, true), pb = make_plan(nq, H, max_keys, false);
-  const size_t part = std::max(plan_partial_bytes(pa, nq, H), plan_partial_bytes(pb, nq, H));
-  return part + std::max(plan_flag_bytes(pa, nq), plan_flag_bytes(pb, nq));
+  // The dtypes are not part of the workspace query: cover every plan kind.
+  size_t part = 0, flags = 0;
+  for (int kind = 0; kind < 3; ++kind) {
+    const MfmaPlan p = make_plan(nq, H, max_keys, kind);
+    part = std::max(part, plan_partial_bytes(p, nq, H));
+    flags = std::max(flags, plan_flag_bytes(p, nq));
+  }
+  return part + flags;
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, a.ent.dtype == CSA_BF16);
+  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
   if (p.n_split > 1) {
     p.ws_o = static_cast<float*>(a.ws);
     p.ws_ml = p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC;
@@ -488,6 +516,9 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   const bool fp8 = a.ent.dtype == CSA_E4M3;
   if (p.bf16_dma) {
     hipError_t e = launch_attend_bf16(a, p, s);
+    if (e != hipSuccess) return e;
+  } else if (p.f8_dma) {
+    hipError_t e = launch_attend_fp8(a, p, s);
     if (e != hipSuccess) return e;
   } else switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
     case 2: attend_mfma_kernel<CSA_BF16, 1><<<grid, 256, 0, s>>>(a, p); break;

@@ -1,0 +1,187 @@
+"""Generates the QK instruction blocks of attend_tile.h (between the GENERATED markers).
+
+The blocks are long, regular instruction sequences (36 MFMAs with K-fragment reads kept four ahead,
+optional transposed V^T reads at the tail, and the next tile's DMA interleaved between the MFMAs);
+writing them by hand would be error-prone, so they are produced here and committed. Run
+`python gen_qk_asm.py` from this directory after changing the sequences below.
+"""
+from __future__ import annotations
+
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TARGET = os.path.join(HERE, "attend_tile.h")
+NL = "\\n"
+N = 36      # k-steps of a 576-dim row (16 dims each)
+D = 4       # K-fragment reads in flight
+T = 5       # rotating K-fragment registers
+
+
+class Ops:
+    """Operand numbering of one asm statement."""
+
+    def __init__(self):
+        self.n = 0
+        self.outs, self.ins = [], []
+
+    def out(self, expr, cons="=&v"):
+        self.outs.append('"%s"(%s)' % (cons, expr))
+        self.n += 1
+        return "%%%d" % (self.n - 1)
+
+    def inp(self, expr, cons="v"):
+        self.ins.append((cons, expr))
+        return None  # numbered after outputs
+
+
+def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v):
+    """Returns (asm text lines, outputs, inputs) for one QK block.
+
+    dmas: list of DMA ops, each (m0_operand, m0_imm, load_mnemonic, addr_operands) where operands
+    are symbolic names resolved below."""
+    outs = ["acc", "t0", "t1", "t2", "t3", "t4"] + ["vr[%d]" % i for i in range(2 * nv)]
+    ins = [("q[%d]" % i, q_lat_cons if i < 32 else "v") for i in range(36)]
+    ins += [("lb[%d]" % i, "v") for i in range(4)] + [("rb[%d]" % i, "v") for i in range(4)]
+    if nv:
+        ins += [("ve", "v"), ("vo", "v")]
+    dma_names = []
+    for d in dmas:
+        for name, cons in d[3]:
+            if (name, cons) not in dma_names:
+                dma_names.append((name, cons))
+        if (d[0], "s") not in dma_names:
+            dma_names.append((d[0], "s"))
+    ins += dma_names
+    num = {}
+    for i, o in enumerate(outs):
+        num[o] = i
+    for j, (name, _) in enumerate(ins):
+        num[name] = len(outs) + j
+
+    def op(x):
+        return "%%%d" % num[x]
+
+    L = []
+
+    def emit(x):
+        L.append('"%s%s"' % (x, NL))
+
+    t = ["t0", "t1", "t2", "t3", "t4"]
+    for j in range(D):
+        emit("ds_read_b128 %s, %s" % (op(t[j]), op("lb[%d]" % j)))
+    vreads = []
+    for f in range(nv):
+        ks, mt = f // 4, f % 4
+        koff = (ks >> 1) * 32 * 1024 + (ks & 1) * 16384
+        base = "vo" if (mt & 1) else "ve"
+        off = 64 * mt + koff
+        vreads.append("ds_read_b64_tr_b16 %s, %s offset:%d" % (op("vr[%d]" % (2 * f)), op(base), off))
+        vreads.append("ds_read_b64_tr_b16 %s, %s offset:%d"
+                      % (op("vr[%d]" % (2 * f + 1)), op(base), off + 8192))
+    plan = {32: 6, 33: 6, 34: 2}   # V^T reads after these MFMAs (lgkmcnt stays <= 15)
+    nd = len(dmas)
+    place = [min(N - 1, (i * N) // nd) for i in range(nd)]
+    issued_tr = 0
+    di = 0
+    for st in range(N):
+        kissued = min(N, st + D)
+        allowed = (kissued - st - 1) + issued_tr
+        assert allowed <= 15
+        emit("s_waitcnt lgkmcnt(%d)" % allowed)
+        src = "0" if st == 0 else op("acc")
+        emit("%s %s, %s, %s, %s" % (mnemonic, op("acc"), op(t[st % T]), op("q[%d]" % st), src))
+        nx = st + D
+        if nx < N:
+            if nx < 32:
+                emit("ds_read_b128 %s, %s offset:%d" % (op(t[nx % T]), op("lb[%d]" % (nx & 3)),
+                                                        128 * (nx >> 2)))
+            else:
+                emit("ds_read_b128 %s, %s" % (op(t[nx % T]), op("rb[%d]" % (nx & 3))))
+        while di < nd and place[di] == st:
+            m0, imm, ld, addr = dmas[di]
+            if imm:
+                emit("s_add_u32 m0, %s, %d" % (op(m0), imm))
+            else:
+                emit("s_mov_b32 m0, %s" % op(m0))
+            emit("s_nop 0")
+            emit("%s %s" % (ld, ", ".join(op(a) if not a.startswith("off") else a
+                                          for a in [x[0] for x in addr] + (["off"] if len(addr) == 1 else []))))
+            di += 1
+        k = plan.get(st, 0) if nv else 0
+        if st == N - 1 and nv:
+            k = len(vreads) - issued_tr
+        for _ in range(min(k, len(vreads) - issued_tr)):
+            emit(vreads[issued_tr])
+            issued_tr += 1
+    assert di == nd
+    if nv:
+        emit("s_waitcnt lgkmcnt(0)")
+    emit("s_nop 7")
+    emit("s_nop 7")
+    emit("s_nop 4")
+    out_s = ", ".join('"=&v"(%s)' % o for o in outs)
+    in_s = ", ".join('"%s"(%s)' % (c, n) for n, c in ins)
+    text = "    asm volatile(\n      " + "\n      ".join(L) + "\n      : " + out_s + "\n      : " + \
+        in_s + "\n      : \"m0\");"
+    return text
+
+
+def bf16_dmas(nlat, nrope, tk):
+    d = [("dma.m0_sel", 0, "global_load_lds_dword", [("dma.sel", "v")])]
+    for j in range(nlat):
+        d.append(("dma.m0_rows", 4096 * j, "global_load_lds_dwordx4",
+                  [("dma.off[%d]" % (j & 1), "v"), ("dma.lat[%d]" % j, "s")]))
+    for jj in range(nrope):
+        d.append(("dma.m0_rows", tk * 1024 + 4096 * jj, "global_load_lds_dwordx4",
+                  [("dma.rope[%d]" % jj, "v")]))
+    return d
+
+
+def f8_dmas():
+    d = [("dma.m0_sel", 0, "global_load_lds_dword", [("dma.sel", "v")])]
+    for i in range(4):
+        d.append(("dma.m0_lat", 4096 * i, "global_load_lds_dwordx4", [("dma.lat[%d]" % i, "v")]))
+    d.append(("dma.m0_rope", 0, "global_load_lds_dwordx4", [("dma.rope", "v")]))
+    d.append(("dma.m0_scl", 0, "global_load_lds_dword", [("dma.scl", "v")]))
+    return d
+
+
+def main():
+    src = open(TARGET).read()
+    b0 = src.index("// ---- BEGIN GENERATED QK BLOCKS ----")
+    b1 = src.index("// ---- END GENERATED QK BLOCKS ----")
+    gen = ["// ---- BEGIN GENERATED QK BLOCKS ----",
+           "// (written by gen_qk_asm.py; edit the generator, not these lines)",
+           "template <bool QA, int NV, int NLAT, int NROPE, int TK>",
+           "__device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int (&lb)[4],",
+           "                                             const int (&rb)[4], int ve, int vo,",
+           "                                             v2i (&vr)[NV > 0 ? 2 * NV : 1],",
+           "                                             const TileDma<NLAT, NROPE>& dma) {",
+           "  floatx16 acc;",
+           "  v4i t0, t1, t2, t3, t4;",
+           "  if constexpr (QA && NV == 16 && NLAT == 16 && NROPE == 2 && TK == 64) {",
+           block("v_mfma_f32_32x32x16_bf16", "a", 16, bf16_dmas(16, 2, 64), 64),
+           "  } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {",
+           block("v_mfma_f32_32x32x16_bf16", "v", 0, bf16_dmas(8, 1, 32), 32),
+           "  } else {",
+           "    static_assert(QA && NV == 16, \"unsupported configuration\");",
+           "  }",
+           "  return acc;",
+           "}",
+           "",
+           "__device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const int (&lb)[4],",
+           "                                                 const int (&rb)[4], const TileDmaF8& dma) {",
+           "  floatx16 acc;",
+           "  v4i t0, t1, t2, t3, t4;",
+           block("v_mfma_f32_32x32x16_f16", "v", 0, f8_dmas(), 32),
+           "  return acc;",
+           "}",
+           ""]
+    src = src[:b0] + "\n".join(gen) + src[b1:]
+    open(TARGET, "w").write(src)
+    print("regenerated", TARGET)
+
+
+if __name__ == "__main__":
+    main()

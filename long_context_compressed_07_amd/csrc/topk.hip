@@ -4,12 +4,12 @@
 // Step 3 (only the top-k compressed rows by indexer score enter attention). Ties go to the lower
 // index and the output lists indices in ascending order (this library's reading).
 //
-// Algorithm (integer work only, deterministic). Scores map to order-preserving 32-bit keys held in
-// LDS. A most-significant-digit radix select with 11/11/10-bit digits (2048-bin LDS histograms,
-// threshold bin found by a parallel suffix scan) yields the k-th largest key K and how many keys
-// equal to K are still needed. Compaction keeps every key > K and the lowest-index keys == K: each
-// thread owns a contiguous segment, two block scans give every segment its output offset, and
-// indices are written in ascending order.
+// Algorithm (integer work only, deterministic). Scores map to order-preserving 32-bit keys. Each
+// thread holds a contiguous segment of PER keys in registers. The k-th largest key K is found bit by
+// bit from the top: a candidate value y is kept when at least k keys are >= y, each count taken by
+// wave ballots and a block sum (32 rounds, no atomics, so clustered keys cost nothing extra).
+// Compaction keeps every key > K and the lowest-index keys == K: two block scans give every
+// segment its output offset, and indices are written in ascending order.
 //
 // Rows of up to kChunk visible entries: one workgroup per row. Longer rows: stage 1 runs the same
 // selection on chunks of kChunk entries (many workgroups per row) and writes each chunk's local
@@ -56,67 +56,50 @@ __device__ __forceinline__ int block_scan(int a, int* s_tmp, int& total) {
   return before + ia - a;
 }
 
-// Radix select over n keys in LDS: returns K (the k-th largest key) and, in *need_eq, how many
-// keys equal to K belong to the top k. Requires n > k >= 1.
-template <int NT>
-__device__ uint32_t radix_select(const uint32_t* keys, int n, int k, int* s_hist, int* s_tmp,
-                                 int* need_eq) {
-  constexpr int kBins = 2048;
+// Number of keys >= y over the block (keys beyond the row are 0, below every probed y >= 1).
+template <int NT, int PER>
+__device__ __forceinline__ int block_count_ge(const uint32_t (&kv)[PER], uint32_t y, int* s_cnt) {
   constexpr int NW = NT / kWave;
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-    for (int i = threadIdx.x; i < kBins; i += NT) s_hist[i] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n; j += NT) {
-      const uint32_t key = keys[j];
-      if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & dmask], 1);
-    }
-    __syncthreads();
-    // Threshold bin: the highest bin whose suffix count (bins >= it) reaches `remaining`.
-    // Thread t owns kPer bins counted down from 2047 - kPer t.
-    constexpr int kPer = kBins / NT;
-    int local = 0;
-    const int top = kBins - 1 - kPer * threadIdx.x;
+  int c = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) local += s_hist[top - i];
-    int total;
-    const int before = block_scan<NT>(local, s_tmp, total);
-    if (before < remaining && before + local >= remaining) {
-      int cum = before, bin = top;
-      for (int i = 0; i < kPer - 1; ++i, --bin) {
-        const int c = s_hist[bin];
-        if (cum + c >= remaining) break;
-        cum += c;
-      }
-      s_tmp[NW] = bin;
-      s_tmp[NW + 1] = remaining - cum;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)s_tmp[NW] << shift;
-    pmask |= dmask << shift;
-    remaining = s_tmp[NW + 1];
-    __syncthreads();
+  for (int i = 0; i < PER; ++i) {
+    c += __popcll(__ballot(kv[i] >= y));
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // keep few ballot masks live
   }
-  *need_eq = remaining;
-  return prefix;
+  if ((threadIdx.x & (kWave - 1)) == 0) s_cnt[threadIdx.x / kWave] = c;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) total += s_cnt[w];
+  __syncthreads();
+  return total;
 }
 
-// Writes, in ascending position order, index_of(j) for the positions j of the top k (keys > K and
-// the first need_eq keys == K) into out[0..).
-template <int NT, typename F>
-__device__ void compact(const uint32_t* keys, int n, uint32_t K, int need_eq, int* s_tmp,
-                        F index_of, int32_t* out) {
-  const int seg = (n + NT - 1) / NT;
-  const int j0 = threadIdx.x * seg < n ? threadIdx.x * seg : n;
-  const int j1 = j0 + seg < n ? j0 + seg : n;
+// The k-th largest of the block's keys (1 <= k < number of real keys), and in *need_eq how many keys
+// equal to it belong to the top k.
+template <int NT, int PER>
+__device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* s_cnt, int* need_eq) {
+  uint32_t x = 0;   // invariant: at least k keys are >= x
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t y = x | (1u << bit);
+    if (block_count_ge<NT, PER>(kv, y, s_cnt) >= k) x = y;
+  }
+  *need_eq = k - (x == 0xffffffffu ? 0 : block_count_ge<NT, PER>(kv, x + 1, s_cnt));
+  return x;
+}
+
+// Writes, in ascending position order, index_of(j) for the positions j (j = PER t + i for key
+// kv[i] of thread t) of the top k: keys > K and the first need_eq keys == K.
+template <int NT, int PER, typename F>
+__device__ void compact_regs(const uint32_t (&kv)[PER], uint32_t K, int need_eq,
+                             int* s_tmp, F index_of, int32_t* out) {
+  // Padding keys (0) are below every real key, and K is a real key (>= 1), so they never count.
+  const int j0 = threadIdx.x * PER;
   int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = keys[j];
-    gt += key > K;
-    eq += key == K;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    gt += kv[i] > K;
+    eq += kv[i] == K;
   }
   int total;
   const int eq_before = block_scan<NT>(eq, s_tmp, total);
@@ -124,14 +107,56 @@ __device__ void compact(const uint32_t* keys, int n, uint32_t K, int need_eq, in
   take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
   int off = block_scan<NT>(gt + take_eq, s_tmp, total);
   int eq_left = take_eq;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = keys[j];
-    bool take = key > K;
-    if (key == K && eq_left > 0) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    bool take = kv[i] > K;
+    if (kv[i] == K && eq_left > 0) {
       take = true;
       --eq_left;
     }
-    if (take) out[off++] = index_of(j);
+    if (take) out[off++] = index_of(j0 + i);
+  }
+}
+
+// Loads keys [PER t, PER t + PER) of a row of n scores (0 beyond n): 16-byte loads for whole,
+// aligned segments, element by element only for the segment holding the row's end.
+template <int PER>
+__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[PER]) {
+  const int j0 = threadIdx.x * PER;
+  const float* src = row + j0;
+  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(src)[q];
+      kv[4 * q] = score_key(v.x);
+      kv[4 * q + 1] = score_key(v.y);
+      kv[4 * q + 2] = score_key(v.z);
+      kv[4 * q + 3] = score_key(v.w);
+    }
+  } else {
+    const int m = n - j0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
+  }
+}
+
+// The same from keys already in LDS (n of them).
+template <int PER>
+__device__ __forceinline__ void load_keys_lds(const uint32_t* keys, int n, uint32_t (&kv)[PER]) {
+  const int j0 = threadIdx.x * PER;
+  if (j0 + PER <= n) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(keys + j0)[q];
+      kv[4 * q] = v.x;
+      kv[4 * q + 1] = v.y;
+      kv[4 * q + 2] = v.z;
+      kv[4 * q + 3] = v.w;
+    }
+  } else {
+    const int m = n - j0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kv[i] = i < m ? keys[j0 + i] : 0u;
   }
 }
 
@@ -142,8 +167,7 @@ struct Identity {
 // Single stage: one workgroup per query row (n_vis <= kChunk).
 template <int NT>
 __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
-  __shared__ uint32_t s_keys[kChunk];
-  __shared__ int s_hist[2048];
+  constexpr int PER = kChunk / NT;
   __shared__ int s_tmp[NT / kWave + 2];
   const int qi = blockIdx.x;
   const int n = (int)n_visible(a.Q.pos[qi], a.m, a.N);
@@ -152,12 +176,11 @@ __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
-  const float* row = a.scores + (int64_t)qi * a.ld_scores;
-  for (int j = threadIdx.x; j < n; j += NT) s_keys[j] = score_key(row[j]);
-  __syncthreads();
+  uint32_t kv[PER];
+  load_keys<PER>(a.scores + (int64_t)qi * a.ld_scores, n, kv);
   int need_eq;
-  const uint32_t K = radix_select<NT>(s_keys, n, a.k, s_hist, s_tmp, &need_eq);
-  compact<NT>(s_keys, n, K, need_eq, s_tmp, Identity{}, out);
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
+  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, out);
 }
 
 // Stage 1: chunk c of query row qi; writes the chunk's local top-k (or all of its visible
@@ -166,9 +189,9 @@ template <int NT>
 __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks,
                                                         uint32_t* cand_key, int32_t* cand_idx,
                                                         int* cand_cnt) {
-  __shared__ uint32_t s_keys[kChunk];
-  __shared__ int s_hist[2048];
+  constexpr int PER = kChunk / NT;
   __shared__ int s_tmp[NT / kWave + 2];
+  __shared__ int s_sel[2048];
   const int qi = blockIdx.x / n_chunks;
   const int c = blockIdx.x - qi * n_chunks;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
@@ -178,24 +201,23 @@ __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks
   uint32_t* ok = cand_key + slot * a.k;
   const int n = base >= nv ? 0 : (int)(nv - base < kChunk ? nv - base : kChunk);
   const float* row = a.scores + (int64_t)qi * a.ld_scores + base;
-  for (int j = threadIdx.x; j < n; j += NT) s_keys[j] = score_key(row[j]);
-  __syncthreads();
   if (n <= a.k) {
     for (int j = threadIdx.x; j < n; j += NT) {
       oi[j] = (int32_t)(base + j);
-      ok[j] = s_keys[j];
+      ok[j] = score_key(row[j]);
     }
     if (threadIdx.x == 0) cand_cnt[slot] = n;
     return;
   }
+  uint32_t kv[PER];
+  load_keys<PER>(row, n, kv);
   int need_eq;
-  const uint32_t K = radix_select<NT>(s_keys, n, a.k, s_hist, s_tmp, &need_eq);
-  // The histogram is free now: it receives the selected chunk positions (k <= 2048).
-  compact<NT>(s_keys, n, K, need_eq, s_tmp, Identity{}, s_hist);
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
+  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, s_sel);   // chunk positions
   __syncthreads();
   for (int i = threadIdx.x; i < a.k; i += NT) {
-    const int j = s_hist[i];
-    ok[i] = s_keys[j];
+    const int j = s_sel[i];
+    ok[i] = score_key(row[j]);
     oi[i] = (int32_t)(base + j);
   }
   if (threadIdx.x == 0) cand_cnt[slot] = a.k;
@@ -208,9 +230,12 @@ struct CandIndex {
   int k;
   const int32_t* idx;    // this row's candidate indices, [n_chunks][k]
   __device__ int32_t operator()(int j) const {
-    int c = 0;
-    while (c + 1 < n_chunks && off[c + 1] <= j) ++c;
-    return idx[(int64_t)c * k + (j - off[c])];
+    int lo = 0, hi = n_chunks - 1;   // last chunk c with off[c] <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return idx[(int64_t)lo * k + (j - off[lo])];
   }
 };
 
@@ -221,8 +246,8 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
                                                         const uint32_t* cand_key,
                                                         const int32_t* cand_idx,
                                                         const int* cand_cnt) {
-  extern __shared__ uint32_t s_cand[];          // up to kCandMax keys
-  __shared__ int s_hist[2048];
+  constexpr int PER = 32;
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_cand[];   // up to kCandMax keys
   __shared__ int s_tmp[NT / kWave + 2];
   __shared__ int s_off[64 + 1];
   const int qi = blockIdx.x;
@@ -238,12 +263,6 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   __syncthreads();
   const int n = s_off[n_chunks];
   const int32_t* cidx = cand_idx + (int64_t)qi * n_chunks * a.k;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int cnt = s_off[c + 1] - s_off[c];
-    const uint32_t* src = cand_key + ((int64_t)qi * n_chunks + c) * a.k;
-    for (int i = threadIdx.x; i < cnt; i += NT) s_cand[s_off[c] + i] = src[i];
-  }
-  __syncthreads();
   if (n <= a.k) {   // no more visible entries than k: every candidate, in order
     for (int c = 0; c < n_chunks; ++c) {
       const int cnt = s_off[c + 1] - s_off[c];
@@ -252,9 +271,18 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
     for (int i = n + threadIdx.x; i < a.k; i += NT) out[i] = -1;
     return;
   }
+  // Candidates -> LDS (coalesced), then each thread takes its segment into registers.
+  for (int c = 0; c < n_chunks; ++c) {
+    const int cnt = s_off[c + 1] - s_off[c];
+    const uint32_t* src = cand_key + ((int64_t)qi * n_chunks + c) * a.k;
+    for (int i = threadIdx.x; i < cnt; i += NT) s_cand[s_off[c] + i] = src[i];
+  }
+  __syncthreads();
+  uint32_t kv[PER];
+  load_keys_lds<PER>(s_cand, n, kv);
   int need_eq;
-  const uint32_t K = radix_select<NT>(s_cand, n, a.k, s_hist, s_tmp, &need_eq);
-  compact<NT>(s_cand, n, K, need_eq, s_tmp, CandIndex{s_off, n_chunks, a.k, cidx}, out);
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
+  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, CandIndex{s_off, n_chunks, a.k, cidx}, out);
 }
 
 int n_chunks_for(int64_t N) { return (int)((N + kChunk - 1) / kChunk); }
@@ -286,14 +314,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
                                                                          cand_idx, cand_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)nc * a.k * sizeof(uint32_t);
-  if (lds > 64 * 1024) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel<1024>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  topk_merge_kernel<1024><<<a.Q.nq, 1024, lds, s>>>(a, nc, cand_key, cand_idx, cand_cnt);
-  return hipGetLastError();
+  // Stage 2 block size: 32 candidate keys per thread.
+  const int64_t cand = (int64_t)nc * a.k;
+  const size_t lds = (size_t)cand * sizeof(uint32_t);
+  auto merge = [&](auto kern, int nt) -> hipError_t {
+    if (lds > 64 * 1024) {
+      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e2 != hipSuccess) return e2;
+    }
+    kern<<<a.Q.nq, nt, lds, s>>>(a, nc, cand_key, cand_idx, cand_cnt);
+    return hipGetLastError();
+  };
+  if (cand <= 128 * 32) return merge(&topk_merge_kernel<128>, 128);
+  if (cand <= 256 * 32) return merge(&topk_merge_kernel<256>, 256);
+  if (cand <= 512 * 32) return merge(&topk_merge_kernel<512>, 512);
+  return merge(&topk_merge_kernel<1024>, 1024);
 }
 
 }  // namespace csa
