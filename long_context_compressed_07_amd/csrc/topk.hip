@@ -5,9 +5,10 @@
 // index and the output lists indices in ascending order (this library's reading).
 //
 // Algorithm (integer work only, deterministic). Scores map to order-preserving 32-bit keys. Each
-// thread holds a contiguous segment of PER keys in registers. The k-th largest key K is found bit by
-// bit from the top: a candidate value y is kept when at least k keys are >= y, each count taken by
-// wave ballots and a block sum (32 rounds, no atomics, so clustered keys cost nothing extra).
+// thread holds a contiguous segment of PER keys in registers. The k-th largest key K is found by a
+// three-level radix select over 11-, 11- and 10-bit digits: each level counts, in an LDS histogram,
+// the next digit of the keys that share the digits found so far, and a block scan over the
+// histogram locates the digit of the k-th key and its rank within that digit.
 // Compaction keeps every key > K and the lowest-index keys == K: two block scans give every
 // segment its output offset, and indices are written in ascending order.
 //
@@ -56,43 +57,83 @@ __device__ __forceinline__ int block_scan(int a, int* s_tmp, int& total) {
   return before + ia - a;
 }
 
-// Number of keys >= y over the block (keys beyond the row are 0, below every probed y >= 1).
-template <int NT, int PER>
-__device__ __forceinline__ int block_count_ge(const uint32_t (&kv)[PER], uint32_t y, int* s_cnt) {
-  constexpr int NW = NT / kWave;
-  int c = 0;
+// Radix digits of the k-th key search: bits [31:21], [20:10] and [9:0] of a key.
+constexpr int kHistBins = 2048;   // LDS ints per histogram; two histograms per workgroup
+
+// Given a histogram of NB digit values, finds the digit d holding the kk-th largest key (digits
+// above d hold fewer than kk keys, digits >= d at least kk) and turns kk into the rank of that key
+// among the keys of digit d. Every thread returns the same d and kk.
+template <int NT, int NB>
+__device__ __forceinline__ uint32_t find_digit(const int* hist, int& kk, int* s_tmp) {
+  static_assert(NB % NT == 0, "bins per thread");
+  constexpr int B = NB / NT;
+  int* s_res = s_tmp + NT / kWave;
+  const int t = threadIdx.x;
+  int h[B];
+  int local = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c += __popcll(__ballot(kv[i] >= y));
-    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // keep few ballot masks live
+  for (int b = 0; b < B; ++b) {
+    h[b] = hist[t * B + b];
+    local += h[b];
   }
-  if ((threadIdx.x & (kWave - 1)) == 0) s_cnt[threadIdx.x / kWave] = c;
-  __syncthreads();
-  int total = 0;
+  int total;
+  const int before = block_scan<NT>(local, s_tmp, total);
+  int acc = total - before - local;   // keys in the digits of higher threads
+  if (acc < kk && kk <= acc + local) {
 #pragma unroll
-  for (int w = 0; w < NW; ++w) total += s_cnt[w];
+    for (int b = B - 1; b >= 0; --b) {
+      if (acc < kk && kk <= acc + h[b]) {
+        s_res[0] = t * B + b;
+        s_res[1] = kk - acc;
+      }
+      acc += h[b];
+    }
+  }
   __syncthreads();
-  return total;
+  kk = s_res[1];
+  return (uint32_t)s_res[0];
 }
 
-// The k-th largest of the block's keys (1 <= k < number of real keys), and in *need_eq how many keys
-// equal to it belong to the top k.
+// The k-th largest of the block's keys (1 <= k <= number of real keys; padding keys are 0, below
+// every real key), and in *need_eq how many keys equal to it belong to the top k. Radix select from
+// the top digit down: each level histograms (LDS atomics) the next digit of the keys that share the
+// digits found so far, then locates the k-th key's digit. s_hist holds 2 kHistBins ints; s_tmp
+// holds NT / 64 + 2 ints.
 template <int NT, int PER>
-__device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* s_cnt, int* need_eq) {
-  uint32_t x = 0;   // invariant: at least k keys are >= x
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t y = x | (1u << bit);
-    if (block_count_ge<NT, PER>(kv, y, s_cnt) >= k) x = y;
+__device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* s_hist, int* s_tmp,
+                            int* need_eq) {
+  int* hA = s_hist;
+  int* hB = s_hist + kHistBins;
+  for (int i = threadIdx.x; i < 2 * kHistBins; i += NT) s_hist[i] = 0;
+  __syncthreads();
+  int kk = k;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) atomicAdd(&hA[kv[i] >> 21], 1);
+  __syncthreads();
+  const uint32_t d0 = find_digit<NT, 2048>(hA, kk, s_tmp);
+  for (int i = threadIdx.x; i < 1024; i += NT) hA[i] = 0;   // level 2 reuses hA[0, 1024)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((kv[i] >> 21) == d0) atomicAdd(&hB[(kv[i] >> 10) & 2047u], 1);
   }
-  *need_eq = k - (x == 0xffffffffu ? 0 : block_count_ge<NT, PER>(kv, x + 1, s_cnt));
-  return x;
+  __syncthreads();
+  const uint32_t hi = (d0 << 11) | find_digit<NT, 2048>(hB, kk, s_tmp);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((kv[i] >> 10) == hi) atomicAdd(&hA[kv[i] & 1023u], 1);
+  }
+  __syncthreads();
+  const uint32_t K = (hi << 10) | find_digit<NT, 1024>(hA, kk, s_tmp);
+  *need_eq = kk;
+  return K;
 }
 
 // Writes, in ascending position order, index_of(j) for the positions j (j = PER t + i for key
-// kv[i] of thread t) of the top k: keys > K and the first need_eq keys == K.
+// kv[i] of thread t) of the top k: keys > K and the first need_eq keys == K; with out_key, also
+// the selected keys.
 template <int NT, int PER, typename F>
 __device__ void compact_regs(const uint32_t (&kv)[PER], uint32_t K, int need_eq,
-                             int* s_tmp, F index_of, int32_t* out) {
+                             int* s_tmp, F index_of, int32_t* out, uint32_t* out_key = nullptr) {
   // Padding keys (0) are below every real key, and K is a real key (>= 1), so they never count.
   const int j0 = threadIdx.x * PER;
   int gt = 0, eq = 0;
@@ -114,7 +155,11 @@ __device__ void compact_regs(const uint32_t (&kv)[PER], uint32_t K, int need_eq,
       take = true;
       --eq_left;
     }
-    if (take) out[off++] = index_of(j0 + i);
+    if (take) {
+      out[off] = index_of(j0 + i);
+      if (out_key != nullptr) out_key[off] = kv[i];
+      ++off;
+    }
   }
 }
 
@@ -164,11 +209,17 @@ struct Identity {
   __device__ int32_t operator()(int j) const { return j; }
 };
 
+struct Offset {
+  int32_t base;
+  __device__ int32_t operator()(int j) const { return base + j; }
+};
+
 // Single stage: one workgroup per query row (n_vis <= kChunk).
 template <int NT>
 __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
   constexpr int PER = kChunk / NT;
   __shared__ int s_tmp[NT / kWave + 2];
+  __shared__ int s_hist[2 * kHistBins];
   const int qi = blockIdx.x;
   const int n = (int)n_visible(a.Q.pos[qi], a.m, a.N);
   int32_t* out = a.idx + (int64_t)qi * a.k;
@@ -179,7 +230,7 @@ __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
   uint32_t kv[PER];
   load_keys<PER>(a.scores + (int64_t)qi * a.ld_scores, n, kv);
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
   compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, out);
 }
 
@@ -191,7 +242,7 @@ __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks
                                                         int* cand_cnt) {
   constexpr int PER = kChunk / NT;
   __shared__ int s_tmp[NT / kWave + 2];
-  __shared__ int s_sel[2048];
+  __shared__ int s_hist[2 * kHistBins];
   const int qi = blockIdx.x / n_chunks;
   const int c = blockIdx.x - qi * n_chunks;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
@@ -212,14 +263,8 @@ __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks
   uint32_t kv[PER];
   load_keys<PER>(row, n, kv);
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
-  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, s_sel);   // chunk positions
-  __syncthreads();
-  for (int i = threadIdx.x; i < a.k; i += NT) {
-    const int j = s_sel[i];
-    ok[i] = score_key(row[j]);
-    oi[i] = (int32_t)(base + j);
-  }
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
+  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Offset{(int32_t)base}, oi, ok);
   if (threadIdx.x == 0) cand_cnt[slot] = a.k;
 }
 
@@ -249,6 +294,7 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   constexpr int PER = 32;
   extern __shared__ __attribute__((aligned(16))) uint32_t s_cand[];   // up to kCandMax keys
   __shared__ int s_tmp[NT / kWave + 2];
+  __shared__ int s_hist[2 * kHistBins];
   __shared__ int s_off[64 + 1];
   const int qi = blockIdx.x;
   int32_t* out = a.idx + (int64_t)qi * a.k;
@@ -271,18 +317,49 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
     for (int i = n + threadIdx.x; i < a.k; i += NT) out[i] = -1;
     return;
   }
-  // Candidates -> LDS (coalesced), then each thread takes its segment into registers.
-  for (int c = 0; c < n_chunks; ++c) {
-    const int cnt = s_off[c + 1] - s_off[c];
-    const uint32_t* src = cand_key + ((int64_t)qi * n_chunks + c) * a.k;
-    for (int i = threadIdx.x; i < cnt; i += NT) s_cand[s_off[c] + i] = src[i];
+  // Candidates -> LDS (coalesced; eight loads in flight per thread), then each thread takes its
+  // segment into registers.
+  const uint32_t* ckeys = cand_key + (int64_t)qi * n_chunks * a.k;
+  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+    for (int i = threadIdx.x; i < a.k; i += NT) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u;
+        v[u] = (c < n_chunks && i < s_off[c + 1] - s_off[c]) ? ckeys[(int64_t)c * a.k + i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u;
+        if (c < n_chunks && i < s_off[c + 1] - s_off[c]) s_cand[s_off[c] + i] = v[u];
+      }
+    }
   }
   __syncthreads();
   uint32_t kv[PER];
   load_keys_lds<PER>(s_cand, n, kv);
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_tmp, &need_eq);
-  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, CandIndex{s_off, n_chunks, a.k, cidx}, out);
+  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
+  // Selected positions -> LDS (the keys are in registers now; the scans inside compact_regs
+  // order these writes after every thread's reads of s_cand), then their entry indices are
+  // gathered eight at a time.
+  int32_t* s_pos = reinterpret_cast<int32_t*>(s_cand);
+  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, s_pos);
+  __syncthreads();
+  const CandIndex ci{s_off, n_chunks, a.k, cidx};
+  for (int i0 = 0; i0 < a.k; i0 += 8 * NT) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT + (int)threadIdx.x;
+      v[u] = i < a.k ? ci(s_pos[i]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * NT + (int)threadIdx.x;
+      if (i < a.k) out[i] = v[u];
+    }
+  }
 }
 
 int n_chunks_for(int64_t N) { return (int)((N + kChunk - 1) / kChunk); }

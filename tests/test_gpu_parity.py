@@ -132,6 +132,16 @@ def test_deterministic(cfg):
                            y.view(torch.uint8) if y.dtype != torch.uint8 else y)
 
 
+@pytest.mark.parametrize("sharp", [False, True])
+def test_csa_prefill_128_heads(sharp):
+    # 128 heads per query: the bf16 kernel's four-row-group form (three tile buffers, selection
+    # indices copied three tiles ahead).
+    wl = SMALL["C2"].replace(H=128, T=901, nq=901, k=160)
+    print(f"[parity] csa prefill 128 heads sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, 20)
+    parity.check_csa(wl, host, step)
+
+
 def test_hca_prefill_128_heads_many_queries():
     # >= 512 queries of 128 heads: four 32-head groups share every staged key tile.
     wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=640, H=128)
