@@ -6,16 +6,21 @@
 //
 // Algorithm (integer work only, deterministic). Scores map to order-preserving 32-bit keys. Each
 // thread holds a contiguous segment of PER keys in registers. The k-th largest key K is found by a
-// three-level radix select over 11-, 11- and 10-bit digits: each level counts, in an LDS histogram,
-// the next digit of the keys that share the digits found so far, and a block scan over the
-// histogram locates the digit of the k-th key and its rank within that digit.
-// Compaction keeps every key > K and the lowest-index keys == K: two block scans give every
-// segment its output offset, and indices are written in ascending order.
+// radix select: the block's largest and smallest keys fix the bits every key shares; then, from
+// the highest differing bit down, each level counts in an LDS histogram the next digit (at most 11
+// bits) of the keys that match the digits found so far, and a block scan over the histogram
+// locates the digit of the k-th key and its rank among the keys of that digit. Starting at the
+// highest differing bit spreads clustered keys over the histogram, which keeps LDS atomic
+// conflicts low. Compaction keeps every key > K and the lowest-position keys == K: two block scans
+// give every segment its output offset; selected positions are staged in LDS and written out with
+// coalesced stores.
 //
 // Rows of up to kChunk visible entries: one workgroup per row. Longer rows: stage 1 runs the same
 // selection on chunks of kChunk entries (many workgroups per row) and writes each chunk's local
 // top-k (ascending); stage 2 selects the row's top-k among the concatenated candidates. The union
 // of the chunks' top-k contains the row's top-k under the same tie rule, so the result is exact.
+// Every chunk before a row's last visible one holds kChunk >= k entries and so yields exactly k
+// candidates: a row's candidates are the first n slots of its [chunks][k] block, in entry order.
 #include "common.h"
 
 namespace csa {
@@ -23,58 +28,134 @@ namespace {
 
 constexpr int kChunk = 8192;      // entries per stage-1 chunk (and single-stage limit)
 constexpr int kCandMax = 32768;   // candidates per row in stage 2
+constexpr int kPer = 32;          // keys per thread
+constexpr int kBins = 2048;       // LDS ints per histogram (11-bit digits); two per workgroup
+constexpr int kMaxK = 2048;       // largest k staged in LDS (and largest k of rows > kChunk)
 
 // Order-preserving map float -> uint32 (larger float -> larger key); -0.0 and +0.0 map alike.
+// Finite scores give keys >= 1; padding keys are 0.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Barrier for LDS hand-offs: waits for this wave's LDS operations only, so global loads and
+// stores stay in flight across it.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// DPP controls (GFX9 encoding): shift right within a row of 16 lanes, and broadcasts of lane 15
+// of each row to the next row / of lane 31 to rows 2 and 3.
+constexpr int kRowShr = 0x110;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp(int fill, int x) {
+  return __builtin_amdgcn_update_dpp(fill, x, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp<kRowShr + 1, 0xf>(0, x);
+  x += dpp<kRowShr + 2, 0xf>(0, x);
+  x += dpp<kRowShr + 4, 0xf>(0, x);
+  x += dpp<kRowShr + 8, 0xf>(0, x);
+  x += dpp<kRowBcast15, 0xa>(0, x);
+  x += dpp<kRowBcast31, 0xc>(0, x);
+  return x;
+}
+
+// Running max / min in lane order (lane 63 holds the wave's result).
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)dpp<kRowShr + 1, 0xf>(0, (int)x));
+  x = max(x, (uint32_t)dpp<kRowShr + 2, 0xf>(0, (int)x));
+  x = max(x, (uint32_t)dpp<kRowShr + 4, 0xf>(0, (int)x));
+  x = max(x, (uint32_t)dpp<kRowShr + 8, 0xf>(0, (int)x));
+  x = max(x, (uint32_t)dpp<kRowBcast15, 0xa>(0, (int)x));
+  x = max(x, (uint32_t)dpp<kRowBcast31, 0xc>(0, (int)x));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
+  x = min(x, (uint32_t)dpp<kRowShr + 1, 0xf>(-1, (int)x));
+  x = min(x, (uint32_t)dpp<kRowShr + 2, 0xf>(-1, (int)x));
+  x = min(x, (uint32_t)dpp<kRowShr + 4, 0xf>(-1, (int)x));
+  x = min(x, (uint32_t)dpp<kRowShr + 8, 0xf>(-1, (int)x));
+  x = min(x, (uint32_t)dpp<kRowBcast15, 0xa>(-1, (int)x));
+  x = min(x, (uint32_t)dpp<kRowBcast31, 0xc>(-1, (int)x));
+  return x;
+}
+
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+
 // Exclusive prefix sum (in thread order) of a per-thread count over the block, and the total.
+// s_tmp: NT / 64 ints.
 template <int NT>
 __device__ __forceinline__ int block_scan(int a, int* s_tmp, int& total) {
   constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
-  int ia = a;   // inclusive wave scan
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int x = __shfl_up(ia, o);
-    if (lane >= o) ia += x;
-  }
-  if (lane == kWave - 1) s_tmp[wv] = ia;
-  __syncthreads();
+  const int ia = wave_incl_sum(a);
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) s_tmp[wv] = ia;
+  lds_sync();
   int before = 0;
   total = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const int c = s_tmp[w];
-    if (w < wv) before += c;
+    before += w < wv ? c : 0;
     total += c;
   }
-  __syncthreads();
+  lds_sync();   // s_tmp is free again
   return before + ia - a;
 }
 
-// Radix digits of the k-th key search: bits [31:21], [20:10] and [9:0] of a key.
-constexpr int kHistBins = 2048;   // LDS ints per histogram; two histograms per workgroup
+// Largest key and smallest nonzero key of the block. s_tmp: 2 NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ void block_range(const uint32_t (&kv)[kPer], int* s_tmp,
+                                            uint32_t& mx, uint32_t& mn) {
+  constexpr int NW = NT / kWave;
+  uint32_t a = 0, b = ~0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    a = max(a, kv[i]);
+    b = min(b, kv[i] == 0u ? ~0u : kv[i]);
+  }
+  a = lane63((int)wave_incl_max(a));
+  b = lane63((int)wave_incl_min(b));
+  const int wv = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    s_tmp[wv] = (int)a;
+    s_tmp[NW + wv] = (int)b;
+  }
+  lds_sync();
+  mx = 0;
+  mn = ~0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mx = max(mx, (uint32_t)s_tmp[w]);
+    mn = min(mn, (uint32_t)s_tmp[NW + w]);
+  }
+  lds_sync();
+}
 
-// Given a histogram of NB digit values, finds the digit d holding the kk-th largest key (digits
+// Given a histogram of kBins digit values, finds the digit d holding the kk-th largest key (digits
 // above d hold fewer than kk keys, digits >= d at least kk) and turns kk into the rank of that key
-// among the keys of digit d. Every thread returns the same d and kk.
-template <int NT, int NB>
+// among the keys of digit d. Every thread returns the same d and kk. s_tmp: NT / 64 + 2 ints.
+template <int NT>
 __device__ __forceinline__ uint32_t find_digit(const int* hist, int& kk, int* s_tmp) {
-  static_assert(NB % NT == 0, "bins per thread");
-  constexpr int B = NB / NT;
+  constexpr int B = kBins / NT;
+  static_assert(B >= 2 && B % 2 == 0, "bins per thread");
   int* s_res = s_tmp + NT / kWave;
   const int t = threadIdx.x;
   int h[B];
   int local = 0;
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    h[b] = hist[t * B + b];
-    local += h[b];
+  for (int b = 0; b < B; b += 2) {
+    const int2 v = reinterpret_cast<const int2*>(hist + t * B)[b / 2];
+    h[b] = v.x;
+    h[b + 1] = v.y;
+    local += v.x + v.y;
   }
   int total;
   const int before = block_scan<NT>(local, s_tmp, total);
@@ -89,56 +170,69 @@ __device__ __forceinline__ uint32_t find_digit(const int* hist, int& kk, int* s_
       acc += h[b];
     }
   }
-  __syncthreads();
+  lds_sync();
   kk = s_res[1];
-  return (uint32_t)s_res[0];
+  const uint32_t d = (uint32_t)s_res[0];
+  lds_sync();   // s_res is free again
+  return d;
+}
+
+__device__ __forceinline__ void clear_hist(int* hist, int nt) {
+  for (int i = threadIdx.x; i < 2 * kBins / 4; i += nt) reinterpret_cast<int4*>(hist)[i] = int4{0, 0, 0, 0};
 }
 
 // The k-th largest of the block's keys (1 <= k <= number of real keys; padding keys are 0, below
-// every real key), and in *need_eq how many keys equal to it belong to the top k. Radix select from
-// the top digit down: each level histograms (LDS atomics) the next digit of the keys that share the
-// digits found so far, then locates the k-th key's digit. s_hist holds 2 kHistBins ints; s_tmp
-// holds NT / 64 + 2 ints.
-template <int NT, int PER>
-__device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* s_hist, int* s_tmp,
+// every real key), and in *need_eq how many keys equal to it belong to the top k. hist: 2 kBins
+// ints, zero on entry (clear_hist, then an LDS barrier); s_tmp: 2 NT / 64 + 2 ints.
+template <int NT>
+__device__ uint32_t kth_key(const uint32_t (&kv)[kPer], int k, int* hist, int* s_tmp,
                             int* need_eq) {
-  int* hA = s_hist;
-  int* hB = s_hist + kHistBins;
-  for (int i = threadIdx.x; i < 2 * kHistBins; i += NT) s_hist[i] = 0;
-  __syncthreads();
+  uint32_t mx, mn;
+  block_range<NT>(kv, s_tmp, mx, mn);
+  if (mx == mn) {   // one distinct real key
+    *need_eq = k;
+    return mx;
+  }
+  const int p = 31 - __builtin_clz(mx ^ mn);   // highest bit in which real keys differ
+  // Keys matching the digits found so far: (key & pmask) == prefix. The bits above p are shared
+  // by every real key; a padding key matches only if they are all zero, and then it sits below
+  // every real key in the lowest digit, which leaves the k-th largest unchanged.
+  uint32_t pmask = p == 31 ? 0u : ~0u << (p + 1);
+  uint32_t prefix = mx & pmask;
   int kk = k;
+  int lo = p + 1;
+  int level = 0;
+  while (lo > 0) {
+    const int hi = lo - 1;
+    lo = hi >= 10 ? hi - 10 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    int* h = hist + (level & 1) * kBins;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) atomicAdd(&hA[kv[i] >> 21], 1);
-  __syncthreads();
-  const uint32_t d0 = find_digit<NT, 2048>(hA, kk, s_tmp);
-  for (int i = threadIdx.x; i < 1024; i += NT) hA[i] = 0;   // level 2 reuses hA[0, 1024)
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if ((kv[i] >> 21) == d0) atomicAdd(&hB[(kv[i] >> 10) & 2047u], 1);
+    for (int i = 0; i < kPer; ++i) {
+      if ((kv[i] & pmask) == prefix) atomicAdd(&h[(kv[i] >> lo) & dmask], 1);
+    }
+    lds_sync();
+    const uint32_t d = find_digit<NT>(h, kk, s_tmp);
+    // This histogram serves the level after next: clear it (every thread has read it).
+    for (int i = threadIdx.x; i < kBins / 4; i += NT) reinterpret_cast<int4*>(h)[i] = int4{0, 0, 0, 0};
+    prefix |= d << lo;
+    pmask |= dmask << lo;
+    ++level;
   }
-  __syncthreads();
-  const uint32_t hi = (d0 << 11) | find_digit<NT, 2048>(hB, kk, s_tmp);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if ((kv[i] >> 10) == hi) atomicAdd(&hA[kv[i] & 1023u], 1);
-  }
-  __syncthreads();
-  const uint32_t K = (hi << 10) | find_digit<NT, 1024>(hA, kk, s_tmp);
   *need_eq = kk;
-  return K;
+  return prefix;
 }
 
-// Writes, in ascending position order, index_of(j) for the positions j (j = PER t + i for key
-// kv[i] of thread t) of the top k: keys > K and the first need_eq keys == K; with out_key, also
-// the selected keys.
-template <int NT, int PER, typename F>
-__device__ void compact_regs(const uint32_t (&kv)[PER], uint32_t K, int need_eq,
-                             int* s_tmp, F index_of, int32_t* out, uint32_t* out_key = nullptr) {
+// Calls put(o, j, key) for the top k in ascending position order o = 0 .. k-1 (j = PER t + i for
+// key kv[i] of thread t): keys > K and the first need_eq keys == K. Ends with an LDS barrier.
+template <int NT, typename Put>
+__device__ void compact(const uint32_t (&kv)[kPer], uint32_t K, int need_eq, int k, int* s_tmp,
+                        Put put) {
   // Padding keys (0) are below every real key, and K is a real key (>= 1), so they never count.
-  const int j0 = threadIdx.x * PER;
+  const int j0 = threadIdx.x * kPer;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     gt += kv[i] > K;
     eq += kv[i] == K;
   }
@@ -149,29 +243,26 @@ __device__ void compact_regs(const uint32_t (&kv)[PER], uint32_t K, int need_eq,
   int off = block_scan<NT>(gt + take_eq, s_tmp, total);
   int eq_left = take_eq;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     bool take = kv[i] > K;
     if (kv[i] == K && eq_left > 0) {
       take = true;
       --eq_left;
     }
-    if (take) {
-      out[off] = index_of(j0 + i);
-      if (out_key != nullptr) out_key[off] = kv[i];
-      ++off;
-    }
+    if (take && (unsigned)off < (unsigned)k) put(off, j0 + i, kv[i]);
+    off += take;
   }
+  lds_sync();
 }
 
 // Loads keys [PER t, PER t + PER) of a row of n scores (0 beyond n): 16-byte loads for whole,
 // aligned segments, element by element only for the segment holding the row's end.
-template <int PER>
-__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[PER]) {
-  const int j0 = threadIdx.x * PER;
+__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[kPer]) {
+  const int j0 = threadIdx.x * kPer;
   const float* src = row + j0;
-  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
+    for (int q = 0; q < kPer / 4; ++q) {
       const float4 v = reinterpret_cast<const float4*>(src)[q];
       kv[4 * q] = score_key(v.x);
       kv[4 * q + 1] = score_key(v.y);
@@ -181,18 +272,18 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv
   } else {
     const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
+    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
   }
 }
 
-// The same from keys already in LDS (n of them).
-template <int PER>
-__device__ __forceinline__ void load_keys_lds(const uint32_t* keys, int n, uint32_t (&kv)[PER]) {
-  const int j0 = threadIdx.x * PER;
-  if (j0 + PER <= n) {
+// The same for keys already mapped (stage-2 candidates).
+__device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_t (&kv)[kPer]) {
+  const int j0 = threadIdx.x * kPer;
+  const uint32_t* src = keys + j0;
+  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      const uint4 v = reinterpret_cast<const uint4*>(keys + j0)[q];
+    for (int q = 0; q < kPer / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
       kv[4 * q] = v.x;
       kv[4 * q + 1] = v.y;
       kv[4 * q + 2] = v.z;
@@ -201,25 +292,16 @@ __device__ __forceinline__ void load_keys_lds(const uint32_t* keys, int n, uint3
   } else {
     const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kv[i] = i < m ? keys[j0 + i] : 0u;
+    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? src[i] : 0u;
   }
 }
 
-struct Identity {
-  __device__ int32_t operator()(int j) const { return j; }
-};
-
-struct Offset {
-  int32_t base;
-  __device__ int32_t operator()(int j) const { return base + j; }
-};
-
-// Single stage: one workgroup per query row (n_vis <= kChunk).
+// Single stage: one workgroup per query row (n_vis <= kChunk = NT * kPer).
 template <int NT>
 __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
-  constexpr int PER = kChunk / NT;
-  __shared__ int s_tmp[NT / kWave + 2];
-  __shared__ int s_hist[2 * kHistBins];
+  static_assert(NT * kPer == kChunk, "one key segment per thread");
+  __shared__ int s_tmp[2 * NT / kWave + 2];
+  __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
   const int qi = blockIdx.x;
   const int n = (int)n_visible(a.Q.pos[qi], a.m, a.N);
   int32_t* out = a.idx + (int64_t)qi * a.k;
@@ -227,22 +309,28 @@ __global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
-  uint32_t kv[PER];
-  load_keys<PER>(a.scores + (int64_t)qi * a.ld_scores, n, kv);
+  uint32_t kv[kPer];
+  load_keys(a.scores + (int64_t)qi * a.ld_scores, n, kv);
+  clear_hist(s_hist, NT);
+  lds_sync();
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
-  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, out);
+  const uint32_t K = kth_key<NT>(kv, a.k, s_hist, s_tmp, &need_eq);
+  if (a.k <= kMaxK) {   // staged in LDS, then coalesced stores
+    compact<NT>(kv, K, need_eq, a.k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = j; });
+    for (int i = threadIdx.x; i < a.k; i += NT) out[i] = s_hist[i];
+  } else {
+    compact<NT>(kv, K, need_eq, a.k, s_tmp, [&](int o, int j, uint32_t) { out[o] = j; });
+  }
 }
 
 // Stage 1: chunk c of query row qi; writes the chunk's local top-k (or all of its visible
-// entries) as (key, index) pairs in ascending index order, and their count.
+// entries) as (key, index) pairs in ascending index order.
 template <int NT>
 __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks,
-                                                        uint32_t* cand_key, int32_t* cand_idx,
-                                                        int* cand_cnt) {
-  constexpr int PER = kChunk / NT;
-  __shared__ int s_tmp[NT / kWave + 2];
-  __shared__ int s_hist[2 * kHistBins];
+                                                        uint32_t* cand_key, int32_t* cand_idx) {
+  static_assert(NT * kPer == kChunk, "one key segment per thread");
+  __shared__ int s_tmp[2 * NT / kWave + 2];
+  __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
   const int qi = blockIdx.x / n_chunks;
   const int c = blockIdx.x - qi * n_chunks;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
@@ -257,102 +345,62 @@ __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks
       oi[j] = (int32_t)(base + j);
       ok[j] = score_key(row[j]);
     }
-    if (threadIdx.x == 0) cand_cnt[slot] = n;
     return;
   }
-  uint32_t kv[PER];
-  load_keys<PER>(row, n, kv);
+  uint32_t kv[kPer];
+  load_keys(row, n, kv);
+  clear_hist(s_hist, NT);
+  lds_sync();
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
-  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Offset{(int32_t)base}, oi, ok);
-  if (threadIdx.x == 0) cand_cnt[slot] = a.k;
+  const uint32_t K = kth_key<NT>(kv, a.k, s_hist, s_tmp, &need_eq);
+  int* s_pos = s_hist;
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(s_hist + kMaxK);
+  compact<NT>(kv, K, need_eq, a.k, s_tmp, [&](int o, int j, uint32_t key) {
+    s_pos[o] = j;
+    s_key[o] = key;
+  });
+  for (int i = threadIdx.x; i < a.k; i += NT) {
+    oi[i] = (int32_t)base + s_pos[i];
+    ok[i] = s_key[i];
+  }
 }
 
-// Maps a position of the concatenated candidate list to its entry index.
-struct CandIndex {
-  const int* off;        // LDS: start of each chunk's candidates, n_chunks + 1 values
-  int n_chunks;
-  int k;
-  const int32_t* idx;    // this row's candidate indices, [n_chunks][k]
-  __device__ int32_t operator()(int j) const {
-    int lo = 0, hi = n_chunks - 1;   // last chunk c with off[c] <= j
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= j) lo = mid; else hi = mid - 1;
-    }
-    return idx[(int64_t)lo * k + (j - off[lo])];
-  }
-};
-
-// Stage 2: the row's top-k among its chunks' candidates (concatenated in chunk order, so positions
-// ascend with entry index).
+// Stage 2: the row's top-k among its candidates (n <= NT * kPer).
 template <int NT>
 __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks,
                                                         const uint32_t* cand_key,
-                                                        const int32_t* cand_idx,
-                                                        const int* cand_cnt) {
-  constexpr int PER = 32;
-  extern __shared__ __attribute__((aligned(16))) uint32_t s_cand[];   // up to kCandMax keys
-  __shared__ int s_tmp[NT / kWave + 2];
-  __shared__ int s_hist[2 * kHistBins];
-  __shared__ int s_off[64 + 1];
+                                                        const int32_t* cand_idx) {
+  __shared__ int s_tmp[2 * NT / kWave + 2];
+  __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
   const int qi = blockIdx.x;
   int32_t* out = a.idx + (int64_t)qi * a.k;
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      s_off[c] = o;
-      o += cand_cnt[(int64_t)qi * n_chunks + c];
-    }
-    s_off[n_chunks] = o;
+  const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
+  int n = 0;
+  if (nv > 0) {
+    const int64_t last = (nv - 1) / kChunk;
+    const int64_t in_last = nv - last * kChunk;
+    n = (int)(last * a.k + (in_last < a.k ? in_last : a.k));
   }
-  __syncthreads();
-  const int n = s_off[n_chunks];
   const int32_t* cidx = cand_idx + (int64_t)qi * n_chunks * a.k;
   if (n <= a.k) {   // no more visible entries than k: every candidate, in order
-    for (int c = 0; c < n_chunks; ++c) {
-      const int cnt = s_off[c + 1] - s_off[c];
-      for (int i = threadIdx.x; i < cnt; i += NT) out[s_off[c] + i] = cidx[(int64_t)c * a.k + i];
-    }
-    for (int i = n + threadIdx.x; i < a.k; i += NT) out[i] = -1;
+    for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n ? cidx[i] : -1;
     return;
   }
-  // Candidates -> LDS (coalesced; eight loads in flight per thread), then each thread takes its
-  // segment into registers.
-  const uint32_t* ckeys = cand_key + (int64_t)qi * n_chunks * a.k;
-  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
-    for (int i = threadIdx.x; i < a.k; i += NT) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u;
-        v[u] = (c < n_chunks && i < s_off[c + 1] - s_off[c]) ? ckeys[(int64_t)c * a.k + i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u;
-        if (c < n_chunks && i < s_off[c + 1] - s_off[c]) s_cand[s_off[c] + i] = v[u];
-      }
-    }
-  }
-  __syncthreads();
-  uint32_t kv[PER];
-  load_keys_lds<PER>(s_cand, n, kv);
+  uint32_t kv[kPer];
+  load_mapped(cand_key + (int64_t)qi * n_chunks * a.k, n, kv);
+  clear_hist(s_hist, NT);
+  lds_sync();
   int need_eq;
-  const uint32_t K = kth_key<NT, PER>(kv, a.k, s_hist, s_tmp, &need_eq);
-  // Selected positions -> LDS (the keys are in registers now; the scans inside compact_regs
-  // order these writes after every thread's reads of s_cand), then their entry indices are
-  // gathered eight at a time.
-  int32_t* s_pos = reinterpret_cast<int32_t*>(s_cand);
-  compact_regs<NT, PER>(kv, K, need_eq, s_tmp, Identity{}, s_pos);
-  __syncthreads();
-  const CandIndex ci{s_off, n_chunks, a.k, cidx};
+  const uint32_t K = kth_key<NT>(kv, a.k, s_hist, s_tmp, &need_eq);
+  compact<NT>(kv, K, need_eq, a.k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = j; });
+  // Entry indices of the selected candidates, gathered eight at a time.
   for (int i0 = 0; i0 < a.k; i0 += 8 * NT) {
     int32_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * NT + (int)threadIdx.x;
-      v[u] = i < a.k ? ci(s_pos[i]) : 0;
+      const int j = i < a.k ? s_hist[i] : 0;
+      v[u] = cidx[(unsigned)j < (unsigned)n ? j : 0];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -369,12 +417,11 @@ int n_chunks_for(int64_t N) { return (int)((N + kChunk - 1) / kChunk); }
 size_t topk_workspace(int nq, int64_t N, int k) {
   if (N <= kChunk) return 0;
   const int nc = n_chunks_for(N);
-  return (size_t)nq * nc * ((size_t)k * (sizeof(uint32_t) + sizeof(int32_t)) + sizeof(int));
+  return (size_t)nq * nc * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
 bool topk_supported(int64_t N, int k) {
-  return N <= kChunk ||
-         (k <= 2048 && n_chunks_for(N) <= 64 && (int64_t)n_chunks_for(N) * k <= kCandMax);
+  return N <= kChunk || (k <= kMaxK && (int64_t)n_chunks_for(N) * k <= kCandMax);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -386,27 +433,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int nc = n_chunks_for(a.N);
   uint32_t* cand_key = static_cast<uint32_t*>(a.ws);
   int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_key + (size_t)a.Q.nq * nc * a.k);
-  int* cand_cnt = reinterpret_cast<int*>(cand_idx + (size_t)a.Q.nq * nc * a.k);
   topk_chunk_kernel<256><<<(unsigned)((int64_t)a.Q.nq * nc), 256, 0, s>>>(a, nc, cand_key,
-                                                                         cand_idx, cand_cnt);
+                                                                         cand_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Stage 2 block size: 32 candidate keys per thread.
+  // Stage 2 block size: kPer candidate keys per thread.
   const int64_t cand = (int64_t)nc * a.k;
-  const size_t lds = (size_t)cand * sizeof(uint32_t);
-  auto merge = [&](auto kern, int nt) -> hipError_t {
-    if (lds > 64 * 1024) {
-      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e2 != hipSuccess) return e2;
-    }
-    kern<<<a.Q.nq, nt, lds, s>>>(a, nc, cand_key, cand_idx, cand_cnt);
-    return hipGetLastError();
-  };
-  if (cand <= 128 * 32) return merge(&topk_merge_kernel<128>, 128);
-  if (cand <= 256 * 32) return merge(&topk_merge_kernel<256>, 256);
-  if (cand <= 512 * 32) return merge(&topk_merge_kernel<512>, 512);
-  return merge(&topk_merge_kernel<1024>, 1024);
+  if (cand <= 128 * kPer) {
+    topk_merge_kernel<128><<<a.Q.nq, 128, 0, s>>>(a, nc, cand_key, cand_idx);
+  } else if (cand <= 256 * kPer) {
+    topk_merge_kernel<256><<<a.Q.nq, 256, 0, s>>>(a, nc, cand_key, cand_idx);
+  } else if (cand <= 512 * kPer) {
+    topk_merge_kernel<512><<<a.Q.nq, 512, 0, s>>>(a, nc, cand_key, cand_idx);
+  } else {
+    topk_merge_kernel<1024><<<a.Q.nq, 1024, 0, s>>>(a, nc, cand_key, cand_idx);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace csa

@@ -175,7 +175,7 @@ def test_attend_mfma_matches_generic_kernel(monkeypatch):
 
 
 @pytest.mark.parametrize("N,k", [(40000, 1024), (40000, 2048), (20000, 1), (9000, 700),
-                                 (8192, 1024), (5000, 96)])
+                                 (8192, 1024), (5000, 96), (8000, 2600), (262144, 128)])
 def test_topk_exact_with_ties_and_long_rows(N, k):
     # Top-k on identical fp32 scores is integer work: bit-exact against the oracle, including
     # heavy ties (coarse score values, -0.0 vs +0.0) and rows longer than one chunk.
