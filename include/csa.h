@@ -178,6 +178,20 @@ csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
                       float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N);
 
+/* ---------------------------------------------------------------------------------------------
+ * Instrumentation (not a step of the layer). Times the main attention kernel of csa_attend
+ * (slot 0) and hca_attend (slot 1) alone, without the split-combine and fixup passes that follow
+ * it, with a HIP event pair recorded on the caller's stream around that kernel.
+ *   csa_kernel_timing_enable(cap): record the next cap launches per slot (0 <= cap <= 1024);
+ *     cap = 0 stops recording and releases the events. Creates HIP events: call outside graph
+ *     capture. Not thread-safe: one host thread at a time.
+ *   csa_kernel_timing_read(slot, &ms, &n): waits for the recorded launches of the slot, returns
+ *     their total duration in milliseconds and their count, and clears the slot.
+ *   Errors: CSA_EINVAL for a capacity or slot out of range or NULL outputs; CSA_EHIP otherwise.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_kernel_timing_enable(int32_t cap);
+csa_status csa_kernel_timing_read(int32_t slot, double* ms, int32_t* n);
+
 /* Text of a status code; for CSA_EHIP the text of the last HIP error seen by this thread. */
 const char* csa_status_str(int32_t status);
 const char* csa_last_error(void);

@@ -227,4 +227,17 @@ csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
   return hip_status(csa::launch_attend(a, static_cast<hipStream_t>(stream)));
 }
 
+csa_status csa_kernel_timing_enable(int32_t cap) {
+  if (cap < 0 || cap > csa::kTimingCap) return fail(CSA_EINVAL, "timing capacity out of range");
+  return hip_status(csa::kernel_timing_enable(cap));
+}
+
+csa_status csa_kernel_timing_read(int32_t slot, double* ms, int32_t* n) {
+  if (ms == nullptr || n == nullptr || slot < 0 || slot > 1) return fail(CSA_EINVAL, "bad timing query");
+  int cnt = 0;
+  const csa_status st = hip_status(csa::kernel_timing_read(slot, ms, &cnt));
+  *n = cnt;
+  return st;
+}
+
 }  // extern "C"

@@ -27,7 +27,11 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.Q.nq == 0 || a.H == 0) return hipSuccess;
   const int64_t max_keys = a.dense ? a.ent.rows : (int64_t)a.k + a.window;
   if (!force_generic() && attend_mfma_supported(a)) return launch_attend_mfma(a, max_keys, s);
-  return launch_attend_generic(a, s);
+  const int slot = a.dense ? 1 : 0;
+  const bool timed = timing_start(slot, s);
+  const hipError_t e = launch_attend_generic(a, s);
+  if (timed) timing_stop(slot, s);
+  return e;
 }
 
 }  // namespace csa

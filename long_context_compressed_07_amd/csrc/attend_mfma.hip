@@ -505,6 +505,62 @@ size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
   return part + flags;
 }
 
+// Optional timing of the main attention kernel alone (slot 0: CSA, slot 1: HCA): a HIP event
+// pair recorded on the launch stream around it.
+namespace {
+struct KernelTiming {
+  int cap = 0;
+  int n[2] = {0, 0};
+  hipEvent_t ev[2][2][kTimingCap];   // [slot][start / end][launch]
+};
+KernelTiming g_timing;
+}  // namespace
+
+hipError_t kernel_timing_enable(int cap) {
+  for (int slot = 0; slot < 2; ++slot)
+    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < g_timing.cap; ++i) (void)hipEventDestroy(g_timing.ev[slot][j][i]);
+  g_timing.cap = 0;
+  g_timing.n[0] = g_timing.n[1] = 0;
+  if (cap < 0 || cap > kTimingCap) return hipErrorInvalidValue;
+  for (int i = 0; i < cap; ++i) {
+    for (int slot = 0; slot < 2; ++slot)
+      for (int j = 0; j < 2; ++j) {
+        hipError_t e = hipEventCreate(&g_timing.ev[slot][j][i]);
+        if (e != hipSuccess) return e;
+      }
+    g_timing.cap = i + 1;
+  }
+  return hipSuccess;
+}
+
+hipError_t kernel_timing_read(int slot, double* ms, int* n) {
+  *ms = 0.0;
+  *n = 0;
+  if (slot < 0 || slot > 1) return hipErrorInvalidValue;
+  for (int i = 0; i < g_timing.n[slot]; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.ev[slot][1][i]);
+    if (e != hipSuccess) return e;
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, g_timing.ev[slot][0][i], g_timing.ev[slot][1][i]);
+    if (e != hipSuccess) return e;
+    *ms += t;
+  }
+  *n = g_timing.n[slot];
+  g_timing.n[slot] = 0;
+  return hipSuccess;
+}
+
+bool timing_start(int slot, hipStream_t s) {
+  if (g_timing.n[slot] >= g_timing.cap) return false;
+  (void)hipEventRecord(g_timing.ev[slot][0][g_timing.n[slot]], s);
+  return true;
+}
+
+void timing_stop(int slot, hipStream_t s) {
+  (void)hipEventRecord(g_timing.ev[slot][1][g_timing.n[slot]++], s);
+}
+
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
   MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
   if (p.n_split > 1) {
@@ -514,6 +570,8 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + plan_partial_bytes(p, a.Q.nq, a.H));
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   const bool fp8 = a.ent.dtype == CSA_E4M3;
+  const int tslot = a.dense ? 1 : 0;
+  const bool timed = timing_start(tslot, s);
   if (p.bf16_dma) {
     hipError_t e = launch_attend_bf16(a, p, s);
     if (e != hipSuccess) return e;
@@ -530,6 +588,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (timed) timing_stop(tslot, s);
   if (p.n_split > 1) {
     combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kDC / 4, 0, s>>>(a, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

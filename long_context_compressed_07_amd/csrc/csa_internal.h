@@ -90,6 +90,13 @@ size_t topk_workspace(int nq, int64_t N, int k);
 bool topk_supported(int64_t N, int k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
+// Instrumentation: event timing of the main attention kernel (see csa.h).
+constexpr int kTimingCap = 1024;
+hipError_t kernel_timing_enable(int cap);
+hipError_t kernel_timing_read(int slot, double* ms, int* n);
+bool timing_start(int slot, hipStream_t s);   // true: an event pair is open for this launch
+void timing_stop(int slot, hipStream_t s);
+
 // ---- attention -----------------------------------------------------------------------------
 struct AttendArgs {
   Queries Q;

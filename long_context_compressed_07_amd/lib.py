@@ -24,7 +24,8 @@ _lib = None
 
 EXPORTS = ("csa_compress", "csa_index", "csa_topk", "csa_topk_workspace_bytes", "csa_attend",
            "csa_attend_workspace_bytes", "hca_attend", "hca_attend_workspace_bytes",
-           "csa_status_str", "csa_last_error", "csa_abi_version")
+           "csa_status_str", "csa_last_error", "csa_abi_version", "csa_kernel_timing_enable",
+           "csa_kernel_timing_read")
 
 
 class KV(ctypes.Structure):
@@ -67,8 +68,10 @@ def load(path: str = LIB_PATH):
     lib.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i64]
     lib.hca_attend.argtypes = [P(Queries), vp, i32, i32, P(KV), i32, f32, vp, vp, vp, sz, vp]
     lib.hca_attend_workspace_bytes.argtypes = [i32, i32, i32, i64]
+    lib.csa_kernel_timing_enable.argtypes = [i32]
+    lib.csa_kernel_timing_read.argtypes = [i32, P(ctypes.c_double), P(i32)]
     for fn in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend",
-               "csa_abi_version"):
+               "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read"):
         getattr(lib, fn).restype = ctypes.c_int32
     for fn in ("csa_topk_workspace_bytes", "csa_attend_workspace_bytes",
                "hca_attend_workspace_bytes"):
@@ -215,3 +218,17 @@ def hca_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m_prime: int,
     _check(lib.hca_attend(ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(e), m_prime,
                           sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
                           0 if ws is None else ws.numel(), _stream(stream)), "hca_attend")
+
+
+def kernel_timing_enable(cap: int):
+    """Record HIP events around the next `cap` main attention kernels of csa_attend (slot 0) and
+    hca_attend (slot 1); cap = 0 stops."""
+    _check(load().csa_kernel_timing_enable(cap), "csa_kernel_timing_enable")
+
+
+def kernel_timing_read(slot: int) -> tuple[float, int]:
+    """(total milliseconds, launches) recorded in a slot since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    _check(load().csa_kernel_timing_read(slot, ctypes.byref(ms), ctypes.byref(n)),
+           "csa_kernel_timing_read")
+    return ms.value, n.value
