@@ -196,6 +196,7 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
   }
   __syncthreads();
   const bool sel_dma = kl.sel != nullptr;   // CSA: selection slots come from idx
+  const KeyCodes32 kc = key_codes32(kl, ke);
   if (sel_dma && threadIdx.x < 64) dma_sel<TK>(kl, k0 + (kAhead + 1) * TK, ke, s_sel[(kAhead + 1) & 1]);
   // Every tile issues exactly kDmaOps DMA instructions per wave (tiles past the end copy the zero
   // row), so the count of outstanding loads is the same on every path and the waits below stay
@@ -366,9 +367,9 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
     __builtin_amdgcn_s_waitcnt(kVmcntDma<2 * kDmaOps + 1>);
     if (threadIdx.x < 64) {
       // Codes of tile t + kAhead + 1, from the selection slots copied during the previous tile.
-      const int64_t kk2 = t0 + (kAhead + 1) * TK + threadIdx.x;
+      const int kk2 = (int)t0 + (kAhead + 1) * TK + (int)threadIdx.x;
       const int raw2 = sel_dma ? s_sel[(it + kAhead + 1) & 1][threadIdx.x] : 0;
-      const int c2 = threadIdx.x < TK ? key_code_of(kl, kk2, raw2, ke) : -1;
+      const int c2 = threadIdx.x < TK ? key_code32(kc, kk2, raw2) : -1;
       const int slot2 = (it + kAhead + 1) % kSlots;
       if (threadIdx.x < TK) {
         s_code[slot2][threadIdx.x] = c2;
@@ -408,6 +409,9 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
   __syncthreads();
   if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
 
+  // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
+  // row group at a time, staged in the (now idle) tile buffers.
+  char* stage = &kv[0][0];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int hrow = 32 * r + (lane & 31);
@@ -416,34 +420,27 @@ attend_bf16_kernel(AttendArgs a, AttnPlan plan) {
     for (int j = 1; j < KB; ++j) l += s_l[j][hrow];
     const float m = s_ref[0][hrow];
     const int head = hbase + hrow;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t row0 = plan.n_split == 1 ? (int64_t)qi * a.H + hbase + 32 * r
+                                           : ((int64_t)qi * plan.n_split + split) * a.H + hbase + 32 * r;
     if (plan.n_split == 1) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float* orow = a.out + ((int64_t)qi * a.H + head) * kDC + 128 * w;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-              make_float4(o[mt][r][4 * j] * inv, o[mt][r][4 * j + 1] * inv,
-                          o[mt][r][4 * j + 2] * inv, o[mt][r][4 * j + 3] * inv);
+      stage_rows<float>(o, r, inv, stage);
       if (a.lse != nullptr && w == 0 && hi == 0)
         a.lse[(int64_t)qi * a.H + head] =
             l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
+      __syncthreads();
+      flush_rows<float>(stage, a.out + row0 * kDC);
     } else {
-      const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
-      float* orow = plan.ws_o + pidx * kDC + 128 * w;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-              make_float4(o[mt][r][4 * j], o[mt][r][4 * j + 1], o[mt][r][4 * j + 2],
-                          o[mt][r][4 * j + 3]);
+      stage_rows<_Float16>(o, r, inv, stage);
       if (w == 0 && hi == 0) {
+        const int64_t pidx = row0 + (lane & 31);
         plan.ws_ml[pidx * 2] = m;
         plan.ws_ml[pidx * 2 + 1] = l;
       }
+      __syncthreads();
+      flush_rows<_Float16>(stage, plan.ws_o + row0 * kDC);
     }
+    __syncthreads();
   }
 }
 

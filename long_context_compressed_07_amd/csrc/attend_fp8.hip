@@ -115,21 +115,33 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = 8 * w + (lane >> 3), p = lane & 7;
   const int f = swz(r);
-  const uint32_t sbits = *reinterpret_cast<const uint32_t*>(st + kStLat + kStRope + 4 * r);
+  // All six LDS reads in flight at once (one instruction block, so the waits cannot split them).
+  v4i lv[4], rv;
+  int sb;
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:16\n\t"
+      "ds_read_b128 %2, %6 offset:32\n\t"
+      "ds_read_b128 %3, %6 offset:48\n\t"
+      "ds_read_b128 %4, %7\n\t"
+      "ds_read_b32 %5, %8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lv[0]), "=&v"(lv[1]), "=&v"(lv[2]), "=&v"(lv[3]), "=&v"(rv), "=&v"(sb)
+      : "v"(lds_addr(st + r * 512 + 64 * p)), "v"(lds_addr(st + kStLat + r * 128 + 16 * p)),
+        "v"(lds_addr(st + kStLat + kStRope + 4 * r)));
+  const uint32_t sbits = (uint32_t)sb;
   const float pow2 = __uint_as_float(sbits & 0x7f800000u);                  // 2^e (0 for 0)
   const _Float16 mant = (_Float16)__uint_as_float((sbits & 0x007fffffu) | 0x3f800000u);
   const h2 mm = {mant, mant};
-  const char* src = st + r * 512 + 64 * p;
   char* row = kvb + r * 1024;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * k);
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[j], pow2, false) * mm;
-      const h2 hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[j], pow2, true) * mm;
+      const uint32_t wd = (uint32_t)lv[k][j];
+      const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, pow2, false) * mm;
+      const h2 hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, pow2, true) * mm;
       o[2 * j] = __builtin_bit_cast(uint32_t, lo);
       o[2 * j + 1] = __builtin_bit_cast(uint32_t, hi2);
     }
@@ -137,8 +149,7 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
     *reinterpret_cast<uint4*>(row + 16 * (c ^ f)) = make_uint4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<uint4*>(row + 16 * ((c + 1) ^ f)) = make_uint4(o[4], o[5], o[6], o[7]);
   }
-  const uint4 rv = *reinterpret_cast<const uint4*>(st + kStLat + r * 128 + 16 * p);
-  const f16x8 rh = bf16x8_to_f16(rv.x, rv.y, rv.z, rv.w);
+  const f16x8 rh = bf16x8_to_f16((uint32_t)rv[0], (uint32_t)rv[1], (uint32_t)rv[2], (uint32_t)rv[3]);
   *reinterpret_cast<f16x8*>(kvb + kTK * 1024 + r * 128 + 16 * (p ^ f)) = rh;
 }
 
@@ -200,6 +211,7 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   bool overflow = false;
   const float cscale = a.sm_scale * kLog2e;
   const bool sel_dma = kl.sel != nullptr;
+  const KeyCodes32 kc = key_codes32(kl, ke);
 
   // Prologue: codes of tiles 0 .. kAheadF8 (wave 0), selection slots of tile kAheadF8 + 1 and
   // kAheadF8 + 2, tiles 0 .. kAheadF8 - 1 staged, tile 0 converted.
@@ -341,9 +353,9 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
     // issued since (two tiles' worth) may still be outstanding.
     __builtin_amdgcn_s_waitcnt(kVmcntDma<2 * (kDmaOpsF8 + 1)>);
     if (threadIdx.x < 64) {
-      const int64_t kk2 = t0 + (kAheadF8 + 1) * kTK + threadIdx.x;
+      const int kk2 = (int)t0 + (kAheadF8 + 1) * kTK + (int)threadIdx.x;
       const int raw2 = sel_dma ? s_sel[(it + kAheadF8 + 1) % 3][threadIdx.x] : 0;
-      const int c2 = threadIdx.x < kTK ? key_code_of(kl, kk2, raw2, ke) : -1;
+      const int c2 = threadIdx.x < kTK ? key_code32(kc, kk2, raw2) : -1;
       const int slot2 = (it + kAheadF8 + 1) % kSlotsF8;
       if (threadIdx.x < kTK) {
         s_code[slot2][threadIdx.x] = c2;
@@ -382,40 +394,36 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   __syncthreads();
   if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
 
+  // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
+  // row group at a time, staged in the (now idle) tile buffers.
+  char* stage = &kv[0][0];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int hrow = 32 * r + (lane & 31);
     const float l = s_l[hrow];
     const float m = s_ref[hrow];
     const int head = hbase + hrow;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t row0 = plan.n_split == 1 ? (int64_t)qi * a.H + hbase + 32 * r
+                                           : ((int64_t)qi * plan.n_split + split) * a.H + hbase + 32 * r;
     if (plan.n_split == 1) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      float* orow = a.out + ((int64_t)qi * a.H + head) * kDC + 128 * w;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-              make_float4(o[mt][r][4 * j] * inv, o[mt][r][4 * j + 1] * inv,
-                          o[mt][r][4 * j + 2] * inv, o[mt][r][4 * j + 3] * inv);
+      stage_rows<float>(o, r, inv, stage);
       if (a.lse != nullptr && w == 0 && hi == 0)
         a.lse[(int64_t)qi * a.H + head] =
             l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
+      __syncthreads();
+      flush_rows<float>(stage, a.out + row0 * kDC);
     } else {
-      const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
-      float* orow = plan.ws_o + pidx * kDC + 128 * w;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-              make_float4(o[mt][r][4 * j], o[mt][r][4 * j + 1], o[mt][r][4 * j + 2],
-                          o[mt][r][4 * j + 3]);
+      stage_rows<_Float16>(o, r, inv, stage);
       if (w == 0 && hi == 0) {
+        const int64_t pidx = row0 + (lane & 31);
         plan.ws_ml[pidx * 2] = m;
         plan.ws_ml[pidx * 2 + 1] = l;
       }
+      __syncthreads();
+      flush_rows<_Float16>(stage, plan.ws_o + row0 * kDC);
     }
+    __syncthreads();
   }
 }
 

@@ -27,8 +27,8 @@
 //                                                 the same LDS rows (ds_read_tr16_b64), P^T is
 //                                                 the softmax output already in registers
 // The KSW key splits of a head group are merged through LDS at the end (log-sum-exp merge); with
-// n_split > 1 workgroups per query, partial (O, m, l) go to the workspace and combine_kernel
-// merges them.
+// n_split > 1 workgroups per query, partial outputs (normalised, fp16) and (m, l) go to the
+// workspace and combine_kernel merges them.
 //
 // Precision: products in fp16 are exact for these inputs (bf16 and scaled fp8 values lie inside
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
@@ -356,13 +356,14 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
           l_run > 0.f ? (m_run + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   } else {
     const int64_t pidx = ((int64_t)qi * plan.n_split + split) * a.H + head;
-    float* orow = plan.ws_o + pidx * kDC;
+    _Float16* orow = plan.ws_o + pidx * kDC;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(orow + 32 * mt + 8 * j + 4 * hi) =
-            make_float4(o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]);
+        store_partial4(orow + 32 * mt + 8 * j + 4 * hi, o[mt][4 * j], o[mt][4 * j + 1],
+                       o[mt][4 * j + 2], o[mt][4 * j + 3], inv);
     if (hi == 0) {
       plan.ws_ml[pidx * 2] = m_run;
       plan.ws_ml[pidx * 2 + 1] = l_run;
@@ -377,17 +378,20 @@ __global__ void __launch_bounds__(128) combine_kernel(AttendArgs a, MfmaPlan pla
   float mx = -INFINITY;
   for (int s = 0; s < plan.n_split; ++s)
     mx = fmaxf(mx, plan.ws_ml[(((int64_t)qi * plan.n_split + s) * a.H + head) * 2]);
+  // Partial s holds o_s / l_s: out = sum_s (l_s 2^(m_s - mx)) (o_s / l_s) / sum_s l_s 2^(m_s - mx).
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   float lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int d0 = threadIdx.x * 4;
   for (int s = 0; s < plan.n_split; ++s) {
     const int64_t pidx = ((int64_t)qi * plan.n_split + s) * a.H + head;
     const float m = plan.ws_ml[pidx * 2];
-    if (m == -INFINITY) continue;
-    const float wgt = exp2f(m - mx);
-    lsum += wgt * plan.ws_ml[pidx * 2 + 1];
-    const float4 v = *reinterpret_cast<const float4*>(plan.ws_o + pidx * kDC + d0);
-    acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+    const float l = plan.ws_ml[pidx * 2 + 1];
+    const h4 v = *reinterpret_cast<const h4*>(plan.ws_o + pidx * kDC + d0);
+    const float wgt = m == -INFINITY ? 0.f : exp2f(m - mx) * l;
+    lsum += wgt;
+    acc.x += wgt * (float)v[0]; acc.y += wgt * (float)v[1];
+    acc.z += wgt * (float)v[2]; acc.w += wgt * (float)v[3];
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   *reinterpret_cast<float4*>(a.out + ((int64_t)qi * a.H + head) * kDC + d0) =
@@ -489,7 +493,8 @@ bool attend_mfma_supported(const AttendArgs& a) {
 // Workspace: partial outputs when a query spans several workgroups, then one flag per workgroup.
 // The dtype is not part of the workspace query, so this covers both plans.
 static size_t plan_partial_bytes(const MfmaPlan& p, int nq, int H) {
-  return p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC + 2) * sizeof(float) : 0;
+  return p.n_split > 1 ? (size_t)nq * p.n_split * H * (kDC * sizeof(_Float16) + 2 * sizeof(float))
+                       : 0;
 }
 static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
   return (size_t)nq * p.head_groups * p.n_split * sizeof(int);
@@ -564,8 +569,8 @@ void timing_stop(int slot, hipStream_t s) {
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
   MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
   if (p.n_split > 1) {
-    p.ws_o = static_cast<float*>(a.ws);
-    p.ws_ml = p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC;
+    p.ws_o = static_cast<_Float16*>(a.ws);
+    p.ws_ml = reinterpret_cast<float*>(p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC);
   }
   p.flags = reinterpret_cast<int*>(static_cast<char*>(a.ws) + plan_partial_bytes(p, a.Q.nq, a.H));
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);

@@ -13,10 +13,18 @@ struct AttnPlan {
   int n_split;        // workgroups per query along keys
   int bf16_dma;       // 1: bf16 rows staged by DMA (attend_bf16.hip); 0: fp16 staging
   int f8_dma;         // 1: fp8 rows staged by DMA and converted in LDS (attend_fp8.hip)
-  float* ws_o;        // [nq][n_split][H][512] partial outputs (unnormalised), n_split > 1
+  _Float16* ws_o;     // [nq][n_split][H][512] partial outputs normalised by their l, n_split > 1
   float* ws_ml;       // [nq][n_split][H][2] partial (max in log2 units, sum)
   int* flags;         // [nq][head_groups][n_split] 1 = some head left the range of P
 };
+
+// Four values of a normalised partial output row (o / l in fp16; zeros when l == 0).
+__device__ __forceinline__ void store_partial4(_Float16* dst, float a, float b, float c, float d,
+                                               float inv) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<h4*>(dst) = h4{(_Float16)(a * inv), (_Float16)(b * inv), (_Float16)(c * inv),
+                                   (_Float16)(d * inv)};
+}
 
 hipError_t launch_attend_bf16(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_fp8(const AttendArgs& a, const AttnPlan& p, hipStream_t s);

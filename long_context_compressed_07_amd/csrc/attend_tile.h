@@ -94,6 +94,59 @@ __device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int ra
   return (int)(kl.wlo + (kk - kl.n_sel) - kl.raw_base) | (1 << 30);   // raw-window row
 }
 
+// Output rows through LDS. The accumulators hold O^T in the MFMA layout (lane: one head, 4-dim
+// pieces of 32 rows at once), so stores straight from registers would write 32 rows x 16 bytes per
+// instruction. Instead each wave stages its 128 dims of 32 heads (row group r of o[mt][r], scaled
+// by the lane's inv) as rows of 512 values of T, and the workgroup then writes whole rows, 16
+// bytes per lane. kStageLd: LDS row stride (16 bytes of padding spread the staging writes over the banks).
+template <typename T>
+constexpr int kStageLd = 512 * (int)sizeof(T) + 16;
+
+template <typename T, int RG>
+__device__ __forceinline__ void stage_rows(const floatx16 (&o)[4][RG], int r, float inv, char* buf) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5;
+  char* row = buf + (lane & 31) * kStageLd<T> + (128 * w + 4 * hi) * (int)sizeof(T);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      const t4 v = {(T)(o[mt][r][4 * j] * inv), (T)(o[mt][r][4 * j + 1] * inv),
+                    (T)(o[mt][r][4 * j + 2] * inv), (T)(o[mt][r][4 * j + 3] * inv)};
+      *reinterpret_cast<t4*>(row + (32 * mt + 8 * j) * (int)sizeof(T)) = v;
+    }
+}
+
+// Writes the 32 staged rows: row h to dst + h * 512 (consecutive heads are consecutive rows).
+template <typename T>
+__device__ __forceinline__ void flush_rows(const char* buf, T* dst) {
+  constexpr int kChunksRow = 512 * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int c = threadIdx.x; c < 32 * kChunksRow; c += 256) {
+    const int h = c / kChunksRow, k = c - h * kChunksRow;
+    const uint4 v = *reinterpret_cast<const uint4*>(buf + h * kStageLd<T> + 16 * k);
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + (int64_t)h * 512) + 16 * k) = v;
+  }
+}
+
+// key_code_of in 32-bit arithmetic, for the tile loops (key indices and rows fit in 31 bits).
+struct KeyCodes32 {
+  int ke;        // end of this workgroup's key range
+  int n_sel;     // entry slots before the window rows
+  int woff;      // raw row of window key kk: kk + woff
+  int has_sel;   // 1: entry slots map through the selection
+};
+
+__device__ __forceinline__ KeyCodes32 key_codes32(const KeyList& kl, int64_t ke) {
+  return {(int)ke, (int)kl.n_sel, (int)(kl.wlo - kl.n_sel - kl.raw_base), kl.sel != nullptr};
+}
+
+__device__ __forceinline__ int key_code32(const KeyCodes32& c, int kk, int raw) {
+  if (kk >= c.ke || raw < 0) return -1;
+  if (kk < c.n_sel) return c.has_sel ? raw : kk;
+  return (kk + c.woff) | (1 << 30);
+}
+
 // S^T[32 keys x 32 heads] = K . Q^T over the 36 k-steps of a 576-dim row, as one instruction
 // block: 4 K-fragment reads stay in flight ahead of the MFMA chain (5 rotating register quads, so a
 // quad is rewritten only after the MFMA that read it and one more have issued). lb[t]: LDS address
