@@ -31,7 +31,11 @@ namespace csa {
 namespace {
 
 constexpr int kTK = 32;                      // keys per tile
-constexpr int kStLat = kTK * 512;            // staging: fp8 latent rows
+// Staging: fp8 latent rows in 16 pairs (rows j and j + 16, 512 B apart, one DMA instruction
+// each); pair j starts at kStPair j, 16 bytes past a multiple of 1 KB per pair, so that the
+// conversion's reads of one part of 8 consecutive rows fall in 8 different LDS bank groups.
+constexpr int kStPair = 1024 + 16;
+constexpr int kStLat = 16 * kStPair;         // staging: fp8 latent rows
 constexpr int kStRope = kTK * 128;           // staging: bf16 RoPE rows
 constexpr int kStB = kStLat + kStRope + 1024;   // + row scales (64 x 4 B written), rounded to 1 KB
 constexpr int kNst = 3;                      // staging slots (tiles t + 1 .. t + 3)
@@ -87,15 +91,15 @@ __device__ __forceinline__ KeyAddr8 key_addr8(const RowBases8& rb, int code) {
 }
 
 // This wave's share of the DMA of one tile into staging slot `st` (the prologue's form of what the
-// QK block issues): latent row pairs w + 4 i (lanes 0-31 the even row, 32-63 the odd one), RoPE
-// rows 8 w .. 8 w + 7, and the 32 row scales (every wave copies the same values).
+// QK block issues): latent row pairs j = w + 4 i (lanes 0-31 row j, 32-63 row j + 16), RoPE rows
+// 8 w .. 8 w + 7, and the 32 row scales (every wave copies the same values).
 __device__ __forceinline__ void dma_stage(const KeyAddr8* ad, char* st) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int p = w + 4 * i;
-    const char* src = ad[2 * p + (lane >> 5)].lat + 16 * (lane & 31);
-    __builtin_amdgcn_global_load_lds(src, (lds_char*)(st + 1024 * p), 16, 0, 0);
+    const int j = w + 4 * i;
+    const char* src = ad[j + 16 * (lane >> 5)].lat + 16 * (lane & 31);
+    __builtin_amdgcn_global_load_lds(src, (lds_char*)(st + kStPair * j), 16, 0, 0);
   }
   {
     const char* src = ad[8 * w + (lane >> 3)].rope + 16 * (lane & 7);
@@ -107,14 +111,16 @@ __device__ __forceinline__ void dma_stage(const KeyAddr8* ad, char* st) {
   }
 }
 
-// Converts staging slot `st` into the fp16 tile `kvb` (layout of attend_tile.h). Wave w converts
-// rows 8 w .. 8 w + 7; lane l takes row 8 w + l / 8 and its 64-dim part p = l & 7 (latent dims
-// 64 p .. 64 p + 63, RoPE dims 8 p .. 8 p + 7).
+// Converts staging slot `st` into the fp16 tile `kvb` (layout of attend_tile.h). Latent: wave w
+// converts rows 8 w .. 8 w + 7, lane l row 8 w + (l & 7) and its 64-dim part p = l >> 3 (so the
+// 8 lanes of one part write 8 different 16-byte bank groups). RoPE: lane l row 8 w + (l >> 3),
+// dims 8 (l & 7) .. + 7.
 __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = 8 * w + (lane >> 3), p = lane & 7;
+  const int r = 8 * w + (lane & 7), p = lane >> 3;
   const int f = swz(r);
+  const int rr = 8 * w + (lane >> 3), pr = lane & 7;
   // All six LDS reads in flight at once (one instruction block, so the waits cannot split them).
   v4i lv[4], rv;
   int sb;
@@ -127,7 +133,8 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
       "ds_read_b32 %5, %8\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(lv[0]), "=&v"(lv[1]), "=&v"(lv[2]), "=&v"(lv[3]), "=&v"(rv), "=&v"(sb)
-      : "v"(lds_addr(st + r * 512 + 64 * p)), "v"(lds_addr(st + kStLat + r * 128 + 16 * p)),
+      : "v"(lds_addr(st + kStPair * (r & 15) + 512 * (r >> 4) + 64 * p)),
+        "v"(lds_addr(st + kStLat + rr * 128 + 16 * pr)),
         "v"(lds_addr(st + kStLat + kStRope + 4 * r)));
   const uint32_t sbits = (uint32_t)sb;
   const float pow2 = __uint_as_float(sbits & 0x7f800000u);                  // 2^e (0 for 0)
@@ -150,7 +157,7 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
     *reinterpret_cast<uint4*>(row + 16 * ((c + 1) ^ f)) = make_uint4(o[4], o[5], o[6], o[7]);
   }
   const f16x8 rh = bf16x8_to_f16((uint32_t)rv[0], (uint32_t)rv[1], (uint32_t)rv[2], (uint32_t)rv[3]);
-  *reinterpret_cast<f16x8*>(kvb + kTK * 1024 + r * 128 + 16 * (p ^ f)) = rh;
+  *reinterpret_cast<f16x8*>(kvb + kTK * 1024 + rr * 128 + 16 * (pr ^ swz(rr))) = rh;
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -269,12 +276,12 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
                     : reinterpret_cast<const char*>(kZeroRow);
       const KeyAddr8* ad = s_addr[(it + kAheadF8) % kSlotsF8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma.lat[i] = ad[2 * (w + 4 * i) + (lane >> 5)].lat + 16 * (lane & 31);
+      for (int i = 0; i < 4; ++i) dma.lat[i] = ad[(w + 4 * i) + 16 * (lane >> 5)].lat + 16 * (lane & 31);
       dma.rope = ad[8 * w + (lane >> 3)].rope + 16 * (lane & 7);
       dma.scl = lane < kTK ? ad[lane].scl : reinterpret_cast<const char*>(kZeroRow);
       dma.m0_sel = __builtin_amdgcn_readfirstlane(
           lds_addr(reinterpret_cast<const char*>(s_sel[(it + kAheadF8 + 3) % 3])));
-      dma.m0_lat = __builtin_amdgcn_readfirstlane(lds_addr(sdst) + 1024 * w);
+      dma.m0_lat = __builtin_amdgcn_readfirstlane(lds_addr(sdst) + kStPair * w);
       dma.m0_rope = __builtin_amdgcn_readfirstlane(lds_addr(sdst) + kStLat + 1024 * w);
       dma.m0_scl = __builtin_amdgcn_readfirstlane(lds_addr(sdst) + kStLat + kStRope);
     }

@@ -371,31 +371,36 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   }
 }
 
-// Log-sum-exp merge of n_split partials: one block per (query, head), one thread per 4 dims.
-__global__ void __launch_bounds__(128) combine_kernel(AttendArgs a, MfmaPlan plan) {
+// Log-sum-exp merge of n_split partials: one block per (query, head), one thread per 8 dims.
+// Partial s holds o_s / l_s: out = sum_s (l_s 2^(m_s - mx)) (o_s / l_s) / sum_s l_s 2^(m_s - mx).
+constexpr int kCombineThreads = kDC / 8;
+
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttendArgs a, MfmaPlan plan) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   const int qi = blockIdx.x / a.H;
   const int head = blockIdx.x - qi * a.H;
+  const int64_t p0 = (int64_t)qi * plan.n_split * a.H + head;   // partial index of split 0
+  const int64_t ps = a.H;                                        // stride between splits
   float mx = -INFINITY;
-  for (int s = 0; s < plan.n_split; ++s)
-    mx = fmaxf(mx, plan.ws_ml[(((int64_t)qi * plan.n_split + s) * a.H + head) * 2]);
-  // Partial s holds o_s / l_s: out = sum_s (l_s 2^(m_s - mx)) (o_s / l_s) / sum_s l_s 2^(m_s - mx).
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+#pragma unroll 8
+  for (int s = 0; s < plan.n_split; ++s) mx = fmaxf(mx, plan.ws_ml[(p0 + s * ps) * 2]);
+  const int d0 = threadIdx.x * 8;
   float lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int d0 = threadIdx.x * 4;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int s = 0; s < plan.n_split; ++s) {
-    const int64_t pidx = ((int64_t)qi * plan.n_split + s) * a.H + head;
-    const float m = plan.ws_ml[pidx * 2];
-    const float l = plan.ws_ml[pidx * 2 + 1];
-    const h4 v = *reinterpret_cast<const h4*>(plan.ws_o + pidx * kDC + d0);
-    const float wgt = m == -INFINITY ? 0.f : exp2f(m - mx) * l;
+    const int64_t pidx = p0 + s * ps;
+    const float2 ml = *reinterpret_cast<const float2*>(plan.ws_ml + pidx * 2);
+    const h8 v = *reinterpret_cast<const h8*>(plan.ws_o + pidx * kDC + d0);
+    const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
     lsum += wgt;
-    acc.x += wgt * (float)v[0]; acc.y += wgt * (float)v[1];
-    acc.z += wgt * (float)v[2]; acc.w += wgt * (float)v[3];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[j];
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  *reinterpret_cast<float4*>(a.out + ((int64_t)qi * a.H + head) * kDC + d0) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  float* dst = a.out + ((int64_t)qi * a.H + head) * kDC + d0;
+  *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if (a.lse != nullptr && threadIdx.x == 0)
     a.lse[(int64_t)qi * a.H + head] =
         lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
@@ -595,7 +600,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   if (e != hipSuccess) return e;
   if (timed) timing_stop(tslot, s);
   if (p.n_split > 1) {
-    combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kDC / 4, 0, s>>>(a, p);
+    combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kCombineThreads, 0, s>>>(a, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int fx = a.Q.nq < 1024 ? a.Q.nq : 1024;

@@ -603,7 +603,7 @@ __device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_f16 %0, %1, %16, %0\n"
       "ds_read_b128 %5, %44 offset:384\n"
-      "s_add_u32 m0, %53, 4096\n"
+      "s_add_u32 m0, %53, 4160\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %54, off\n"
       "s_waitcnt lgkmcnt(3)\n"
@@ -621,7 +621,7 @@ __device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_f16 %0, %1, %21, %0\n"
       "ds_read_b128 %5, %45 offset:512\n"
-      "s_add_u32 m0, %53, 8192\n"
+      "s_add_u32 m0, %53, 8320\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %55, off\n"
       "s_waitcnt lgkmcnt(3)\n"
@@ -639,7 +639,7 @@ __device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const 
       "s_waitcnt lgkmcnt(3)\n"
       "v_mfma_f32_32x32x16_f16 %0, %1, %26, %0\n"
       "ds_read_b128 %5, %42 offset:768\n"
-      "s_add_u32 m0, %53, 12288\n"
+      "s_add_u32 m0, %53, 12480\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %56, off\n"
       "s_waitcnt lgkmcnt(3)\n"

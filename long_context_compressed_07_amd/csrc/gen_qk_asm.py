@@ -14,8 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TARGET = os.path.join(HERE, "attend_tile.h")
 NL = "\\n"
 N = 36      # k-steps of a 576-dim row (16 dims each)
-D = 4       # K-fragment reads in flight
-T = 5       # rotating K-fragment registers
+D = 4       # K-fragment reads in flight (default)
+D_RG2 = 4        # K-fragment reads in flight in the 64-head bf16 block
+C_QK = 1         # independent accumulation chains per QK block (summed on return)
+ST_PAIR = 1040   # fp8 staging: bytes between latent row pairs (kStPair in attend_fp8.hip)
 
 
 class Ops:
@@ -35,12 +37,14 @@ class Ops:
         return None  # numbered after outputs
 
 
-def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v):
+def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
     """Returns (asm text lines, outputs, inputs) for one QK block.
 
     dmas: list of DMA ops, each (m0_operand, m0_imm, load_mnemonic, addr_operands) where operands
     are symbolic names resolved below."""
-    outs = ["acc", "t0", "t1", "t2", "t3", "t4"] + ["vr[%d]" % i for i in range(2 * nv)]
+    T = D + 1   # rotating K-fragment registers
+    accs = ["acc"] if C == 1 else ["acc", "acc2"]   # C independent accumulation chains
+    outs = accs + ["t%d" % i for i in range(T)] + ["vr[%d]" % i for i in range(2 * nv)]
     ins = [("q[%d]" % i, q_lat_cons if i < 32 else "v") for i in range(36)]
     ins += [("lb[%d]" % i, "v") for i in range(4)] + [("rb[%d]" % i, "v") for i in range(4)]
     if nv:
@@ -67,9 +71,10 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v):
     def emit(x):
         L.append('"%s%s"' % (x, NL))
 
-    t = ["t0", "t1", "t2", "t3", "t4"]
+    t = ["t%d" % i for i in range(T)]
     for j in range(D):
-        emit("ds_read_b128 %s, %s" % (op(t[j]), op("lb[%d]" % j)))
+        emit("ds_read_b128 %s, %s%s" % (op(t[j]), op("lb[%d]" % (j & 3)),
+                                        "" if j < 4 else " offset:%d" % (128 * (j >> 2))))
     vreads = []
     for f in range(nv):
         ks, mt = f // 4, f % 4
@@ -89,8 +94,9 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v):
         allowed = (kissued - st - 1) + issued_tr
         assert allowed <= 15
         emit("s_waitcnt lgkmcnt(%d)" % allowed)
-        src = "0" if st == 0 else op("acc")
-        emit("%s %s, %s, %s, %s" % (mnemonic, op("acc"), op(t[st % T]), op("q[%d]" % st), src))
+        a = accs[st % C]
+        src = "0" if st < C else op(a)
+        emit("%s %s, %s, %s, %s" % (mnemonic, op(a), op(t[st % T]), op("q[%d]" % st), src))
         nx = st + D
         if nx < N:
             if nx < 32:
@@ -141,7 +147,8 @@ def bf16_dmas(nlat, nrope, tk):
 def f8_dmas():
     d = [("dma.m0_sel", 0, "global_load_lds_dword", [("dma.sel", "v")])]
     for i in range(4):
-        d.append(("dma.m0_lat", 4096 * i, "global_load_lds_dwordx4", [("dma.lat[%d]" % i, "v")]))
+        d.append(("dma.m0_lat", 4 * ST_PAIR * i, "global_load_lds_dwordx4",
+                  [("dma.lat[%d]" % i, "v")]))
     d.append(("dma.m0_rope", 0, "global_load_lds_dwordx4", [("dma.rope", "v")]))
     d.append(("dma.m0_scl", 0, "global_load_lds_dword", [("dma.scl", "v")]))
     return d
@@ -158,24 +165,24 @@ def main():
            "                                             const int (&rb)[4], int ve, int vo,",
            "                                             v2i (&vr)[NV > 0 ? 2 * NV : 1],",
            "                                             const TileDma<NLAT, NROPE>& dma) {",
-           "  floatx16 acc;",
-           "  v4i t0, t1, t2, t3, t4;",
+           "  floatx16 acc" + (", acc2" if C_QK == 2 else "") + ";",
+           "  v4i " + ", ".join("t%d" % i for i in range(D_RG2 + 1)) + ";",
            "  if constexpr (QA && NV == 16 && NLAT == 16 && NROPE == 2 && TK == 64) {",
-           block("v_mfma_f32_32x32x16_bf16", "a", 16, bf16_dmas(16, 2, 64), 64),
+           block("v_mfma_f32_32x32x16_bf16", "a", 16, bf16_dmas(16, 2, 64), 64, D=D_RG2, C=C_QK),
            "  } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {",
-           block("v_mfma_f32_32x32x16_bf16", "v", 0, bf16_dmas(8, 1, 32), 32),
+           block("v_mfma_f32_32x32x16_bf16", "v", 0, bf16_dmas(8, 1, 32), 32, C=C_QK),
            "  } else {",
            "    static_assert(QA && NV == 16, \"unsupported configuration\");",
            "  }",
-           "  return acc;",
+           "  return acc" + (" + acc2" if C_QK == 2 else "") + ";",
            "}",
            "",
            "__device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const int (&lb)[4],",
            "                                                 const int (&rb)[4], const TileDmaF8& dma) {",
-           "  floatx16 acc;",
+           "  floatx16 acc" + (", acc2" if C_QK == 2 else "") + ";",
            "  v4i t0, t1, t2, t3, t4;",
-           block("v_mfma_f32_32x32x16_f16", "v", 0, f8_dmas(), 32),
-           "  return acc;",
+           block("v_mfma_f32_32x32x16_f16", "v", 0, f8_dmas(), 32, C=C_QK),
+           "  return acc" + (" + acc2" if C_QK == 2 else "") + ";",
            "}",
            ""]
     src = src[:b0] + "\n".join(gen) + src[b1:]

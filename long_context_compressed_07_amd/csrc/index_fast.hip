@@ -152,8 +152,8 @@ __device__ __forceinline__ half8 e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
                (_Float16)p2.x, (_Float16)p2.y, (_Float16)p3.x, (_Float16)p3.y};
 }
 
-// Workgroup (query qi, chunk c) covers entries [c * per_wg, (c + 1) * per_wg); each wave step
-// handles 16 entries. The fp8 codes are widened exactly to fp16 and contracted with the fp16
+// Workgroup (query qi, chunk c) covers entries [c * per_wg, (c + 1) * per_wg) (per_wg a multiple
+// of 512); each wave step handles 16 entries. The fp8 codes are widened exactly to fp16 and contracted with the fp16
 // MFMA (fp32 accumulation): the fp8 MFMA's own accumulation is narrower than fp32, which would
 // move scores by ~2^-14 of the row maximum and with them near-boundary selections.
 __global__ void __launch_bounds__(256) index_fp8_stream_kernel(IndexArgs a, int64_t per_wg,
@@ -168,36 +168,49 @@ __global__ void __launch_bounds__(256) index_fp8_stream_kernel(IndexArgs a, int6
   const int64_t j1 = j0 + per_wg < nv ? j0 + per_wg : nv;
   if (j0 >= j1) return;
   // A fragments: head `col` (< 8 real), dims 16 g + 8 s + [0, 8) for k-step s.
-  half8 a0 = half8{0, 0, 0, 0, 0, 0, 0, 0}, a1 = a0;
-  if (col < 8) {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q_i) + ((int64_t)qi * 8 + col) * 64 + 16 * g;
-    const uint4 v = *reinterpret_cast<const uint4*>(qp);
-    a0 = e4m3x8_to_f16(v.x, v.y);
-    a1 = e4m3x8_to_f16(v.z, v.w);
-  }
+  // (Loads are unconditional, from clamped indices, so that they are all in flight together.)
+  const uint8_t* qp =
+      static_cast<const uint8_t*>(a.q_i) + ((int64_t)qi * 8 + (col & 7)) * 64 + 16 * g;
+  const uint4 qv = *reinterpret_cast<const uint4*>(qp);
   float wh[4];   // w_h * scale_q,h for the heads of this lane's accumulators (4 g + i)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    wh[i] = h < 8 ? a.w[(int64_t)qi * 8 + h] * a.q_i_scale[(int64_t)qi * 8 + h] : 0.f;
+    const int h = (4 * g + i) & 7;
+    wh[i] = a.w[(int64_t)qi * 8 + h] * a.q_i_scale[(int64_t)qi * 8 + h];
+    wh[i] = g < 2 ? wh[i] : 0.f;
   }
+  const half8 zero8 = half8{0, 0, 0, 0, 0, 0, 0, 0};
+  const half8 a0 = col < 8 ? e4m3x8_to_f16(qv.x, qv.y) : zero8;
+  const half8 a1 = col < 8 ? e4m3x8_to_f16(qv.z, qv.w) : zero8;
   const uint8_t* kb = static_cast<const uint8_t*>(a.k_i) + b * a.N * 64;
   const float* ks = a.k_i_scale + b * a.N;
   float* out = a.scores + (int64_t)qi * a.ld_scores;
-#pragma unroll 4
-  for (int64_t e = j0 + 16 * w; e < j1; e += 64) {
-    const int64_t ent = e + col;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (ent < j1) v = *reinterpret_cast<const uint4*>(kb + ent * 64 + 16 * g);
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, e4m3x8_to_f16(v.x, v.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, e4m3x8_to_f16(v.z, v.w), acc, 0, 0, 0);
-    // acc[i] = q-head (4 g + i) . entry `ent` (codes); groups 0, 1 hold the 8 real heads.
-    float p = 0.f;
+  // Batches of 8 steps per wave (128 entries; 512 per workgroup): all 8 row loads and scale loads
+  // are issued before any is used. Rows past the end are clamped to the last entry (loaded, not
+  // stored), so the loads need no branches.
+  for (int64_t base = j0 + 128 * w; base < j1; base += 512) {
+    uint4 v[8];
+    float sc[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p = fmaf(wh[i], fmaxf(acc[i], 0.f), p);
-    p += __shfl_xor(p, 16);
-    if (g == 0 && ent < j1) out[ent] = p * ks[ent];
+    for (int u = 0; u < 8; ++u) {
+      int64_t ent = base + 16 * u + col;
+      ent = ent < j1 ? ent : j1 - 1;
+      v[u] = *reinterpret_cast<const uint4*>(kb + ent * 64 + 16 * g);
+      sc[u] = ks[ent];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, e4m3x8_to_f16(v[u].x, v[u].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, e4m3x8_to_f16(v[u].z, v[u].w), acc, 0, 0, 0);
+      // acc[i] = q-head (4 g + i) . entry (codes); groups 0, 1 hold the 8 real heads.
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p = fmaf(wh[i], fmaxf(acc[i], 0.f), p);
+      p += __shfl_xor(p, 16);
+      const int64_t ent = base + 16 * u + col;
+      if (g == 0 && ent < j1) out[ent] = p * sc[u];
+    }
   }
 }
 
@@ -215,7 +228,7 @@ bool index_fast(const IndexArgs& a, hipStream_t s, hipError_t* err) {
     // Enough workgroups to keep every CU streaming: >= 2048 in total, >= 1024 entries each.
     int64_t per_wg = (a.N * a.Q.nq + 2047) / 2048;
     per_wg = per_wg < 1024 ? 1024 : per_wg;
-    per_wg = (per_wg + 63) / 64 * 64;
+    per_wg = (per_wg + 511) / 512 * 512;
     const int64_t nx = (a.N + per_wg - 1) / per_wg;
     if (nx == 0) { *err = hipSuccess; return true; }
     index_fp8_stream_kernel<<<(unsigned)(nx * a.Q.nq), 256, 0, s>>>(a, per_wg, (int)nx);
