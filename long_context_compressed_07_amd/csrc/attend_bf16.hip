@@ -39,78 +39,6 @@
 namespace csa {
 namespace {
 
-// Row addressing of the two stores for one sequence, computed once per workgroup (kept as plain
-// scalars: a runtime-indexed array would live in scratch memory).
-struct RowBases {
-  const char* c0;          // latent rows of sequence b in the entry store
-  const char* c1;          // ... in the raw window store
-  const char* r0;          // RoPE rows, entry store
-  const char* r1;          // RoPE rows, raw window store
-  uint32_t ldc0, ldc1, ldr0, ldr1;   // row strides in bytes
-};
-
-__device__ __forceinline__ RowBases row_bases(const AttendArgs& a, int64_t b) {
-  RowBases rb;
-  rb.c0 = static_cast<const char*>(a.ent.c) + b * a.ent.rows * a.ent.ld_c * 2;
-  rb.r0 = static_cast<const char*>(a.ent.r) + b * a.ent.rows * a.ent.ld_r * 2;
-  rb.ldc0 = (uint32_t)(a.ent.ld_c * 2);
-  rb.ldr0 = (uint32_t)(a.ent.ld_r * 2);
-  const bool win = a.raw.c != nullptr;
-  rb.c1 = win ? static_cast<const char*>(a.raw.c) + b * a.raw.rows * a.raw.ld_c * 2 : rb.c0;
-  rb.r1 = win ? static_cast<const char*>(a.raw.r) + b * a.raw.rows * a.raw.ld_r * 2 : rb.r0;
-  rb.ldc1 = win ? (uint32_t)(a.raw.ld_c * 2) : rb.ldc0;
-  rb.ldr1 = win ? (uint32_t)(a.raw.ld_r * 2) : rb.ldr0;
-  return rb;
-}
-
-// Global addresses of one key's latent and RoPE parts (a zero row for an empty slot).
-struct KeyAddr {
-  const char* lat;
-  const char* rope;
-};
-
-__device__ __forceinline__ KeyAddr key_addr(const RowBases& rb, int code) {
-  KeyAddr k;
-  if (code < 0) {
-    k.lat = k.rope = reinterpret_cast<const char*>(kZeroRow);
-  } else {
-    const bool raw = code >> 30;
-    const uint64_t row = (uint32_t)(code & 0x3fffffff);
-    k.lat = (raw ? rb.c1 : rb.c0) + row * (raw ? rb.ldc1 : rb.ldc0);
-    k.rope = (raw ? rb.r1 : rb.r0) + row * (raw ? rb.ldr1 : rb.ldr0);
-  }
-  return k;
-}
-
-// Issue the DMA of one tile (TK rows) into buf = [latent region TK x 1024 B][RoPE region TK x 128 B].
-// addr[r] holds the global addresses of row r. Latent: one instruction per row (wave w takes rows
-// w, w + 4, ...): the row address is a scalar base and lane l adds 16 (l ^ f(row)). RoPE: one
-// instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk (l & 7) ^ f(row).
-template <int TK>
-__device__ __forceinline__ void dma_tile(const KeyAddr* addr, char* buf) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // Lane j holds the latent address of row 4 j + w; rows of one wave have f(row) in {f(w), f(w + 4)}.
-  const char* mine = lane < TK / 4 ? addr[4 * lane + w].lat : nullptr;
-  const uint32_t off0 = 16 * (lane ^ swz(w)), off1 = 16 * (lane ^ swz(w + 4));
-#pragma unroll
-  for (int j = 0; j < TK / 4; ++j) {
-    const int r = 4 * j + w;
-    const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                               (int)(uint32_t)(uintptr_t)mine, j)) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                               (int)(uint32_t)((uintptr_t)mine >> 32), j) << 32);
-    const char* src = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
-    __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + 1024 * r), 16, 0, 0);
-  }
-  char* rbuf = buf + TK * 1024;
-#pragma unroll
-  for (int j = w; j < TK / 8; j += 4) {
-    const int r = 8 * j + (lane >> 3);
-    const char* src = addr[r].rope + 16 * ((lane & 7) ^ swz(r));
-    __builtin_amdgcn_global_load_lds(src, (lds_char*)(rbuf + 1024 * j), 16, 0, 0);
-  }
-}
-
 template <int RG, int NBUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attend_bf16_kernel(AttendArgs a, AttnPlan plan) {

@@ -34,6 +34,7 @@
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
 // rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
 #include <algorithm>
+#include <cstdlib>
 
 #include "attend_generic.h"
 #include "attend_plan.h"
@@ -434,6 +435,13 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
 // workgroups (n_split), merged by combine_kernel.
 enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 
+// CSA_ATTEND_PP=0 selects the single-role 64-head kernel instead of the two-role one (for
+// comparisons).
+static bool pp_disabled() {
+  const char* e = std::getenv("CSA_ATTEND_PP");
+  return e != nullptr && e[0] == '0';
+}
+
 MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
   MfmaPlan p{};
   const int groups32 = H / 32;
@@ -446,6 +454,7 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
   if (kind == kPlanBf16 && groups32 % 2 == 0) {
     p.bf16_dma = 1;
     p.rg = groups32 % 4 == 0 ? 4 : 2;
+    p.pp = p.rg == 2 && !pp_disabled();
     p.head_groups = groups32 / p.rg;
     p.n_split = splits_for(p.head_groups, cap);
     return p;
@@ -582,7 +591,10 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   const bool fp8 = a.ent.dtype == CSA_E4M3;
   const int tslot = a.dense ? 1 : 0;
   const bool timed = timing_start(tslot, s);
-  if (p.bf16_dma) {
+  if (p.pp) {
+    hipError_t e = launch_attend_pp(a, p, s);
+    if (e != hipSuccess) return e;
+  } else if (p.bf16_dma) {
     hipError_t e = launch_attend_bf16(a, p, s);
     if (e != hipSuccess) return e;
   } else if (p.f8_dma) {

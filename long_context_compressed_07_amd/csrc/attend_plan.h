@@ -13,6 +13,7 @@ struct AttnPlan {
   int n_split;        // workgroups per query along keys
   int bf16_dma;       // 1: bf16 rows staged by DMA (attend_bf16.hip); 0: fp16 staging
   int f8_dma;         // 1: fp8 rows staged by DMA and converted in LDS (attend_fp8.hip)
+  int pp;             // 1: bf16, 64 heads per workgroup, QK and PV wave roles (attend_pp.hip)
   _Float16* ws_o;     // [nq][n_split][H][512] partial outputs normalised by their l, n_split > 1
   float* ws_ml;       // [nq][n_split][H][2] partial (max in log2 units, sum)
   int* flags;         // [nq][head_groups][n_split] 1 = some head left the range of P
@@ -28,5 +29,6 @@ __device__ __forceinline__ void store_partial4(_Float16* dst, float a, float b, 
 
 hipError_t launch_attend_bf16(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_fp8(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_attend_pp(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 
 }  // namespace csa

@@ -1,0 +1,454 @@
+// MFMA attention for bf16 caches with 64 heads per workgroup (csa_attend / hca_attend; 512
+// latent + 64 RoPE dims per row, bf16 queries): the 64-head prefill path, with the work of each
+// key tile split between two wave roles that share every SIMD.
+//
+// Method: deepseek.csdn.net "一文搞懂 DeepSeek" V4 改进一 (CSA: selected compressed rows plus the
+// raw window, MQA with one KV shared by every head; HCA: dense over the m'-compressed rows) and the
+// MLA section (key row = [latent; RoPE key], value row = latent); yudonglee.me "DeepSeek-V4 详解"
+// 2.2 Step 4 and 2.3 Step 2.
+//
+// A workgroup is 8 waves, 2 per SIMD, serving the 64 heads (two row groups of 32) of one query.
+// Key rows reach LDS by DMA in tiles of 32 rows (the layout of attend_tile.h), four buffers deep.
+// In iteration i:
+//   QK waves 0-3 (row group w & 1, key half w >> 1) compute S^T[16 keys x 32 heads] = K . Q^T
+//     for tile i with 36 mfma_f32_16x16x32_bf16 (Q^T of the row group in registers, its latent
+//     part in accumulation registers), issue the DMA of tile i + 2 and the selection indices of
+//     tile i + 5 from inside that instruction block, apply the softmax with the fixed per-head
+//     reference, and write P (fp16) for the PV waves;
+//   PV waves 4-7 (value dims [128 p, 128 p + 128), p = w - 4) accumulate
+//     O^T[128 dims x 64 heads] += V^T . P^T for tile i - 1 with 16 mfma_f32_32x32x16_f16, V^T
+//     read transposed (ds_read_b64_tr_b16) and converted to fp16 in registers; waves 4 and 5
+//     also compute the key codes and row addresses of tile i + 3.
+// One barrier closes each iteration. Each SIMD holds one wave of each role, so while one runs its
+// softmax, conversions or LDS traffic the other keeps the matrix unit busy.
+//
+// Numerics as in attend_bf16.hip: bf16 products exact in fp32, V converted to fp16 (exact in
+// fp16's normal range), P fp16, fixed reference maximum from the first tile that holds a key, and a
+// non-finite output flags the workgroup for the fp32 fixup pass.
+#include "attend_generic.h"
+#include "attend_plan.h"
+#include "attend_tile.h"
+
+namespace csa {
+namespace {
+
+constexpr int kPpTK = 32;                   // keys per tile
+constexpr int kPpBuf = 4;                   // tile buffers: PV (i-1), QK (i), DMA (i+1, i+2)
+constexpr int kPpTileB = kPpTK * kRowB;     // 32 x (1024 + 128) bytes
+constexpr int kPpRowOps = kPpTK / 4 + 1;    // row DMA instructions per QK wave and tile
+constexpr int kPpR = 64;                    // heads per workgroup
+
+// Q^T fragments of a QK wave for mfma_f32_16x16x32_bf16: q[2 s + h] = Q[head 16 h + (lane & 15)]
+// [dims 32 s + 8 (lane >> 4) + (0..7)] of the row group. The 32 latent fragments go straight into
+// accumulation registers, in one block that waits for its loads.
+__device__ __forceinline__ void load_q16(const uint16_t* q0, const uint16_t* q1, v4i (&q)[36]) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const uint16_t* p0 = q0 + 8 * g;
+  const uint16_t* p1 = q1 + 8 * g;
+  asm volatile(
+      "global_load_dwordx4 %0, %32, off offset:0\n"
+      "global_load_dwordx4 %1, %33, off offset:0\n"
+      "global_load_dwordx4 %2, %32, off offset:64\n"
+      "global_load_dwordx4 %3, %33, off offset:64\n"
+      "global_load_dwordx4 %4, %32, off offset:128\n"
+      "global_load_dwordx4 %5, %33, off offset:128\n"
+      "global_load_dwordx4 %6, %32, off offset:192\n"
+      "global_load_dwordx4 %7, %33, off offset:192\n"
+      "global_load_dwordx4 %8, %32, off offset:256\n"
+      "global_load_dwordx4 %9, %33, off offset:256\n"
+      "global_load_dwordx4 %10, %32, off offset:320\n"
+      "global_load_dwordx4 %11, %33, off offset:320\n"
+      "global_load_dwordx4 %12, %32, off offset:384\n"
+      "global_load_dwordx4 %13, %33, off offset:384\n"
+      "global_load_dwordx4 %14, %32, off offset:448\n"
+      "global_load_dwordx4 %15, %33, off offset:448\n"
+      "global_load_dwordx4 %16, %32, off offset:512\n"
+      "global_load_dwordx4 %17, %33, off offset:512\n"
+      "global_load_dwordx4 %18, %32, off offset:576\n"
+      "global_load_dwordx4 %19, %33, off offset:576\n"
+      "global_load_dwordx4 %20, %32, off offset:640\n"
+      "global_load_dwordx4 %21, %33, off offset:640\n"
+      "global_load_dwordx4 %22, %32, off offset:704\n"
+      "global_load_dwordx4 %23, %33, off offset:704\n"
+      "global_load_dwordx4 %24, %32, off offset:768\n"
+      "global_load_dwordx4 %25, %33, off offset:768\n"
+      "global_load_dwordx4 %26, %32, off offset:832\n"
+      "global_load_dwordx4 %27, %33, off offset:832\n"
+      "global_load_dwordx4 %28, %32, off offset:896\n"
+      "global_load_dwordx4 %29, %33, off offset:896\n"
+      "global_load_dwordx4 %30, %32, off offset:960\n"
+      "global_load_dwordx4 %31, %33, off offset:960\n"
+      "s_waitcnt vmcnt(0)\n"
+      : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]),
+        "=a"(q[7]), "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]),
+        "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]),
+        "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]),
+        "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
+      : "v"(p0), "v"(p1));
+#pragma unroll
+  for (int s = 16; s < 18; ++s) {
+    q[2 * s] = *reinterpret_cast<const v4i*>(p0 + 32 * s);
+    q[2 * s + 1] = *reinterpret_cast<const v4i*>(p1 + 32 * s);
+  }
+}
+
+__global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan plan) {
+  constexpr int TK = kPpTK;
+  constexpr int R = kPpR;
+  __shared__ __attribute__((aligned(1024))) char kv[kPpBuf][kPpTileB];
+  __shared__ __attribute__((aligned(16))) char s_p[2][4 * 1024];   // P^T of tiles i, i + 1
+  __shared__ int s_code[kPpBuf][TK];
+  __shared__ KeyAddr s_addr[kPpBuf][TK];
+  __shared__ int s_sel[3][64];          // selection slots of tiles i + 3 (read), i + 4, i + 5
+  __shared__ float s_ref[2][R];         // per key half: maxima of the reference tile
+  __shared__ float s_l[2][R];           // per key half: softmax sums
+  __shared__ float s_m[R];              // reference maxima
+  __shared__ int s_flag;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hi = lane >> 5;
+  const int per_q = plan.head_groups * plan.n_split;
+  const int qi = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qi * per_q;
+  const int hgrp = rem / plan.n_split;
+  const int split = rem - hgrp * plan.n_split;
+  const int hbase = hgrp * R;
+  if (threadIdx.x == 0) s_flag = 0;
+
+  const KeyList kl = make_key_list(a, qi);
+  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
+  const int64_t k0 = (int64_t)split * per_split;
+  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
+  const RowBases rbases = row_bases(a, kl.b);
+  const bool sel_dma = kl.sel != nullptr;   // CSA: selection slots come from idx
+  const KeyCodes32 kc = key_codes32(kl, ke);
+  const int nt = ke > k0 ? (int)((ke - k0 + TK - 1) / TK) : 0;
+  const float cscale = a.sm_scale * kLog2e;
+
+  // Prologue, in parallel: the QK waves load their queries while wave 4 computes the codes of
+  // tiles 0-2, copies the selection slots of tiles 3 and 4 and issues (and waits for) the DMA of
+  // tiles 0 and 1, all rows.
+  if (w < 4) {
+    // ================================ QK waves ================================
+    const int rg = w & 1, kh = w >> 1;
+    const int c = lane & 15, g = lane >> 4;
+    v4i qb[36];
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + 32 * rg + c) * kD;
+    load_q16(qrow, qrow + 16 * kD, qb);
+    __syncthreads();
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    bool have_ref = false;
+    // K fragment of key row 16 kh + c: chunk 4 s + g (latent k-step s) sits at (4 s + g) ^ f.
+    const int r = 16 * kh + c;
+    const int f = swz(r);
+    const int oe = 16 * (g ^ f), oo = 16 * ((4 | g) ^ f);
+    const int lat_off = r * 1024, rope_off = TK * 1024 + r * 128;
+
+    auto tile = [&](const char* __restrict__ cbuf, char* __restrict__ nbuf,
+                    char* __restrict__ pbuf, int i) {
+      const int64_t t0 = k0 + (int64_t)i * TK;
+      const int slot = i % kPpBuf;
+      TileDma<TK / 4, TK / 32> dma;
+      {
+        const int64_t kk = t0 + 5 * TK + lane;
+        dma.sel = (sel_dma && lane < TK && kk < ke && kk < kl.n_sel)
+                      ? reinterpret_cast<const char*>(kl.sel + kk)
+                      : reinterpret_cast<const char*>(kZeroRow);
+        const KeyAddr* ad = s_addr[(i + 2) % kPpBuf];
+        const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
+        dma.off[0] = 16 * (lane ^ swz(w));
+        dma.off[1] = 16 * (lane ^ swz(w + 4));
+#pragma unroll
+        for (int j = 0; j < TK / 4; ++j) {
+          const uint64_t base =
+              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uintptr_t)mine, j)) |
+              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uintptr_t)mine >> 32), j)
+               << 32);
+          dma.lat[j] = reinterpret_cast<const char*>(base);
+        }
+        const int rr = 8 * w + (lane >> 3);
+        dma.rope[0] = ad[rr].rope + 16 * ((lane & 7) ^ swz(rr));
+        dma.m0_rows = __builtin_amdgcn_readfirstlane(lds_addr(nbuf) + 1024 * w);
+        dma.m0_sel = __builtin_amdgcn_readfirstlane(
+            lds_addr(reinterpret_cast<const char*>(s_sel[(i + 5) % 3])));
+      }
+      // Whether the tile holds a key / only keys (uniform), from its 32 codes.
+      const int code_l = s_code[slot][lane & (TK - 1)];
+      floatx4 acc[2];
+      const int cb = lds_addr(cbuf);
+      qk16_chain(qb, cb + lat_off + oe, cb + lat_off + oo, cb + rope_off + oe, cb + rope_off + oo,
+                 dma, acc[0], acc[1]);
+      // acc[h][j]: key 16 kh + 4 g + j, head 32 rg + 16 h + c.
+      const bool has_key = __any(code_l >= 0);
+      if (!__all(code_l >= 0)) {
+        const int* codes = s_code[slot];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = codes[16 * kh + 4 * g + j] >= 0;
+          acc[0][j] = ok ? acc[0][j] : -INFINITY;
+          acc[1][j] = ok ? acc[1][j] : -INFINITY;
+        }
+      }
+      if (!have_ref && has_key) {   // uniform over the workgroup (the PV waves match it)
+        float tm[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float t = fmaxf(fmaxf(acc[h][0], acc[h][1]), fmaxf(acc[h][2], acc[h][3])) * cscale;
+          t = fmaxf(t, __shfl_xor(t, 16));
+          t = fmaxf(t, __shfl_xor(t, 32));
+          tm[h] = t;
+        }
+        if (g == 0) {
+          s_ref[kh][32 * rg + c] = tm[0];
+          s_ref[kh][32 * rg + 16 + c] = tm[1];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          m_ref[h] = fmaxf(s_ref[0][32 * rg + 16 * h + c], s_ref[1][32 * rg + 16 * h + c]);
+        have_ref = true;
+      }
+      // Logits more than 2^16 above the reference overflow P's fp16 and reach O as inf/NaN, which
+      // the final check flags. Before the reference (empty tiles) every logit is -inf: P = 0.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float nm = have_ref ? -m_ref[h] : 0.f;
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 ph;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][j], cscale, nm));
+          l_run[h] += p;
+          ph[j] = (_Float16)p;
+        }
+        // P^T fragment (row group rg, k-step kh) of the PV MFMA: lane L = head (16 h + c) +
+        // 32 (g & 1) holds keys 4 (g & 1) + (0..3) then 8 + 4 (g & 1) + (0..3).
+        const int L = 16 * h + c + 32 * (g & 1);
+        *reinterpret_cast<h4*>(pbuf + ((2 * kh + rg) * 64 + L) * 16 + 8 * (g >> 1)) = ph;
+      }
+      // Everything this wave issued before this tile's block (tile i + 1, the selection slots of
+      // tile i + 4) has landed once at most the block's own DMA is outstanding.
+      __builtin_amdgcn_s_waitcnt(kVmcntDma<kPpRowOps + 1>);
+    };
+    for (int i = 0; i <= nt; ++i) {
+      if (i < nt) tile(kv[i % kPpBuf], kv[(i + 2) % kPpBuf], s_p[i & 1], i);
+      lds_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // no DMA may land in LDS after the workgroup has finished
+    // Softmax sums of this wave's keys per head (lanes 16 g + c share head c).
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float l = l_run[h];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      if (g == 0) {
+        s_l[kh][32 * rg + 16 * h + c] = l;
+        if (kh == 0) s_m[32 * rg + 16 * h + c] = m_ref[h];
+      }
+    }
+    lds_barrier();                    // sums and maxima in LDS (epilogue barrier 1)
+    // The PV waves stage and write the outputs in two row groups, two barriers each.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_barrier();
+  } else {
+    // ================================ PV waves ================================
+    if (w == 4) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = lane < TK ? key_code(a, kl, k0 + j * TK + lane, ke) : -1;
+        if (lane < TK) {
+          s_code[j][lane] = c;
+          s_addr[j][lane] = key_addr(rbases, c);
+        }
+      }
+      if (sel_dma) {
+        dma_sel<TK>(kl, k0 + 3 * TK, ke, s_sel[0]);
+        dma_sel<TK>(kl, k0 + 4 * TK, ke, s_sel[1]);
+      }
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        dma_tile<TK>(s_addr[0], kv[0], wv);
+        dma_tile<TK>(s_addr[1], kv[1], wv);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    const int p = w - 4;
+    floatx16 o[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o[mt][0] = o[mt][1] = floatx16{};
+    bool have_ref = false;
+    int v_even, v_odd;   // V^T fragment addressing (the layout and key order of attend_bf16.hip)
+    {
+      const int g = lane >> 4, la = lane & 15;
+      const int f = 2 * (la >> 2) + hi;
+      const int c0 = 2 * (g & 1) + ((la & 3) >> 1);
+      const int f2 = f >> 2;
+      const int base = (4 * hi + (la >> 2)) * 1024 + 16 * (c0 ^ (f & 3)) + 8 * (la & 1) + 256 * p;
+      v_even = base + 64 * f2;
+      v_odd = base - 64 * f2;
+    }
+    // V^T of a tile (16 half-fragments: k-step ks, dim tile mt, rows +0 / +8) is read in the
+    // iteration before its PV, so its latency hides behind that iteration's MFMAs; the P^T
+    // fragments (written by the QK waves in the previous iteration) are read just before use.
+    v2i vr[16];
+    auto read_v = [&](int cb) {
+      const int ve = cb + v_even, vo = cb + v_odd;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n"
+          "ds_read_b64_tr_b16 %1, %16 offset:8192\n"
+          "ds_read_b64_tr_b16 %2, %17 offset:64\n"
+          "ds_read_b64_tr_b16 %3, %17 offset:8256\n"
+          "ds_read_b64_tr_b16 %4, %16 offset:128\n"
+          "ds_read_b64_tr_b16 %5, %16 offset:8320\n"
+          "ds_read_b64_tr_b16 %6, %17 offset:192\n"
+          "ds_read_b64_tr_b16 %7, %17 offset:8384\n"
+          "ds_read_b64_tr_b16 %8, %16 offset:16384\n"
+          "ds_read_b64_tr_b16 %9, %16 offset:24576\n"
+          "ds_read_b64_tr_b16 %10, %17 offset:16448\n"
+          "ds_read_b64_tr_b16 %11, %17 offset:24640\n"
+          "ds_read_b64_tr_b16 %12, %16 offset:16512\n"
+          "ds_read_b64_tr_b16 %13, %16 offset:24704\n"
+          "ds_read_b64_tr_b16 %14, %17 offset:16576\n"
+          "s_waitcnt lgkmcnt(7)\n"
+          "ds_read_b64_tr_b16 %15, %17 offset:24768\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+            "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
+            "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(ve), "v"(vo));
+    };
+    auto pv = [&](int pb) {
+      v4i pf[4];
+      asm volatile(
+          "ds_read_b128 %0, %4\n"
+          "ds_read_b128 %1, %4 offset:1024\n"
+          "ds_read_b128 %2, %4 offset:2048\n"
+          "ds_read_b128 %3, %4 offset:3072\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(pf[0]), "=&v"(pf[1]), "=&v"(pf[2]), "=&v"(pf[3])
+          : "v"(pb + lane * 16));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const v2i* x = &vr[8 * ks + 2 * mt];
+          const f16x8 vf = bf16x8_to_f16((uint32_t)x[0][0], (uint32_t)x[0][1], (uint32_t)x[1][0],
+                                         (uint32_t)x[1][1]);
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg)
+            o[mt][rg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                vf, __builtin_bit_cast(f16x8, pf[2 * ks + rg]), o[mt][rg], 0, 0, 0);
+        }
+    };
+    for (int i = 0; i <= nt; ++i) {
+      if (i < nt && !have_ref) {   // the QK waves' reference barrier, at the first tile with a key
+        if (__any(s_code[i % kPpBuf][lane & (TK - 1)] >= 0)) {
+          lds_barrier();
+          have_ref = true;
+        }
+      }
+      // Selection slots of tile i + 3 (copied during iteration i - 2), read before the PV work so
+      // that their latency is hidden behind it.
+      const int raw2 = (w < 6 && sel_dma) ? s_sel[(i + 3) % 3][lane] : 0;
+      if (i >= 1) pv(lds_addr(s_p[(i - 1) & 1]));
+      if (i < nt) read_v(lds_addr(kv[i % kPpBuf]));   // tile i, for the next iteration
+      // Codes of tile i + 3, split over two waves: wave 4 the codes and flags, wave 5 the row
+      // addresses.
+      if (w == 5 && i < nt) {
+        const int kk2 = (int)k0 + (i + 3) * TK + lane;
+        const int c2 = lane < TK ? key_code32(kc, kk2, raw2) : -1;
+        if (lane < TK) s_addr[(i + 3) % kPpBuf][lane] = key_addr(rbases, c2);
+      }
+      if (w == 4 && i < nt) {
+        const int kk2 = (int)k0 + (i + 3) * TK + lane;
+        const int c2 = lane < TK ? key_code32(kc, kk2, raw2) : -1;
+        const int slot2 = (i + 3) % kPpBuf;
+        if (lane < TK) s_code[slot2][lane] = c2;
+      }
+      lds_barrier();
+    }
+    bool overflow = false;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][rg][i]);
+    if (__any(overflow)) atomicOr(&s_flag, 1);
+    lds_barrier();                    // epilogue barrier 1: sums, maxima and flag complete
+    if (threadIdx.x == 256) plan.flags[blockIdx.x] = s_flag;
+    // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
+    // row group at a time, staged in the (idle) tile buffers by the PV waves, written as rows.
+    char* stage = &kv[0][0];
+    const int pt = threadIdx.x - 256;   // 0 .. 255 over the PV waves
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int hrow = 32 * rg + (lane & 31);
+      const float l = s_l[0][hrow] + s_l[1][hrow];
+      const float m = s_m[hrow];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const int head = hbase + hrow;
+      const int64_t row0 = plan.n_split == 1
+                               ? (int64_t)qi * a.H + hbase + 32 * rg
+                               : ((int64_t)qi * plan.n_split + split) * a.H + hbase + 32 * rg;
+      if (plan.n_split == 1) {
+        char* row = stage + (lane & 31) * kStageLd<float> + (128 * p + 4 * hi) * 4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(row + (32 * mt + 8 * j) * 4) =
+                make_float4(o[mt][rg][4 * j] * inv, o[mt][rg][4 * j + 1] * inv,
+                            o[mt][rg][4 * j + 2] * inv, o[mt][rg][4 * j + 3] * inv);
+        if (a.lse != nullptr && p == 0 && hi == 0)
+          a.lse[(int64_t)qi * a.H + head] =
+              l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
+      } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        char* row = stage + (lane & 31) * kStageLd<_Float16> + (128 * p + 4 * hi) * 2;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<h4*>(row + (32 * mt + 8 * j) * 2) =
+                h4{(_Float16)(o[mt][rg][4 * j] * inv), (_Float16)(o[mt][rg][4 * j + 1] * inv),
+                   (_Float16)(o[mt][rg][4 * j + 2] * inv), (_Float16)(o[mt][rg][4 * j + 3] * inv)};
+        if (p == 0 && hi == 0) {
+          const int64_t pidx = row0 + (lane & 31);
+          plan.ws_ml[pidx * 2] = m;
+          plan.ws_ml[pidx * 2 + 1] = l;
+        }
+      }
+      lds_barrier();                  // rows staged (the QK waves take part in every barrier)
+      if (plan.n_split == 1) {
+        constexpr int kCh = 512 * 4 / 16;
+        for (int ci = pt; ci < 32 * kCh; ci += 256) {
+          const int h = ci / kCh, k = ci - h * kCh;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kStageLd<float> + 16 * k);
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.out + (row0 + h) * kDC) + 16 * k) = v;
+        }
+      } else {
+        constexpr int kCh = 512 * 2 / 16;
+        for (int ci = pt; ci < 32 * kCh; ci += 256) {
+          const int h = ci / kCh, k = ci - h * kCh;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kStageLd<_Float16> + 16 * k);
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(plan.ws_o + (row0 + h) * kDC) + 16 * k) = v;
+        }
+      }
+      lds_barrier();                  // rows written, staging area free
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend_pp(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
+  attend_pp_kernel<<<grid, 512, 0, s>>>(a, p);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -18,6 +18,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -126,6 +127,80 @@ __device__ __forceinline__ void flush_rows(const char* buf, T* dst) {
     const int h = c / kChunksRow, k = c - h * kChunksRow;
     const uint4 v = *reinterpret_cast<const uint4*>(buf + h * kStageLd<T> + 16 * k);
     *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + (int64_t)h * 512) + 16 * k) = v;
+  }
+}
+
+// ---- bf16 caches: row addressing and the prologue's tile DMA ----------------------------------
+
+// Row addressing of the two stores for one sequence, computed once per workgroup (kept as plain
+// scalars: a runtime-indexed array would live in scratch memory).
+struct RowBases {
+  const char* c0;          // latent rows of sequence b in the entry store
+  const char* c1;          // ... in the raw window store
+  const char* r0;          // RoPE rows, entry store
+  const char* r1;          // RoPE rows, raw window store
+  uint32_t ldc0, ldc1, ldr0, ldr1;   // row strides in bytes
+};
+
+__device__ __forceinline__ RowBases row_bases(const AttendArgs& a, int64_t b) {
+  RowBases rb;
+  rb.c0 = static_cast<const char*>(a.ent.c) + b * a.ent.rows * a.ent.ld_c * 2;
+  rb.r0 = static_cast<const char*>(a.ent.r) + b * a.ent.rows * a.ent.ld_r * 2;
+  rb.ldc0 = (uint32_t)(a.ent.ld_c * 2);
+  rb.ldr0 = (uint32_t)(a.ent.ld_r * 2);
+  const bool win = a.raw.c != nullptr;
+  rb.c1 = win ? static_cast<const char*>(a.raw.c) + b * a.raw.rows * a.raw.ld_c * 2 : rb.c0;
+  rb.r1 = win ? static_cast<const char*>(a.raw.r) + b * a.raw.rows * a.raw.ld_r * 2 : rb.r0;
+  rb.ldc1 = win ? (uint32_t)(a.raw.ld_c * 2) : rb.ldc0;
+  rb.ldr1 = win ? (uint32_t)(a.raw.ld_r * 2) : rb.ldr0;
+  return rb;
+}
+
+// Global addresses of one key's latent and RoPE parts (a zero row for an empty slot).
+struct KeyAddr {
+  const char* lat;
+  const char* rope;
+};
+
+__device__ __forceinline__ KeyAddr key_addr(const RowBases& rb, int code) {
+  KeyAddr k;
+  if (code < 0) {
+    k.lat = k.rope = reinterpret_cast<const char*>(kZeroRow);
+  } else {
+    const bool raw = code >> 30;
+    const uint64_t row = (uint32_t)(code & 0x3fffffff);
+    k.lat = (raw ? rb.c1 : rb.c0) + row * (raw ? rb.ldc1 : rb.ldc0);
+    k.rope = (raw ? rb.r1 : rb.r0) + row * (raw ? rb.ldr1 : rb.ldr0);
+  }
+  return k;
+}
+
+// Issue the DMA of one tile (TK rows) into buf = [latent region TK x 1024 B][RoPE region TK x 128 B].
+// addr[r] holds the global addresses of row r. Latent: one instruction per row (wave w takes rows
+// w, w + 4, ...): the row address is a scalar base and lane l adds 16 (l ^ f(row)). RoPE: one
+// instruction per 8 rows, lane l fetching row 8 j + l / 8, chunk (l & 7) ^ f(row).
+template <int TK>
+__device__ __forceinline__ void dma_tile(const KeyAddr* addr, char* buf, int w = threadIdx.x >> 6) {
+  const int lane = threadIdx.x & 63;
+  // Lane j holds the latent address of row 4 j + w; rows of one wave have f(row) in {f(w), f(w + 4)}.
+  const char* mine = lane < TK / 4 ? addr[4 * lane + w].lat : nullptr;
+  const uint32_t off0 = 16 * (lane ^ swz(w)), off1 = 16 * (lane ^ swz(w + 4));
+#pragma unroll
+  for (int j = 0; j < TK / 4; ++j) {
+    const int r = 4 * j + w;
+    const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                               (int)(uint32_t)(uintptr_t)mine, j)) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                               (int)(uint32_t)((uintptr_t)mine >> 32), j) << 32);
+    const char* src = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
+    __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + 1024 * r), 16, 0, 0);
+  }
+  char* rbuf = buf + TK * 1024;
+#pragma unroll
+  for (int j = w; j < TK / 8; j += 4) {
+    const int r = 8 * j + (lane >> 3);
+    const char* src = addr[r].rope + 16 * ((lane & 7) ^ swz(r));
+    __builtin_amdgcn_global_load_lds(src, (lds_char*)(rbuf + 1024 * j), 16, 0, 0);
   }
 }
 
@@ -553,6 +628,121 @@ __device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int 
     static_assert(QA && NV == 16, "unsupported configuration");
   }
   return acc;
+}
+
+__device__ __forceinline__ void qk16_chain(const v4i (&q)[36], int lbe, int lbo, int rbe,
+                                           int rbo, const TileDma<8, 1>& dma,
+                                           floatx4& acc0, floatx4& acc1) {
+  v4i t0, t1, t2, t3, t4;
+    asm volatile(
+      "ds_read_b128 %2, %43\n"
+      "ds_read_b128 %3, %44\n"
+      "ds_read_b128 %4, %43 offset:128\n"
+      "ds_read_b128 %5, %44 offset:128\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %7, 0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %8, 0\n"
+      "ds_read_b128 %6, %43 offset:256\n"
+      "s_mov_b32 m0, %48\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %47, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %9, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %10, %1\n"
+      "ds_read_b128 %2, %44 offset:256\n"
+      "s_mov_b32 m0, %51\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %49, %50\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %11, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %12, %1\n"
+      "ds_read_b128 %3, %43 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %14, %1\n"
+      "ds_read_b128 %4, %44 offset:384\n"
+      "s_add_u32 m0, %51, 4096\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %52, %53\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %15, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %16, %1\n"
+      "ds_read_b128 %5, %43 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %17, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %18, %1\n"
+      "ds_read_b128 %6, %44 offset:512\n"
+      "s_add_u32 m0, %51, 8192\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %49, %54\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %19, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %20, %1\n"
+      "ds_read_b128 %2, %43 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %21, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %22, %1\n"
+      "ds_read_b128 %3, %44 offset:640\n"
+      "s_add_u32 m0, %51, 12288\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %52, %55\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %23, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %24, %1\n"
+      "ds_read_b128 %4, %43 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %25, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %26, %1\n"
+      "ds_read_b128 %5, %44 offset:768\n"
+      "s_add_u32 m0, %51, 16384\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %49, %56\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %27, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %28, %1\n"
+      "ds_read_b128 %6, %43 offset:896\n"
+      "s_add_u32 m0, %51, 20480\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %52, %57\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %29, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %30, %1\n"
+      "ds_read_b128 %2, %44 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %31, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %32, %1\n"
+      "ds_read_b128 %3, %45\n"
+      "s_add_u32 m0, %51, 24576\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %49, %58\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %33, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %34, %1\n"
+      "ds_read_b128 %4, %46\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %35, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %36, %1\n"
+      "s_add_u32 m0, %51, 28672\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %52, %59\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %37, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %38, %1\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %39, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %40, %1\n"
+      "s_add_u32 m0, %51, 32768\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %60, off\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %41, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %42, %1\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 4\n"
+      : "=&v"(acc0), "=&v"(acc1), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
+      : "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "a"(q[4]), "a"(q[5]), "a"(q[6]), "a"(q[7]), "a"(q[8]), "a"(q[9]), "a"(q[10]), "a"(q[11]), "a"(q[12]), "a"(q[13]), "a"(q[14]), "a"(q[15]), "a"(q[16]), "a"(q[17]), "a"(q[18]), "a"(q[19]), "a"(q[20]), "a"(q[21]), "a"(q[22]), "a"(q[23]), "a"(q[24]), "a"(q[25]), "a"(q[26]), "a"(q[27]), "a"(q[28]), "a"(q[29]), "a"(q[30]), "a"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lbe), "v"(lbo), "v"(rbe), "v"(rbo), "v"(dma.sel), "s"(dma.m0_sel), "v"(dma.off[0]), "s"(dma.lat[0]), "s"(dma.m0_rows), "v"(dma.off[1]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "v"(dma.rope[0])
+      : "m0");
 }
 
 __device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const int (&lb)[4],

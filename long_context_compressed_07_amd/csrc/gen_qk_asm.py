@@ -133,6 +133,86 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
     return text
 
 
+def block16(dmas, D=4):
+    """S^T for 16 keys x 32 heads with v_mfma_f32_16x16x32_bf16: 18 k-steps of 32 dims, two
+    accumulators (heads 0-15, 16-31 of the row group) sharing each K fragment. K-step s reads the
+    lane's 16 bytes at (s & 1 ? lbo : lbe) + 128 (s >> 1) for the latent steps 0-15 and at
+    (s & 1 ? rbo : rbe) for the RoPE steps 16, 17; Q^T fragment of step s and head half h is
+    q[2 s + h] (latent ones from accumulation registers)."""
+    NS = 18
+    T = D + 1
+    outs = ["acc0", "acc1"] + ["t%d" % i for i in range(T)]
+    ins = [("q[%d]" % i, "a" if i < 32 else "v") for i in range(36)]
+    ins += [("lbe", "v"), ("lbo", "v"), ("rbe", "v"), ("rbo", "v")]
+    dma_names = []
+    for d in dmas:
+        for name, cons in d[3]:
+            if (name, cons) not in dma_names:
+                dma_names.append((name, cons))
+        if (d[0], "s") not in dma_names:
+            dma_names.append((d[0], "s"))
+    ins += dma_names
+    num = {}
+    for i, o in enumerate(outs):
+        num[o] = i
+    for j, (name, _) in enumerate(ins):
+        num[name] = len(outs) + j
+
+    def op(x):
+        return "%%%d" % num[x]
+
+    L = []
+
+    def emit(x):
+        L.append('"%s%s"' % (x, NL))
+
+    def kread(st):
+        if st < 16:
+            base = op("lbo" if st & 1 else "lbe")
+            off = 128 * (st >> 1)
+        else:
+            base = op("rbo" if st & 1 else "rbe")
+            off = 0
+        return "%s%s" % (base, "" if off == 0 else " offset:%d" % off)
+
+    t = ["t%d" % i for i in range(T)]
+    for j in range(D):
+        emit("ds_read_b128 %s, %s" % (op(t[j]), kread(j)))
+    nd = len(dmas)
+    place = [min(NS - 1, (i * NS) // nd) for i in range(nd)]
+    di = 0
+    for st in range(NS):
+        allowed = min(NS, st + D) - st - 1
+        assert allowed <= 15
+        emit("s_waitcnt lgkmcnt(%d)" % allowed)
+        for h in range(2):
+            a = "acc%d" % h
+            src = "0" if st == 0 else op(a)
+            emit("v_mfma_f32_16x16x32_bf16 %s, %s, %s, %s" % (op(a), op(t[st % T]),
+                                                              op("q[%d]" % (2 * st + h)), src))
+        nx = st + D
+        if nx < NS:
+            emit("ds_read_b128 %s, %s" % (op(t[nx % T]), kread(nx)))
+        while di < nd and place[di] == st:
+            m0, imm, ld, addr = dmas[di]
+            if imm:
+                emit("s_add_u32 m0, %s, %d" % (op(m0), imm))
+            else:
+                emit("s_mov_b32 m0, %s" % op(m0))
+            emit("s_nop 0")
+            emit("%s %s" % (ld, ", ".join(op(a) if not a.startswith("off") else a
+                                          for a in [x[0] for x in addr] + (["off"] if len(addr) == 1 else []))))
+            di += 1
+    assert di == nd
+    emit("s_nop 7")
+    emit("s_nop 7")
+    emit("s_nop 4")
+    out_s = ", ".join('"=&v"(%s)' % o for o in outs)
+    in_s = ", ".join('"%s"(%s)' % (c, n) for n, c in ins)
+    return "    asm volatile(\n      " + "\n      ".join(L) + "\n      : " + out_s + "\n      : " + \
+        in_s + "\n      : \"m0\");"
+
+
 def bf16_dmas(nlat, nrope, tk):
     d = [("dma.m0_sel", 0, "global_load_lds_dword", [("dma.sel", "v")])]
     for j in range(nlat):
@@ -175,6 +255,13 @@ def main():
            "    static_assert(QA && NV == 16, \"unsupported configuration\");",
            "  }",
            "  return acc" + (" + acc2" if C_QK == 2 else "") + ";",
+           "}",
+           "",
+           "__device__ __forceinline__ void qk16_chain(const v4i (&q)[36], int lbe, int lbo, int rbe,",
+           "                                           int rbo, const TileDma<8, 1>& dma,",
+           "                                           floatx4& acc0, floatx4& acc1) {",
+           "  v4i t0, t1, t2, t3, t4;",
+           block16(bf16_dmas(8, 1, 32)),
            "}",
            "",
            "__device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const int (&lb)[4],",

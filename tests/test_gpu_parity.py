@@ -142,6 +142,16 @@ def test_csa_prefill_128_heads(sharp):
     parity.check_csa(wl, host, step)
 
 
+@pytest.mark.parametrize("sharp", [False, True])
+def test_csa_prefill_64_heads_key_splits(sharp):
+    # Few queries over many keys: 64-head workgroups split each query's keys (partials merged by
+    # the combine kernel).
+    wl = SMALL["C2"].replace(T=8003, nq=6, k=1000, window=40)
+    print(f"[parity] csa prefill 64 heads key splits sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, 21)
+    parity.check_csa(wl, host, step)
+
+
 def test_hca_prefill_128_heads_many_queries():
     # >= 512 queries of 128 heads: four 32-head groups share every staged key tile.
     wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=640, H=128)
