@@ -38,6 +38,30 @@ constexpr int kPpTileB = kPpTK * kRowB;     // 32 x (1024 + 128) bytes
 constexpr int kPpRowOps = kPpTK / 4 + 1;    // row DMA instructions per QK wave and tile
 constexpr int kPpR = 64;                    // heads per workgroup
 
+// Transposed 64-bit LDS read (ds_read_b64_tr_b16) from a pointer into shared memory.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s16 lds_v4s16;
+__device__ __forceinline__ v2i lds_tr16(const char* p) {
+  return __builtin_bit_cast(
+      v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(lds_char*)const_cast<char*>(p)));
+}
+
+// key_code32 and key_addr as selects (no branches), so that the PV waves' code arithmetic can
+// be scheduled among their MFMAs.
+__device__ __forceinline__ int key_code_sel(const KeyCodes32& c, int kk, int raw) {
+  const int v = kk < c.n_sel ? (c.has_sel ? raw : kk) : ((kk + c.woff) | (1 << 30));
+  return (kk >= c.ke || raw < 0) ? -1 : v;
+}
+
+__device__ __forceinline__ KeyAddr key_addr_sel(const RowBases& rb, int code) {
+  const bool raw = (code >> 30) & 1;
+  const uint64_t row = (uint32_t)(code & 0x3fffffff);
+  const char* lat = (raw ? rb.c1 : rb.c0) + row * (raw ? rb.ldc1 : rb.ldc0);
+  const char* rope = (raw ? rb.r1 : rb.r0) + row * (raw ? rb.ldr1 : rb.ldr0);
+  const char* z = reinterpret_cast<const char*>(kZeroRow);
+  return KeyAddr{code < 0 ? z : lat, code < 0 ? z : rope};
+}
+
 // Q^T fragments of a QK wave for mfma_f32_16x16x32_bf16: q[2 s + h] = Q[head 16 h + (lane & 15)]
 // [dims 32 s + 8 (lane >> 4) + (0..7)] of the row group. The 32 latent fragments go straight into
 // accumulation registers, in one block that waits for its loads.
@@ -290,83 +314,84 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       v_even = base + 64 * f2;
       v_odd = base - 64 * f2;
     }
-    // V^T of a tile (16 half-fragments: k-step ks, dim tile mt, rows +0 / +8) is read in the
-    // iteration before its PV, so its latency hides behind that iteration's MFMAs; the P^T
-    // fragments (written by the QK waves in the previous iteration) are read just before use.
-    v2i vr[16];
-    auto read_v = [&](int cb) {
-      const int ve = cb + v_even, vo = cb + v_odd;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16\n"
-          "ds_read_b64_tr_b16 %1, %16 offset:8192\n"
-          "ds_read_b64_tr_b16 %2, %17 offset:64\n"
-          "ds_read_b64_tr_b16 %3, %17 offset:8256\n"
-          "ds_read_b64_tr_b16 %4, %16 offset:128\n"
-          "ds_read_b64_tr_b16 %5, %16 offset:8320\n"
-          "ds_read_b64_tr_b16 %6, %17 offset:192\n"
-          "ds_read_b64_tr_b16 %7, %17 offset:8384\n"
-          "ds_read_b64_tr_b16 %8, %16 offset:16384\n"
-          "ds_read_b64_tr_b16 %9, %16 offset:24576\n"
-          "ds_read_b64_tr_b16 %10, %17 offset:16448\n"
-          "ds_read_b64_tr_b16 %11, %17 offset:24640\n"
-          "ds_read_b64_tr_b16 %12, %16 offset:16512\n"
-          "ds_read_b64_tr_b16 %13, %16 offset:24704\n"
-          "ds_read_b64_tr_b16 %14, %17 offset:16576\n"
-          "s_waitcnt lgkmcnt(7)\n"
-          "ds_read_b64_tr_b16 %15, %17 offset:24768\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
-            "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
-            "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
-          : "v"(ve), "v"(vo));
+    // V^T of a tile (16 half-fragments: k-step ks, dim tile mt, rows +0 / +8) and the P^T
+    // fragments of the tile before it are read at the start of an iteration, ahead of that
+    // iteration's MFMAs (which use the V^T read one iteration earlier), so the reads overlap the
+    // matrix work. The two V^T register sets alternate between iterations (loop unrolled by two).
+    auto read_v = [&](const char* buf, v2i (&vr)[16]) {
+      const char* be = buf + v_even;
+      const char* bo = buf + v_odd;
+      vr[0] = lds_tr16(be);
+      vr[1] = lds_tr16(be + 8192);
+      vr[2] = lds_tr16(bo + 64);
+      vr[3] = lds_tr16(bo + 8256);
+      vr[4] = lds_tr16(be + 128);
+      vr[5] = lds_tr16(be + 8320);
+      vr[6] = lds_tr16(bo + 192);
+      vr[7] = lds_tr16(bo + 8384);
+      vr[8] = lds_tr16(be + 16384);
+      vr[9] = lds_tr16(be + 24576);
+      vr[10] = lds_tr16(bo + 16448);
+      vr[11] = lds_tr16(bo + 24640);
+      vr[12] = lds_tr16(be + 16512);
+      vr[13] = lds_tr16(be + 24704);
+      vr[14] = lds_tr16(bo + 16576);
+      vr[15] = lds_tr16(bo + 24768);
     };
-    auto pv = [&](int pb) {
-      v4i pf[4];
-      asm volatile(
-          "ds_read_b128 %0, %4\n"
-          "ds_read_b128 %1, %4 offset:1024\n"
-          "ds_read_b128 %2, %4 offset:2048\n"
-          "ds_read_b128 %3, %4 offset:3072\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(pf[0]), "=&v"(pf[1]), "=&v"(pf[2]), "=&v"(pf[3])
-          : "v"(pb + lane * 16));
+    auto read_p = [&](const char* pbuf, v4i (&pf)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf[j] = *reinterpret_cast<const v4i*>(pbuf + 1024 * j + 16 * lane);
+    };
+    // O^T += V^T . P^T for one tile: V^T already in fp16 (vh), P^T fragments in pf.
+    auto pv = [&](const f16x8 (&vh)[8], const v4i (&pf)[4]) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const v2i* x = &vr[8 * ks + 2 * mt];
-          const f16x8 vf = bf16x8_to_f16((uint32_t)x[0][0], (uint32_t)x[0][1], (uint32_t)x[1][0],
-                                         (uint32_t)x[1][1]);
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg)
             o[mt][rg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                vf, __builtin_bit_cast(f16x8, pf[2 * ks + rg]), o[mt][rg], 0, 0, 0);
-        }
+                vh[4 * ks + mt], __builtin_bit_cast(f16x8, pf[2 * ks + rg]), o[mt][rg], 0, 0, 0);
     };
+    // Codes and row addresses of tile i + 3 from its selection slots (copied during iteration
+    // i - 2). Every PV wave computes them (lanes l and l + 32 alike) and stores the same values,
+    // so the stores need no branch and the arithmetic can interleave with the MFMAs.
+    const int kl32 = lane & (TK - 1);
+    auto codes = [&](int i, int raw) {
+      const int kk = (int)k0 + (i + 3) * TK + kl32;
+      const int c2 = key_code_sel(kc, kk, sel_dma ? raw : 0);
+      const int slot2 = (i + 3) % kPpBuf;
+      s_code[slot2][kl32] = c2;
+      s_addr[slot2][kl32] = key_addr_sel(rbases, c2);
+    };
+    // Iteration i: PV of tile i - 1 (its V^T converted at the end of iteration i - 1), while the
+    // V^T of tile i and the codes of tile i + 3 are fetched. The first iteration's PV adds zero;
+    // the last iteration's reads and codes (of tiles past the end) go unused.
+    f16x8 vh[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vh[j] = f16x8{};
     for (int i = 0; i <= nt; ++i) {
       if (i < nt && !have_ref) {   // the QK waves' reference barrier, at the first tile with a key
-        if (__any(s_code[i % kPpBuf][lane & (TK - 1)] >= 0)) {
+        if (__any(s_code[i % kPpBuf][kl32] >= 0)) {
           lds_barrier();
           have_ref = true;
         }
       }
-      // Selection slots of tile i + 3 (copied during iteration i - 2), read before the PV work so
-      // that their latency is hidden behind it.
-      const int raw2 = (w < 6 && sel_dma) ? s_sel[(i + 3) % 3][lane] : 0;
-      if (i >= 1) pv(lds_addr(s_p[(i - 1) & 1]));
-      if (i < nt) read_v(lds_addr(kv[i % kPpBuf]));   // tile i, for the next iteration
-      // Codes of tile i + 3, split over two waves: wave 4 the codes and flags, wave 5 the row
-      // addresses.
-      if (w == 5 && i < nt) {
-        const int kk2 = (int)k0 + (i + 3) * TK + lane;
-        const int c2 = lane < TK ? key_code32(kc, kk2, raw2) : -1;
-        if (lane < TK) s_addr[(i + 3) % kPpBuf][lane] = key_addr(rbases, c2);
-      }
-      if (w == 4 && i < nt) {
-        const int kk2 = (int)k0 + (i + 3) * TK + lane;
-        const int c2 = lane < TK ? key_code32(kc, kk2, raw2) : -1;
-        const int slot2 = (i + 3) % kPpBuf;
-        if (lane < TK) s_code[slot2][lane] = c2;
+      const int raw = s_sel[(i + 3) % 3][kl32];   // issued first: waited for by count
+      v4i pf[4];
+      read_p(s_p[(i + 1) & 1], pf);
+      v2i vr[16];
+      read_v(kv[i % kPpBuf], vr);
+      codes(i, raw);
+      const bool first = i == 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf[j] = first ? v4i{} : pf[j];
+      pv(vh, pf);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const v2i* x = &vr[2 * j];
+        vh[j] = bf16x8_to_f16((uint32_t)x[0][0], (uint32_t)x[0][1], (uint32_t)x[1][0],
+                              (uint32_t)x[1][1]);
       }
       lds_barrier();
     }
