@@ -62,6 +62,29 @@ __device__ __forceinline__ KeyAddr key_addr_sel(const RowBases& rb, int code) {
   return KeyAddr{code < 0 ? z : lat, code < 0 ? z : rope};
 }
 
+// The DMA of one tile's rows (the layout of dma_tile in attend_tile.h), share wv of 4, from
+// row addresses held in registers: lane l (and l + 32) holds those of key l.
+__device__ __forceinline__ void dma_tile_regs(const KeyAddr& ka, char* buf, int wv) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t off0 = 16 * (lane ^ swz(wv)), off1 = 16 * (lane ^ swz(wv + 4));
+  const uint32_t lat_lo = (uint32_t)(uintptr_t)ka.lat, lat_hi = (uint32_t)((uintptr_t)ka.lat >> 32);
+#pragma unroll
+  for (int j = 0; j < kPpTK / 4; ++j) {
+    const int r = 4 * j + wv;
+    const uint64_t base = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lat_lo, r) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lat_hi, r) << 32);
+    const char* src = reinterpret_cast<const char*>(base) + ((j & 1) ? off1 : off0);
+    __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + 1024 * r), 16, 0, 0);
+  }
+  // RoPE rows 8 wv .. 8 wv + 7, eight lanes per row.
+  const int r = 8 * wv + (lane >> 3);
+  const uint32_t rp_lo = (uint32_t)__shfl((int)(uint32_t)(uintptr_t)ka.rope, r);
+  const uint32_t rp_hi = (uint32_t)__shfl((int)(uint32_t)((uintptr_t)ka.rope >> 32), r);
+  const char* src = reinterpret_cast<const char*>((uint64_t)rp_lo | ((uint64_t)rp_hi << 32)) +
+                    16 * ((lane & 7) ^ swz(r));
+  __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + kPpTK * 1024 + 1024 * wv), 16, 0, 0);
+}
+
 // Q^T fragments of a QK wave for mfma_f32_16x16x32_bf16: q[2 s + h] = Q[head 16 h + (lane & 15)]
 // [dims 32 s + 8 (lane >> 4) + (0..7)] of the row group. The 32 latent fragments go straight into
 // accumulation registers, in one block that waits for its loads.
@@ -278,24 +301,36 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     for (int j = 0; j < 4; ++j) lds_barrier();
   } else {
     // ================================ PV waves ================================
-    if (w == 4) {
+    // Prologue, PV side: every PV wave computes the codes and row addresses of tiles 0-2 (the
+    // three selection loads issued together) and stores them (the same values from every wave),
+    // then issues its quarter of the DMA of tiles 0 and 1 from those registers; wave 4 also copies
+    // the selection slots of tiles 3 and 4.
+    {
+      const int kl32 = lane & (TK - 1);
+      int raw[3];
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        const int c = lane < TK ? key_code(a, kl, k0 + j * TK + lane, ke) : -1;
-        if (lane < TK) {
-          s_code[j][lane] = c;
-          s_addr[j][lane] = key_addr(rbases, c);
-        }
+        const int kk = (int)k0 + j * TK + kl32;
+        const int32_t* src = (sel_dma && kk < kc.ke && kk < kc.n_sel)
+                                 ? kl.sel + kk
+                                 : reinterpret_cast<const int32_t*>(kZeroRow);
+        raw[j] = *src;
       }
-      if (sel_dma) {
+      KeyAddr ad[2];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = key_code_sel(kc, (int)k0 + j * TK + kl32, raw[j]);
+        const KeyAddr ka = key_addr_sel(rbases, c);
+        s_code[j][kl32] = c;
+        s_addr[j][kl32] = ka;
+        if (j < 2) ad[j] = ka;
+      }
+      if (w == 4 && sel_dma) {
         dma_sel<TK>(kl, k0 + 3 * TK, ke, s_sel[0]);
         dma_sel<TK>(kl, k0 + 4 * TK, ke, s_sel[1]);
       }
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
-        dma_tile<TK>(s_addr[0], kv[0], wv);
-        dma_tile<TK>(s_addr[1], kv[1], wv);
-      }
+      dma_tile_regs(ad[0], kv[0], w - 4);
+      dma_tile_regs(ad[1], kv[1], w - 4);
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
@@ -449,19 +484,30 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       }
       lds_barrier();                  // rows staged (the QK waves take part in every barrier)
       if (plan.n_split == 1) {
+        // 16-byte chunk k of head row h: thread pt takes k = pt & 127 of rows pt / 128 + 2 u.
         constexpr int kCh = 512 * 4 / 16;
-        for (int ci = pt; ci < 32 * kCh; ci += 256) {
-          const int h = ci / kCh, k = ci - h * kCh;
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kStageLd<float> + 16 * k);
-          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.out + (row0 + h) * kDC) + 16 * k) = v;
-        }
+        constexpr int kU = 32 * kCh / 256;
+        const int k = pt & (kCh - 1), h0 = pt / kCh;
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          v[u] = *reinterpret_cast<const uint4*>(stage + (h0 + 2 * u) * kStageLd<float> + 16 * k);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.out + (row0 + h0 + 2 * u) * kDC) +
+                                    16 * k) = v[u];
       } else {
         constexpr int kCh = 512 * 2 / 16;
-        for (int ci = pt; ci < 32 * kCh; ci += 256) {
-          const int h = ci / kCh, k = ci - h * kCh;
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kStageLd<_Float16> + 16 * k);
-          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(plan.ws_o + (row0 + h) * kDC) + 16 * k) = v;
-        }
+        constexpr int kU = 32 * kCh / 256;
+        const int k = pt & (kCh - 1), h0 = pt / kCh;
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          v[u] = *reinterpret_cast<const uint4*>(stage + (h0 + 4 * u) * kStageLd<_Float16> + 16 * k);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(plan.ws_o + (row0 + h0 + 4 * u) * kDC) +
+                                    16 * k) = v[u];
       }
       lds_barrier();                  // rows written, staging area free
     }
