@@ -152,6 +152,17 @@ def test_csa_prefill_64_heads_key_splits(sharp):
     parity.check_csa(wl, host, step)
 
 
+@pytest.mark.parametrize("sharp", [False, True])
+def test_csa_prefill_192_heads(sharp):
+    # Three 64-head groups per query (head groups of one query in different workgroups), many
+    # queries; sampled queries across the whole range, the first and the last ones included.
+    wl = SMALL["C2"].replace(H=192, T=1203, nq=1203, k=160, window=64)
+    print(f"[parity] csa prefill 192 heads sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, 22)
+    qsel = np.unique(np.concatenate([np.arange(0, 1203, 37), np.arange(1195, 1203)]))
+    parity.check_csa(wl, host, step, qsel=qsel)
+
+
 def test_hca_prefill_128_heads_many_queries():
     # >= 512 queries of 128 heads: four 32-head groups share every staged key tile.
     wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=640, H=128)
