@@ -183,8 +183,9 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   const int rg = w;                     // QK: row group
   const int hi = lane >> 5;
   const int per_q = plan.head_groups * plan.n_split;
-  const int qi = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qi * per_q;
+  const int item = xcd_item();
+  const int qi = item / per_q;
+  const int rem = item - qi * per_q;
   const int hgrp = rem / plan.n_split;
   const int split = rem - hgrp * plan.n_split;
   const int hbase = hgrp * R;
@@ -399,7 +400,7 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
       for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][r][i]);
   if (__any(overflow)) atomicOr(&s_flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
+  if (threadIdx.x == 0) plan.flags[item] = s_flag;
 
   // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
   // row group at a time, staged in the (now idle) tile buffers.

@@ -179,8 +179,9 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   const int ks = w / HGW;
   const int hi = lane >> 5;                       // lane half
   const int per_q = plan.head_groups * plan.n_split;
-  const int qi = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qi * per_q;
+  const int item = xcd_item();
+  const int qi = item / per_q;
+  const int rem = item - qi * per_q;
   const int hgrp = rem / plan.n_split;
   const int split = rem - hgrp * plan.n_split;
   const int h0 = (hgrp * HGW + hgw) * 32;
@@ -337,7 +338,7 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) plan.flags[blockIdx.x] = s_flag;
+  if (threadIdx.x == 0) plan.flags[item] = s_flag;
   if (ks != 0) return;
 
   // Output rows: lane owns head `head`, dims 32 mt + 8 j + 4 hi + [0, 4).

@@ -19,6 +19,17 @@ struct AttnPlan {
   int* flags;         // [nq][head_groups][n_split] 1 = some head left the range of P
 };
 
+// The work item of this workgroup. Workgroups go to the 8 XCDs in turn (workgroup b to XCD
+// b mod 8); this mapping gives each XCD a contiguous range of items, so that the key splits and
+// head groups of one query, and neighbouring queries, share that XCD's L2. The last
+// gridDim.x mod 8 workgroups keep their own index.
+__device__ __forceinline__ int xcd_item() {
+  const int b = blockIdx.x, n = gridDim.x;
+  const int n8 = n & ~7;
+  if (b >= n8) return b;
+  return (b & 7) * (n8 >> 3) + (b >> 3);
+}
+
 // Four values of a normalised partial output row (o / l in fp16; zeros when l == 0).
 __device__ __forceinline__ void store_partial4(_Float16* dst, float a, float b, float c, float d,
                                                float inv) {

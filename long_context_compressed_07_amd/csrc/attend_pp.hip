@@ -156,8 +156,9 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
   const int w = threadIdx.x >> 6;
   const int hi = lane >> 5;
   const int per_q = plan.head_groups * plan.n_split;
-  const int qi = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qi * per_q;
+  const int item = xcd_item();
+  const int qi = item / per_q;
+  const int rem = item - qi * per_q;
   const int hgrp = rem / plan.n_split;
   const int split = rem - hgrp * plan.n_split;
   const int hbase = hgrp * R;
@@ -439,7 +440,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
         for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][rg][i]);
     if (__any(overflow)) atomicOr(&s_flag, 1);
     lds_barrier();                    // epilogue barrier 1: sums, maxima and flag complete
-    if (threadIdx.x == 256) plan.flags[blockIdx.x] = s_flag;
+    if (threadIdx.x == 256) plan.flags[item] = s_flag;
     // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
     // row group at a time, staged in the (idle) tile buffers by the PV waves, written as rows.
     char* stage = &kv[0][0];
