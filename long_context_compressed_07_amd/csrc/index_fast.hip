@@ -50,7 +50,9 @@ __global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
   __shared__ float s_w[kQ * 8];
   __shared__ int64_t s_nv[kQ];
   __shared__ int s_uniform;
-  const int q0 = blockIdx.x * kQ;
+  // The last query blocks first: under causality they see the most entries, and starting them
+  // first shortens the tail of the grid.
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kQ;
   const int nqw = a.Q.nq - q0 < kQ ? a.Q.nq - q0 : kQ;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, hi = lane >> 5;
@@ -90,17 +92,28 @@ __global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
     }
   }
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_i) + b * a.N * 64;
-  for (int64_t e0 = 0; e0 < nmax; e0 += kE) {
-    // Stage entries [e0, e0 + 128): 128 rows x 128 bytes, 16 bytes per thread-task.
+  // Entries [e0, e0 + 128): 128 rows x 128 bytes, 16 bytes per thread-task; the next block's
+  // loads are issued before the current block's MFMAs, so their latency hides behind them.
+  uint4 pre[4];
+  auto load_block = [&](int64_t e0) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = tid + 256 * it;
       const int r = t >> 3, c = t & 7;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (e0 + r < a.N) v = *reinterpret_cast<const uint4*>(kbase + (e0 + r) * 64 + 8 * c);
-      *reinterpret_cast<uint4*>(s_k + r * kRowK + 8 * c) = v;
+      pre[it] = e0 + r < a.N ? *reinterpret_cast<const uint4*>(kbase + (e0 + r) * 64 + 8 * c)
+                             : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  load_block(0);
+  for (int64_t e0 = 0; e0 < nmax; e0 += kE) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int t = tid + 256 * it;
+      const int r = t >> 3, c = t & 7;
+      *reinterpret_cast<uint4*>(s_k + r * kRowK + 8 * c) = pre[it];
     }
     __syncthreads();
+    if (e0 + kE < nmax) load_block(e0 + kE);
 #pragma unroll
     for (int ct = 0; ct < kE / 32; ++ct) {
       if (e0 + 32 * ct >= nmax) break;
@@ -120,8 +133,8 @@ __global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
         float part[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const float* wq = s_w + (8 * w + 4 * rt + qq) * 8 + 4 * hi;
           float p = 0.f;
+          const float* wq = s_w + (8 * w + 4 * rt + qq) * 8 + 4 * hi;
 #pragma unroll
           for (int j = 0; j < 4; ++j) p = fmaf(wq[j], fmaxf(acc[4 * qq + j], 0.f), p);
           part[qq] = p + __shfl_xor(p, 32);
