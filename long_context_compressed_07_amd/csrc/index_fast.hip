@@ -5,8 +5,8 @@
 //
 // index_bf16_mfma_kernel (many queries, bf16): a workgroup takes 32 consecutive queries of one
 // sequence; rows of the contraction are (query, head) pairs, 4 queries x 8 heads per 32-row
-// MFMA tile, columns are entries. Per 32x32 output tile a lane holds 4 heads of 4 queries for one
-// entry, so the ReLU-weighted head sum is 4 in-register terms plus one exchange with lane ^ 32.
+// MFMA tile, columns are entries. The rows are ordered so that in the 32x32 output tile a lane
+// holds all 8 heads of two queries for one entry: the ReLU-weighted head sum stays in registers.
 // Entry blocks of 128 rows are staged once in LDS and read as B fragments by all four waves. Only
 // visible entries (j < n_vis of each query) are computed and written.
 //
@@ -45,7 +45,8 @@ __device__ void index_one_query_generic(const IndexArgs& a, int qi) {
   }
 }
 
-__global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+index_bf16_mfma_kernel(IndexArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kE * kRowK];
   __shared__ float s_w[kQ * 8];
   __shared__ int64_t s_nv[kQ];
@@ -75,13 +76,15 @@ __global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
   int64_t nmax = 0;
   for (int i = 0; i < kQ; ++i) nmax = s_nv[i] > nmax ? s_nv[i] : nmax;
 
-  // A fragments: wave w owns queries q0 + 8 w + [0, 8) as two 32-row tiles.
+  // A fragments: wave w owns queries q0 + 8 w + [0, 8) as two 32-row tiles. Row r of a tile
+  // holds head 4 ((r >> 3) & 1) + (r & 3) of query 2 ((r >> 2) & 1) + (r >> 4), so that in the
+  // 32x32 output layout each lane holds all 8 heads of two queries for its entry.
   bf16x8 af[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = lane & 31;
-    const int qq = 8 * w + 4 * rt + row / 8;
-    const int h = row & 7;
+    const int qq = 8 * w + 4 * rt + 2 * ((row >> 2) & 1) + (row >> 4);
+    const int h = 4 * ((row >> 3) & 1) + (row & 3);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -129,22 +132,15 @@ __global__ void __launch_bounds__(256) index_bf16_mfma_kernel(IndexArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][s], bfr[s], acc, 0, 0, 0);
-        // acc[4 qq + j] = head 4 hi + j of query 8 w + 4 rt + qq, entry `ent`.
-        float part[4];
+        // acc[8 u + e] = head e of query 8 w + 4 rt + 2 hi + u (u = 0, 1), entry `ent`.
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
+        for (int u = 0; u < 2; ++u) {
+          const int ql = 8 * w + 4 * rt + 2 * hi + u;
+          const float* wq = s_w + ql * 8;
           float p = 0.f;
-          const float* wq = s_w + (8 * w + 4 * rt + qq) * 8 + 4 * hi;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p = fmaf(wq[j], fmaxf(acc[4 * qq + j], 0.f), p);
-          part[qq] = p + __shfl_xor(p, 32);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int qq = 2 * hi + k2;
-          const int ql = 8 * w + 4 * rt + qq;
-          if (ql < nqw && ent < s_nv[ql])
-            a.scores[(int64_t)(q0 + ql) * a.ld_scores + ent] = part[qq];
+          for (int e = 0; e < 8; ++e) p = fmaf(wq[e], fmaxf(acc[8 * u + e], 0.f), p);
+          if (ql < nqw && ent < s_nv[ql]) a.scores[(int64_t)(q0 + ql) * a.ld_scores + ent] = p;
         }
       }
     }
