@@ -436,14 +436,15 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
 // workgroups (n_split), merged by combine_kernel.
 enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 
-// CSA_ATTEND_PP=0 selects the single-role 64-head kernel instead of the two-role one (for
-// comparisons).
+// CSA_ATTEND_PP=0 selects the single-role bf16 kernels (64 or 128 heads per workgroup) instead of
+// the two-role 64-head one (for comparisons and their tests).
 static bool pp_disabled() {
   const char* e = std::getenv("CSA_ATTEND_PP");
   return e != nullptr && e[0] == '0';
 }
 
-MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
+// two_role: bf16 heads in 64-head workgroups with the two wave roles (attend_pp.hip).
+MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind, bool two_role) {
   MfmaPlan p{};
   const int groups32 = H / 32;
   const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
@@ -454,8 +455,12 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
   };
   if (kind == kPlanBf16 && groups32 % 2 == 0) {
     p.bf16_dma = 1;
-    p.rg = groups32 % 4 == 0 ? 4 : 2;
-    p.pp = p.rg == 2 && !pp_disabled();
+    // 64-head workgroups with the two wave roles (attend_pp.hip) for every even number of 32-head
+    // groups (measured on 128 heads: 8.3 vs 9.2 ms for the HCA prefill, although each key tile is
+    // loaded once per 64 heads instead of once per 128); CSA_ATTEND_PP=0 selects the 4-wave kernel
+    // (128 heads per workgroup where they divide).
+    p.pp = two_role;
+    p.rg = (!p.pp && groups32 % 4 == 0) ? 4 : 2;
     p.head_groups = groups32 / p.rg;
     p.n_split = splits_for(p.head_groups, cap);
     return p;
@@ -517,11 +522,12 @@ static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
   // The dtypes are not part of the workspace query: cover every plan kind.
   size_t part = 0, flags = 0;
-  for (int kind = 0; kind < 3; ++kind) {
-    const MfmaPlan p = make_plan(nq, H, max_keys, kind);
-    part = std::max(part, plan_partial_bytes(p, nq, H));
-    flags = std::max(flags, plan_flag_bytes(p, nq));
-  }
+  for (int kind = 0; kind < 3; ++kind)
+    for (int two_role = 0; two_role < 2; ++two_role) {   // either choice of the bf16 kernel
+      const MfmaPlan p = make_plan(nq, H, max_keys, kind, two_role != 0);
+      part = std::max(part, plan_partial_bytes(p, nq, H));
+      flags = std::max(flags, plan_flag_bytes(p, nq));
+    }
   return part + flags;
 }
 
@@ -582,7 +588,7 @@ void timing_stop(int slot, hipStream_t s) {
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
+  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a), !pp_disabled());
   if (p.n_split > 1) {
     p.ws_o = static_cast<_Float16*>(a.ws);
     p.ws_ml = reinterpret_cast<float*>(p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC);

@@ -134,12 +134,26 @@ def test_deterministic(cfg):
 
 @pytest.mark.parametrize("sharp", [False, True])
 def test_csa_prefill_128_heads(sharp):
-    # 128 heads per query: the bf16 kernel's four-row-group form (three tile buffers, selection
-    # indices copied three tiles ahead).
+    # 128 heads per query: two 64-head workgroups of the two-role kernel.
     wl = SMALL["C2"].replace(H=128, T=901, nq=901, k=160)
     print(f"[parity] csa prefill 128 heads sharp={sharp}", flush=True)
     host, step = _run(wl, sharp, 20)
     parity.check_csa(wl, host, step)
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_single_role_bf16_kernels(H, monkeypatch):
+    # CSA_ATTEND_PP=0: the 4-wave bf16 kernel, 64 heads (two row groups, 64-key tiles) or 128
+    # heads (four row groups, three tile buffers, selection copied three tiles ahead).
+    monkeypatch.setenv("CSA_ATTEND_PP", "0")
+    wl = SMALL["C2"].replace(H=H, T=901, nq=901, k=160)
+    print(f"[parity] csa prefill single-role kernel H={H}", flush=True)
+    host, step = _run(wl, True, 23)
+    parity.check_csa(wl, host, step)
+    wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=300, H=H)
+    print(f"[parity] hca prefill single-role kernel H={H}", flush=True)
+    host, step = _run(wl, True, 24)
+    parity.check_hca(wl, host, step)
 
 
 @pytest.mark.parametrize("sharp", [False, True])
