@@ -139,6 +139,54 @@ __device__ __forceinline__ void load_q16(const uint16_t* q0, const uint16_t* q1,
   }
 }
 
+// The Q^T fragments of load_q16 from LDS, where the workgroup's DMA has put fragment f of this
+// row group at base + 1 KB f (lane l's 16 bytes at 16 l): one block that waits for its reads,
+// the 32 latent fragments into accumulation registers (at most 15 reads outstanding).
+__device__ __forceinline__ void load_q16_lds(int base, v4i (&q)[36]) {
+  asm volatile(
+      "ds_read_b128 %0, %32 offset:0\n"
+      "ds_read_b128 %1, %32 offset:1024\n"
+      "ds_read_b128 %2, %32 offset:2048\n"
+      "ds_read_b128 %3, %32 offset:3072\n"
+      "ds_read_b128 %4, %32 offset:4096\n"
+      "ds_read_b128 %5, %32 offset:5120\n"
+      "ds_read_b128 %6, %32 offset:6144\n"
+      "ds_read_b128 %7, %32 offset:7168\n"
+      "ds_read_b128 %8, %32 offset:8192\n"
+      "ds_read_b128 %9, %32 offset:9216\n"
+      "ds_read_b128 %10, %32 offset:10240\n"
+      "ds_read_b128 %11, %32 offset:11264\n"
+      "ds_read_b128 %12, %32 offset:12288\n"
+      "ds_read_b128 %13, %32 offset:13312\n"
+      "ds_read_b128 %14, %32 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "ds_read_b128 %15, %32 offset:15360\n"
+      "ds_read_b128 %16, %32 offset:16384\n"
+      "ds_read_b128 %17, %32 offset:17408\n"
+      "ds_read_b128 %18, %32 offset:18432\n"
+      "ds_read_b128 %19, %32 offset:19456\n"
+      "ds_read_b128 %20, %32 offset:20480\n"
+      "ds_read_b128 %21, %32 offset:21504\n"
+      "ds_read_b128 %22, %32 offset:22528\n"
+      "ds_read_b128 %23, %32 offset:23552\n"
+      "ds_read_b128 %24, %32 offset:24576\n"
+      "ds_read_b128 %25, %32 offset:25600\n"
+      "ds_read_b128 %26, %32 offset:26624\n"
+      "ds_read_b128 %27, %32 offset:27648\n"
+      "ds_read_b128 %28, %32 offset:28672\n"
+      "ds_read_b128 %29, %32 offset:29696\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "ds_read_b128 %30, %32 offset:30720\n"
+      "ds_read_b128 %31, %32 offset:31744\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]),
+        "=a"(q[7]), "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]),
+        "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]),
+        "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]),
+        "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
+      : "v"(base));
+}
+
 __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int TK = kPpTK;
   constexpr int R = kPpR;
@@ -174,17 +222,36 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
   const int nt = ke > k0 ? (int)((ke - k0 + TK - 1) / TK) : 0;
   const float cscale = a.sm_scale * kLog2e;
 
-  // Prologue, in parallel: the QK waves load their queries while wave 4 computes the codes of
-  // tiles 0-2, copies the selection slots of tiles 3 and 4 and issues (and waits for) the DMA of
-  // tiles 0 and 1, all rows.
+  // Prologue, in parallel: every wave copies its share of the queries by DMA, while the PV
+  // waves compute the codes of tiles 0-2, copy the selection slots of tiles 3 and 4 and issue the
+  // DMA of tiles 0 and 1. The queries of the 64 heads go to tile buffers 2 and 3 (idle until the
+  // first tile's block) in the QK waves' fragment order: fragment f of row group rg at
+  // (36 rg + f) KB, lane l's 16 bytes at 16 l; each of the 8 waves copies 9 of the 72 fragments.
+  {
+    const int c = lane & 15, g = lane >> 4;
+    const char* qblk = static_cast<const char*>(a.q) + ((int64_t)qi * a.H + hbase) * kD * 2;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int F = 9 * w + i;
+      const int rgF = F / 36, f = F - 36 * rgF;
+      const char* src = qblk + ((32 * rgF + 16 * (f & 1) + c) * kD + 32 * (f >> 1) + 8 * g) * 2;
+      __builtin_amdgcn_global_load_lds(src, (lds_char*)(&kv[2][0] + 1024 * F), 16, 0, 0);
+    }
+  }
   if (w < 4) {
     // ================================ QK waves ================================
     const int rg = w & 1, kh = w >> 1;
     const int c = lane & 15, g = lane >> 4;
     v4i qb[36];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + 32 * rg + c) * kD;
-    load_q16(qrow, qrow + 16 * kD, qb);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the queries
+    __syncthreads();                  // all queries and the prologue's tiles in LDS
+    {
+      const char* qf = &kv[2][0] + 36 * 1024 * rg + 16 * lane;
+      load_q16_lds(lds_addr(qf), qb);
+#pragma unroll
+      for (int f = 32; f < 36; ++f) qb[f] = *reinterpret_cast<const v4i*>(qf + 1024 * f);
+    }
+    __syncthreads();                  // queries read: buffers 2 and 3 free for the tile DMA
     float m_ref[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
     bool have_ref = false;
@@ -335,6 +402,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
+    __syncthreads();                  // the QK waves have read their queries
     const int p = w - 4;
     floatx16 o[4][2];
 #pragma unroll
