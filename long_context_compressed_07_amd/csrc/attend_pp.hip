@@ -1,6 +1,6 @@
 // MFMA attention for bf16 caches with 64 heads per workgroup (csa_attend / hca_attend; 512
-// latent + 64 RoPE dims per row, bf16 queries): the 64-head prefill path, with the work of each
-// key tile split between two wave roles that share every SIMD.
+// latent + 64 RoPE dims per row, bf16 queries, H a multiple of 64), with the work of each key
+// tile split between two wave roles that share every SIMD.
 //
 // Method: deepseek.csdn.net "一文搞懂 DeepSeek" V4 改进一 (CSA: selected compressed rows plus the
 // raw window, MQA with one KV shared by every head; HCA: dense over the m'-compressed rows) and the
@@ -16,11 +16,14 @@
 //     tile i + 5 from inside that instruction block, apply the softmax with the fixed per-head
 //     reference, and write P (fp16) for the PV waves;
 //   PV waves 4-7 (value dims [128 p, 128 p + 128), p = w - 4) accumulate
-//     O^T[128 dims x 64 heads] += V^T . P^T for tile i - 1 with 16 mfma_f32_32x32x16_f16, V^T
-//     read transposed (ds_read_b64_tr_b16) and converted to fp16 in registers; waves 4 and 5
-//     also compute the key codes and row addresses of tile i + 3.
+//     O^T[128 dims x 64 heads] += V^T . P^T for tile i - 1 with 16 mfma_f32_32x32x16_f16, the
+//     P^T and the transposed V^T (ds_read_b64_tr_b16) of the next step read ahead of those
+//     MFMAs, V^T converted to fp16 in registers; every PV wave also computes the key codes and
+//     row addresses of tile i + 3 (the same values), in between.
 // One barrier closes each iteration. Each SIMD holds one wave of each role, so while one runs its
-// softmax, conversions or LDS traffic the other keeps the matrix unit busy.
+// softmax, conversions or LDS traffic the other keeps the matrix unit busy. The prologue copies
+// the 64 heads' queries once by DMA (into the two buffers idle until the first tile) and the QK
+// waves read their fragments from there.
 //
 // Numerics as in attend_bf16.hip: bf16 products exact in fp32, V converted to fp16 (exact in
 // fp16's normal range), P fp16, fixed reference maximum from the first tile that holds a key, and a
@@ -421,7 +424,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     // V^T of a tile (16 half-fragments: k-step ks, dim tile mt, rows +0 / +8) and the P^T
     // fragments of the tile before it are read at the start of an iteration, ahead of that
     // iteration's MFMAs (which use the V^T read one iteration earlier), so the reads overlap the
-    // matrix work. The two V^T register sets alternate between iterations (loop unrolled by two).
+    // matrix work.
     auto read_v = [&](const char* buf, v2i (&vr)[16]) {
       const char* be = buf + v_even;
       const char* bo = buf + v_odd;
