@@ -234,3 +234,34 @@ def test_topk_exact_with_ties_and_long_rows(N, k):
         nv = orc.n_visible(int(pos[q]), m, N)
         want, _ = orc.topk(s64[q], nv, k)
         assert (got[q] == want).all(), (q, nv)
+
+
+@pytest.mark.parametrize("N,k", [(8192, 1024), (30000, 1024), (3000, 257), (6000, 1)])
+def test_topk_exact_continuous_and_extreme_scores(N, k):
+    # Continuous scores take the selection's equal-width score bins; one score far above the
+    # rest crowds the others into a few bins and infinite or tiny-range scores leave no usable
+    # bin width (both take the radix path); the results are bit-exact against the oracle.
+    from oracle import csa_oracle as orc
+    rng = np.random.default_rng(7 * N + k)
+    nq, m = 6, 4
+    sc = rng.standard_normal((nq, N)).astype(np.float32)
+    sc[1, N // 3] = 1e30
+    sc[2, ::97] = np.inf
+    sc[2, 5::89] = -np.inf
+    sc[3] *= np.float32(1e-38)
+    sc[4] = 0.5
+    sc[4, N // 2] = 0.75
+    sc[5] = sc[5] * 1e-3 - 40.0
+    pos = np.full(nq, 4 * N + 3, dtype=np.int64)
+    seq = np.zeros(nq, dtype=np.int32)
+    scores = torch.tensor(sc, dtype=torch.float32, device="cuda")
+    idx = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+    lib.csa_topk(torch.tensor(seq, device="cuda"), torch.tensor(pos, device="cuda"), scores,
+                 idx, N, m, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    s64 = scores.cpu().numpy().astype(np.float64)
+    for q in range(nq):
+        with np.errstate(invalid="ignore"):   # the oracle's score gap of two infinite scores
+            want, _ = orc.topk(s64[q], orc.n_visible(int(pos[q]), m, N), k)
+        assert (got[q] == want).all(), q
