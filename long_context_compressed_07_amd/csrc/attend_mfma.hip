@@ -20,9 +20,10 @@
 //                                                 later tiles may reach 2^15 above it (fp16 P
 //                                                 range), so the accumulators are never rescaled
 //                                                 inside the loop. A head that would exceed the
-//                                                 range flags its workgroup, and fixup_kernel
-//                                                 recomputes the flagged queries with the fp32
-//                                                 reference code.
+//                                                 range flags its workgroup, and the heads it
+//                                                 computed are recomputed with the fp32
+//                                                 reference code (combine_kernel for key-split
+//                                                 plans, fixup_kernel: the whole query).
 //   O^T[512 x 32 heads] += V^T . P^T              32 x mfma, V^T fragments read transposed from
 //                                                 the same LDS rows (ds_read_tr16_b64), P^T is
 //                                                 the softmax output already in registers
@@ -373,55 +374,96 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
   }
 }
 
-// Log-sum-exp merge of n_split partials: one block per (query, head), one thread per 8 dims.
-// Partial s holds o_s / l_s: out = sum_s (l_s 2^(m_s - mx)) (o_s / l_s) / sum_s l_s 2^(m_s - mx).
-constexpr int kCombineThreads = kDC / 8;
+// Log-sum-exp merge of n_split partials, fused with the overflow fixup of split plans: one block of
+// four waves per (query, four heads), wave w merging head h0 + w with one lane per 8 dims. Partial
+// s holds o_s / l_s: out = sum_s (l_s 2^(m_s - mx)) (o_s / l_s) / sum_s l_s 2^(m_s - mx), taken in
+// batches of 8 splits whose loads are all issued before use, with a running maximum. When a
+// workgroup that computed these heads (their head group, any key split) flagged a head whose
+// logits left the fp16 range of P, the block recomputes the four heads with the fp32 reference
+// code instead.
+constexpr int kCombHeads = kGenThreads / kWave;
+constexpr int kCombBatch = 8;
 
-__global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttendArgs a, MfmaPlan plan) {
+__global__ void __launch_bounds__(kGenThreads) combine_kernel(AttendArgs a, MfmaPlan plan) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  const int qi = blockIdx.x / a.H;
-  const int head = blockIdx.x - qi * a.H;
+  __shared__ float smem[generic_smem_bytes(kD) / sizeof(float)];
+  const int per_q = a.H / kCombHeads;
+  const int qi = blockIdx.x / per_q;
+  const int h0 = (blockIdx.x - qi * per_q) * kCombHeads;
+  const int hgrp = h0 / (a.H / plan.head_groups);
+  const int t = threadIdx.x;
+  int flag = 0;
+  for (int s = t; s < plan.n_split; s += kGenThreads)
+    flag |= plan.flags[((int64_t)qi * plan.head_groups + hgrp) * plan.n_split + s];
+  if (__syncthreads_or(flag)) {
+    for (int h = h0; h < h0 + kCombHeads; ++h) attend_generic_one(a, qi, h, smem);
+    return;
+  }
+  const int head = h0 + t / kWave;
+  const int d0 = (t & (kWave - 1)) * 8;
   const int64_t p0 = (int64_t)qi * plan.n_split * a.H + head;   // partial index of split 0
   const int64_t ps = a.H;                                        // stride between splits
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < plan.n_split; ++s) mx = fmaxf(mx, plan.ws_ml[(p0 + s * ps) * 2]);
-  const int d0 = threadIdx.x * 8;
-  float lsum = 0.f;
+  float mx = -INFINITY, lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < plan.n_split; ++s) {
-    const int64_t pidx = p0 + s * ps;
-    const float2 ml = *reinterpret_cast<const float2*>(plan.ws_ml + pidx * 2);
-    const h8 v = *reinterpret_cast<const h8*>(plan.ws_o + pidx * kDC + d0);
-    const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mx) * ml.y;
-    lsum += wgt;
+  for (int s0 = 0; s0 < plan.n_split; s0 += kCombBatch) {
+    float2 ml[kCombBatch];
+    h8 v[kCombBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[j];
+    for (int u = 0; u < kCombBatch; ++u) {
+      const bool in = s0 + u < plan.n_split;
+      const int64_t pidx = p0 + (int64_t)(in ? s0 + u : s0) * ps;
+      ml[u] = *reinterpret_cast<const float2*>(plan.ws_ml + pidx * 2);
+      v[u] = *reinterpret_cast<const h8*>(plan.ws_o + pidx * kDC + d0);
+      if (!in) ml[u].x = -INFINITY;
+    }
+    float nm = mx;
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) nm = fmaxf(nm, ml[u].x);
+    const float r = mx == -INFINITY ? 0.f : exp2f(mx - nm);
+    lsum *= r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= r;
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+      const float wgt = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - nm) * ml[u].y;
+      lsum += wgt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[u][j];
+    }
+    mx = nm;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   float* dst = a.out + ((int64_t)qi * a.H + head) * kDC + d0;
   *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse != nullptr && threadIdx.x == 0)
+  if (a.lse != nullptr && d0 == 0)
     a.lse[(int64_t)qi * a.H + head] =
         lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
-// Recompute, with the fp32 reference code, every query one of whose workgroups flagged a head
-// whose logits left the fp16 range of P. Nearly always a no-op scan of the flags.
+// Plans without key splits: recompute, with the fp32 reference code, every query one of whose
+// workgroups flagged a head whose logits left the fp16 range of P. Nearly always a no-op: block b
+// owns queries b + gridDim.x j, each thread checks one of them at a time, and the block recomputes
+// the flagged ones.
 __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPlan plan) {
   __shared__ float smem[generic_smem_bytes(kD) / sizeof(float)];
-  __shared__ int s_any;
+  __shared__ int s_q[kGenThreads];
+  __shared__ int s_n;
   const int per_q = plan.head_groups * plan.n_split;
-  for (int qi = blockIdx.x; qi < a.Q.nq; qi += gridDim.x) {
-    if (threadIdx.x == 0) s_any = 0;
+  const int64_t stride = (int64_t)gridDim.x * kGenThreads;
+  for (int64_t q0 = blockIdx.x; q0 < a.Q.nq; q0 += stride) {
+    if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < per_q; i += kGenThreads)
-      if (plan.flags[(int64_t)qi * per_q + i]) s_any = 1;
+    const int64_t qi = q0 + (int64_t)threadIdx.x * gridDim.x;
+    if (qi < a.Q.nq) {
+      int any = 0;
+      for (int i = 0; i < per_q; ++i) any |= plan.flags[qi * per_q + i];
+      if (any) s_q[atomicAdd(&s_n, 1)] = (int)qi;
+    }
     __syncthreads();
-    if (s_any)
-      for (int h = 0; h < a.H; ++h) attend_generic_one(a, qi, h, smem);
+    const int n = s_n;
+    for (int j = 0; j < n; ++j)
+      for (int h = 0; h < a.H; ++h) attend_generic_one(a, s_q[j], h, smem);
     __syncthreads();
   }
 }
@@ -619,11 +661,10 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   if (e != hipSuccess) return e;
   if (timed) timing_stop(tslot, s);
   if (p.n_split > 1) {
-    combine_kernel<<<(unsigned)((int64_t)a.Q.nq * a.H), kCombineThreads, 0, s>>>(a, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    combine_kernel<<<(unsigned)((int64_t)a.Q.nq * (a.H / kCombHeads)), kGenThreads, 0, s>>>(a, p);
+  } else {
+    fixup_kernel<<<(unsigned)(a.Q.nq < 1024 ? a.Q.nq : 1024), kGenThreads, 0, s>>>(a, p);
   }
-  const int fx = a.Q.nq < 1024 ? a.Q.nq : 1024;
-  fixup_kernel<<<fx, kGenThreads, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

@@ -52,6 +52,28 @@ def test_csa_layer_small(cfg, sharp):
     print(stats)
 
 
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C4", "C5"])
+def test_fp16_overflow_recompute(cfg):
+    # Unit-scale queries with a softmax scale of 40: logits spread over tens of nats, so later key
+    # tiles exceed the fixed per-head reference of the first tile by far more than the fp16 range
+    # of P, nearly every head is flagged and recomputed by the fp32 reference code (unsplit
+    # plans: the fixup pass; key-split plans: inside the merge of the partials).
+    wl = SMALL[cfg]
+    print(f"[parity] overflow {cfg} {wl.name}", flush=True)
+    host = make_inputs(wl, _cfg_seed(cfg) + 5, sharp=True)
+    step = Step(wl, host, sm_scale=40.0)
+    step.run()
+    torch.cuda.synchronize()
+    stats = {}
+    if wl.kind == "hca_prefill":
+        parity.check_hca(wl, host, step, stats=stats)
+    else:
+        parity.check_csa(wl, host, step, stats=stats)
+        if wl.kind == "hybrid_decode":
+            parity.check_hca(wl, host, step, stats=stats)
+    print(stats)
+
+
 @pytest.mark.parametrize("sharp", [False, True])
 def test_hca_prefill_small(sharp):
     wl = SMALL["C3"]
