@@ -192,6 +192,20 @@ size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N)
 csa_status csa_kernel_timing_enable(int32_t cap);
 csa_status csa_kernel_timing_read(int32_t slot, double* ms, int32_t* n);
 
+/* ---------------------------------------------------------------------------------------------
+ * Instrumentation (not a step of the layer): the device's measured dense bf16 matrix-core rate,
+ * the denominator beside the datasheet peak when a kernel is rated against the MFMA roofline.
+ *   csa_peak_mfma_bf16(iters, sink, &tflops, stream): launches 768 blocks of 4 waves (3 per CU),
+ *     each wave running 4 independent chains of iters mfma_f32_32x32x16_bf16 on register operands
+ *     (no memory traffic in the loop), once short to warm up and once timed with a HIP event pair
+ *     on `stream`; waits for it and returns the rate in TFLOP/s. sink: device memory of at least
+ *     csa_peak_sink_floats() floats, owned by the caller, overwritten with one sum per wave.
+ *     Creates HIP events: call outside graph capture.
+ *   Errors: CSA_EINVAL for iters <= 0 or NULL sink / tflops; CSA_EHIP otherwise.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_peak_mfma_bf16(int32_t iters, float* sink, double* tflops, void* stream);
+int32_t csa_peak_sink_floats(void);
+
 /* Text of a status code; for CSA_EHIP the text of the last HIP error seen by this thread. */
 const char* csa_status_str(int32_t status);
 const char* csa_last_error(void);

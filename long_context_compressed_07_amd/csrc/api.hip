@@ -53,6 +53,13 @@ csa_status check_queries(const csa_queries_t* Q) {
 
 }  // namespace
 
+namespace csa {
+// Measured dense bf16 MFMA rate (peak.hip): synchronises with the stream; sink holds
+// peak_sink_floats() floats of device memory.
+int peak_sink_floats();
+hipError_t peak_mfma_bf16(int iters, float* sink, double* tflops, hipStream_t s);
+}  // namespace csa
+
 extern "C" {
 
 int32_t csa_abi_version(void) { return CSA_ABI_VERSION; }
@@ -230,6 +237,13 @@ csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
 csa_status csa_kernel_timing_enable(int32_t cap) {
   if (cap < 0 || cap > csa::kTimingCap) return fail(CSA_EINVAL, "timing capacity out of range");
   return hip_status(csa::kernel_timing_enable(cap));
+}
+
+int32_t csa_peak_sink_floats(void) { return csa::peak_sink_floats(); }
+
+csa_status csa_peak_mfma_bf16(int32_t iters, float* sink, double* tflops, void* stream) {
+  if (iters <= 0 || sink == nullptr || tflops == nullptr) return fail(CSA_EINVAL, "bad peak query");
+  return hip_status(csa::peak_mfma_bf16(iters, sink, tflops, static_cast<hipStream_t>(stream)));
 }
 
 csa_status csa_kernel_timing_read(int32_t slot, double* ms, int32_t* n) {

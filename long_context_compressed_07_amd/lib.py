@@ -25,7 +25,7 @@ _lib = None
 EXPORTS = ("csa_compress", "csa_index", "csa_topk", "csa_topk_workspace_bytes", "csa_attend",
            "csa_attend_workspace_bytes", "hca_attend", "hca_attend_workspace_bytes",
            "csa_status_str", "csa_last_error", "csa_abi_version", "csa_kernel_timing_enable",
-           "csa_kernel_timing_read")
+           "csa_kernel_timing_read", "csa_peak_mfma_bf16", "csa_peak_sink_floats")
 
 
 class KV(ctypes.Structure):
@@ -70,8 +70,11 @@ def load(path: str = LIB_PATH):
     lib.hca_attend_workspace_bytes.argtypes = [i32, i32, i32, i64]
     lib.csa_kernel_timing_enable.argtypes = [i32]
     lib.csa_kernel_timing_read.argtypes = [i32, P(ctypes.c_double), P(i32)]
+    lib.csa_peak_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
+    lib.csa_peak_sink_floats.argtypes = []
     for fn in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend",
-               "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read"):
+               "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read",
+               "csa_peak_mfma_bf16", "csa_peak_sink_floats"):
         getattr(lib, fn).restype = ctypes.c_int32
     for fn in ("csa_topk_workspace_bytes", "csa_attend_workspace_bytes",
                "hca_attend_workspace_bytes"):
@@ -224,6 +227,16 @@ def kernel_timing_enable(cap: int):
     """Record HIP events around the next `cap` main attention kernels of csa_attend (slot 0) and
     hca_attend (slot 1); cap = 0 stops."""
     _check(load().csa_kernel_timing_enable(cap), "csa_kernel_timing_enable")
+
+
+def peak_mfma_bf16(iters: int = 50000, stream=None) -> float:
+    """Measured dense bf16 MFMA rate of the current device in TFLOP/s (waits for the stream)."""
+    L = load()
+    sink = torch.empty(L.csa_peak_sink_floats(), dtype=torch.float32, device="cuda")
+    tf = ctypes.c_double()
+    _check(L.csa_peak_mfma_bf16(iters, _ptr(sink), ctypes.byref(tf), _stream(stream)),
+           "csa_peak_mfma_bf16")
+    return tf.value
 
 
 def kernel_timing_read(slot: int) -> tuple[float, int]:
