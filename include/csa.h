@@ -117,6 +117,32 @@ csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const fl
                         const csa_kv_out_t* out, float* raw_x_out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_cache_append -- decode-time cache maintenance: one new token per sequence.
+ * [csdn] V4 改进一 (CSA step one, HCA) and [yudong] 2.2 Step 1 / 2.3 Step 1 (m consecutive tokens
+ * pooled into one entry with position-biased softmax weights); [jaylab] 其他技术细节 (cache rows:
+ * fp8 latent with a row scale, bf16 RoPE dims). For every sequence b, with its new token at the
+ * absolute position p = pos[b] (int64, device, p >= 0):
+ *   - stage_x[b][p % m] = x_new[b] and stage_g[b][p % m] = g_new[b], widened to fp32;
+ *   - raw row p - raw_pos0[b] (raw_pos0 NULL: p) of `raw` = x_new[b], stored like a csa_compress
+ *     output row (f32 / bf16 / e4m3 latent with sigma = max|latent| / 448; RoPE bf16, or f32 in
+ *     an f32 store); not written when that row lies outside [0, raw->rows);
+ *   - when p + 1 is a multiple of m: entry row (p + 1) / m - 1 of `entries` = the pooling of the
+ *     m staged rows of the block (csa_compress's e[j,c] = sum_i softmax_i(g[i,c] + bias[i]) x[i,c]),
+ *     stored by the same rules; not written outside [0, entries->rows).
+ *   x_new, g_new [B][d] in in_dtype (F32 or BF16), d = d_c + d_r <= 1024. bias [m] fp32.
+ *   stage_x, stage_g [B][m][d] fp32: caller-owned staging ring, kept between calls (the rows of
+ *     earlier positions of the open block must hold those tokens). Store rows are per sequence
+ *     (batch stride rows); the raw store is the window store csa_attend reads with pos0 = raw_pos0.
+ *   Errors: CSA_EINVAL for a bad dtype, m <= 0, B < 0, non-positive d_c, NULL arguments or store
+ *     fields inconsistent with d_c / d_r / dtype; CSA_EUNSUPPORTED for d > 1024.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dtype,
+                            const float* bias, int32_t m, int32_t B, const int64_t* pos,
+                            int32_t d_c, int32_t d_r, float* stage_x, float* stage_g,
+                            const csa_kv_out_t* entries, const csa_kv_out_t* raw,
+                            const int64_t* raw_pos0, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_index -- lightning-indexer scores of every visible entry for every query.
  * [csdn] V4 改进一 and [yudong] 2.2 Step 2 (a light indexer, in the manner of the V3.2 lightning
  * indexer, scores each compressed row against the query; fp8 accelerated).

@@ -2,6 +2,7 @@
 // pointers and shapes, then dispatch to the kernel launchers. Nothing is enqueued on error.
 #include <string>
 
+#include "append.h"
 #include "csa_internal.h"
 
 namespace {
@@ -237,6 +238,49 @@ csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
 csa_status csa_kernel_timing_enable(int32_t cap) {
   if (cap < 0 || cap > csa::kTimingCap) return fail(CSA_EINVAL, "timing capacity out of range");
   return hip_status(csa::kernel_timing_enable(cap));
+}
+
+csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dtype,
+                            const float* bias, int32_t m, int32_t B, const int64_t* pos,
+                            int32_t d_c, int32_t d_r, float* stage_x, float* stage_g,
+                            const csa_kv_out_t* entries, const csa_kv_out_t* raw,
+                            const int64_t* raw_pos0, void* stream) {
+  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16) return fail(CSA_EINVAL, "in_dtype must be F32 or BF16");
+  if (m <= 0 || B < 0 || d_c <= 0 || d_r < 0) return fail(CSA_EINVAL, "bad m / B / dims");
+  if (d_c + d_r > 1024) return fail(CSA_EUNSUPPORTED, "d_c + d_r > 1024");
+  if (B == 0) return CSA_OK;
+  if (x_new == nullptr || g_new == nullptr || bias == nullptr || pos == nullptr ||
+      stage_x == nullptr || stage_g == nullptr || entries == nullptr || raw == nullptr)
+    return fail(CSA_EINVAL, "null argument");
+  const csa_kv_out_t* st[2] = {entries, raw};
+  for (const csa_kv_out_t* o : st) {
+    if (!valid_dtype(o->dtype_c)) return fail(CSA_EINVAL, "bad store dtype");
+    if (o->d_c != d_c || o->d_r != d_r) return fail(CSA_EINVAL, "store dims differ from d_c/d_r");
+    if (o->rows < 0 || o->ld_c < d_c || (d_r > 0 && o->ld_r < d_r))
+      return fail(CSA_EINVAL, "store rows / leading dimension");
+    if (o->rows > 0 && o->c == nullptr) return fail(CSA_EINVAL, "null store c");
+    if ((d_r > 0) != (o->r != nullptr)) return fail(CSA_EINVAL, "store r must be set iff d_r > 0");
+    if ((o->dtype_c == CSA_E4M3) != (o->scale != nullptr))
+      return fail(CSA_EINVAL, "store scale must be set iff its dtype is E4M3");
+  }
+  csa::AppendArgs a{};
+  a.x_new = x_new;
+  a.g_new = g_new;
+  a.in_dtype = in_dtype;
+  a.bias = bias;
+  a.m = m;
+  a.B = B;
+  a.pos = pos;
+  a.d_c = d_c;
+  a.d_r = d_r;
+  a.stage_x = stage_x;
+  a.stage_g = stage_g;
+  a.ent = csa::OutStore{entries->c, entries->r, entries->scale, entries->dtype_c, d_c, d_r,
+                        entries->rows, entries->ld_c, entries->ld_r};
+  a.raw = csa::OutStore{raw->c, raw->r, raw->scale, raw->dtype_c, d_c, d_r, raw->rows, raw->ld_c,
+                        raw->ld_r};
+  a.raw_pos0 = raw_pos0;
+  return hip_status(csa::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t csa_peak_sink_floats(void) { return csa::peak_sink_floats(); }

@@ -25,7 +25,8 @@ _lib = None
 EXPORTS = ("csa_compress", "csa_index", "csa_topk", "csa_topk_workspace_bytes", "csa_attend",
            "csa_attend_workspace_bytes", "hca_attend", "hca_attend_workspace_bytes",
            "csa_status_str", "csa_last_error", "csa_abi_version", "csa_kernel_timing_enable",
-           "csa_kernel_timing_read", "csa_peak_mfma_bf16", "csa_peak_sink_floats")
+           "csa_kernel_timing_read", "csa_peak_mfma_bf16", "csa_peak_sink_floats",
+           "csa_cache_append")
 
 
 class KV(ctypes.Structure):
@@ -72,9 +73,11 @@ def load(path: str = LIB_PATH):
     lib.csa_kernel_timing_read.argtypes = [i32, P(ctypes.c_double), P(i32)]
     lib.csa_peak_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
     lib.csa_peak_sink_floats.argtypes = []
+    lib.csa_cache_append.argtypes = [vp, vp, i32, vp, i32, i32, vp, i32, i32, vp, vp, P(KVOut),
+                                     P(KVOut), vp, vp]
     for fn in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend",
                "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read",
-               "csa_peak_mfma_bf16", "csa_peak_sink_floats"):
+               "csa_peak_mfma_bf16", "csa_peak_sink_floats", "csa_cache_append"):
         getattr(lib, fn).restype = ctypes.c_int32
     for fn in ("csa_topk_workspace_bytes", "csa_attend_workspace_bytes",
                "hca_attend_workspace_bytes"):
@@ -147,6 +150,20 @@ def _queries(seq: torch.Tensor, pos: torch.Tensor) -> Queries:
     if seq.dtype != torch.int32 or pos.dtype != torch.int64:
         raise ValueError("seq must be int32 and pos int64")
     return Queries(_ptr(seq), _ptr(pos), seq.numel())
+
+
+def csa_cache_append(x_new, g_new, in_dtype: int, bias, m: int, pos, d_c: int, d_r: int,
+                     stage_x, stage_g, entries: Store, raw: Store, raw_pos0=None, stream=None):
+    """One new token per sequence: staging ring, raw window row, and the entry of a completed
+    block (csa_cache_append in include/csa.h)."""
+    lib = load()
+    if pos.dtype != torch.int64 or (raw_pos0 is not None and raw_pos0.dtype != torch.int64):
+        raise ValueError("pos and raw_pos0 must be int64")
+    e, r = entries.as_out(), raw.as_out()
+    _check(lib.csa_cache_append(_ptr(x_new), _ptr(g_new), in_dtype, _ptr(bias), m, pos.numel(),
+                                _ptr(pos), d_c, d_r, _ptr(stage_x), _ptr(stage_g),
+                                ctypes.byref(e), ctypes.byref(r), _ptr(raw_pos0),
+                                _stream(stream)), "csa_cache_append")
 
 
 def csa_compress(x, g, in_dtype: int, bias, m: int, B: int, T: int, d_c: int, d_r: int,
