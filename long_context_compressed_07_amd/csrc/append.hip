@@ -65,37 +65,69 @@ __global__ void __launch_bounds__(kAppThreads) append_kernel(AppendArgs a) {
   const bool ent_ok = close && erow >= 0 && erow < a.ent.rows;
   if (t < 2) s_amax[t] = 0u;
   __syncthreads();
-  float xv[kAppMaxCh], ev[kAppMaxCh];
-  float am_x = 0.f, am_e = 0.f;
-  float* sx = a.stage_x + (int64_t)b * a.m * d;
-  float* sg = a.stage_g + (int64_t)b * a.m * d;
+  // Phase 1: every load of the token rows first (the staging ring may alias nothing the
+  // compiler can prove, so loads are kept ahead of all stores).
+  float xv[kAppMaxCh], gv[kAppMaxCh], ev[kAppMaxCh];
 #pragma unroll
   for (int u = 0; u < kAppMaxCh; ++u) {
     const int c = t + u * kAppThreads;
-    xv[u] = ev[u] = 0.f;
-    if (c >= d) continue;
-    const float x = load_in<TIn>(a.x_new, (int64_t)b * d + c);
-    const float g = load_in<TIn>(a.g_new, (int64_t)b * d + c);
-    sx[(int64_t)slot * d + c] = x;
-    sg[(int64_t)slot * d + c] = g;
-    xv[u] = x;
-    if (c < a.d_c) am_x = fmaxf(am_x, fabsf(x));
-    if (ent_ok) {
-      // Softmax over the block's m positions of g + bias (max-subtracted), then the weighted sum.
-      float mx = g + a.bias[slot];
-      for (int i = 0; i < a.m; ++i)
-        if (i != slot) mx = fmaxf(mx, sg[(int64_t)i * d + c] + a.bias[i]);
-      float den = 0.f, num = 0.f;
-      for (int i = 0; i < a.m; ++i) {
-        const float gi = i == slot ? g : sg[(int64_t)i * d + c];
-        const float xi = i == slot ? x : sx[(int64_t)i * d + c];
-        const float w = __expf(gi + a.bias[i] - mx);
-        den += w;
-        num = fmaf(w, xi, num);
-      }
-      ev[u] = num / den;
-      if (c < a.d_c) am_e = fmaxf(am_e, fabsf(ev[u]));
+    const int cc = c < d ? c : d - 1;
+    xv[u] = load_in<TIn>(a.x_new, (int64_t)b * d + cc);
+    gv[u] = load_in<TIn>(a.g_new, (int64_t)b * d + cc);
+    ev[u] = 0.f;
+  }
+  float* sx = a.stage_x + (int64_t)b * a.m * d;
+  float* sg = a.stage_g + (int64_t)b * a.m * d;
+  float am_x = 0.f, am_e = 0.f;
+#pragma unroll
+  for (int u = 0; u < kAppMaxCh; ++u)
+    if (t + u * kAppThreads < a.d_c) am_x = fmaxf(am_x, fabsf(xv[u]));
+  if (ent_ok) {
+    // Phase 2: the block's pooling, per channel a softmax over its m positions of g + bias
+    // (max-subtracted) and the weighted sum of x; the new token's row comes from registers.
+    float mx[kAppMaxCh], den[kAppMaxCh], num[kAppMaxCh];
+#pragma unroll
+    for (int u = 0; u < kAppMaxCh; ++u) {
+      mx[u] = gv[u] + a.bias[slot];
+      den[u] = 0.f;
+      num[u] = 0.f;
     }
+    for (int i = 0; i < a.m; ++i) {
+      if (i == slot) continue;
+      const float bi = a.bias[i];
+#pragma unroll
+      for (int u = 0; u < kAppMaxCh; ++u) {
+        const int c = t + u * kAppThreads;
+        const int cc = c < d ? c : d - 1;
+        mx[u] = fmaxf(mx[u], sg[(int64_t)i * d + cc] + bi);
+      }
+    }
+    for (int i = 0; i < a.m; ++i) {
+      const float bi = a.bias[i];
+#pragma unroll
+      for (int u = 0; u < kAppMaxCh; ++u) {
+        const int c = t + u * kAppThreads;
+        const int cc = c < d ? c : d - 1;
+        const float gi = i == slot ? gv[u] : sg[(int64_t)i * d + cc];
+        const float xi = i == slot ? xv[u] : sx[(int64_t)i * d + cc];
+        const float w = __expf(gi + bi - mx[u]);
+        den[u] += w;
+        num[u] = fmaf(w, xi, num[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAppMaxCh; ++u) {
+      ev[u] = num[u] / den[u];
+      if (t + u * kAppThreads < a.d_c) am_e = fmaxf(am_e, fabsf(ev[u]));
+    }
+  }
+  // Phase 3: the stores.
+#pragma unroll
+  for (int u = 0; u < kAppMaxCh; ++u) {
+    const int c = t + u * kAppThreads;
+    if (c >= d) continue;
+    sx[(int64_t)slot * d + c] = xv[u];
+    sg[(int64_t)slot * d + c] = gv[u];
   }
   atomicMax(&s_amax[0], __float_as_uint(am_x));
   atomicMax(&s_amax[1], __float_as_uint(am_e));
