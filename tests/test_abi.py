@@ -108,3 +108,27 @@ def test_compress_validation(L):
     out8 = lib.KVOut(0x100, 0x200, 0x300, 2, 512, 64, 25, 512, 64)
     assert L.csa_compress(None, None, 0, 0x30, 4, 1, 100, 512, 64, 0x40, 0x50, 0x60, 256,
                           ctypes.byref(out8), 0x70, None) == 2
+
+
+def test_cache_append_validation(L):
+    def out(**kw):
+        base = dict(c=0x100, r=0x200, scale=0x300, dtype_c=2, d_c=512, d_r=64, rows=10, ld_c=512,
+                    ld_r=64)
+        base.update(kw)
+        return lib.KVOut(base["c"], base["r"], base["scale"], base["dtype_c"], base["d_c"],
+                         base["d_r"], base["rows"], base["ld_c"], base["ld_r"])
+
+    def call(in_dtype=1, m=4, B=2, d_c=512, d_r=64, ent=None, raw=None, x=0x10):
+        e, r = ent or out(), raw or out()
+        return L.csa_cache_append(x, 0x20, in_dtype, 0x30, m, B, 0x40, d_c, d_r, 0x50, 0x60,
+                                  ctypes.byref(e), ctypes.byref(r), None, None)
+
+    assert call(in_dtype=2) == 1                               # e4m3 token rows
+    assert call(m=0) == 1
+    assert call(x=None) == 1                                   # null token rows
+    assert call(ent=out(scale=None)) == 1                      # e4m3 store without scales
+    assert call(raw=out(d_c=256)) == 1                         # store dims differ
+    assert call(raw=out(dtype_c=1, scale=None, ld_c=256)) == 1   # leading dimension < d_c
+    assert call(d_c=1024, d_r=64, ent=out(d_c=1024, ld_c=1024),
+                raw=out(d_c=1024, ld_c=1024)) == 2             # d > 1024
+    assert call(B=0) == 0                                      # nothing to do
