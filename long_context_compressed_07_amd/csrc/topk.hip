@@ -393,9 +393,11 @@ __device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_
   }
 }
 
-// Single stage: one workgroup per query row (n_vis <= kChunk = NT * kPer).
+// Single stage: one workgroup per query row (n_vis <= kChunk = NT * kPer). Six waves per SIMD (at
+// most 80 VGPRs, no spills): 370 -> 336 us for 32768 rows of up to 8192 scores against five.
 template <int NT>
-__global__ void __launch_bounds__(NT) topk_row_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 6)))
+topk_row_kernel(TopkArgs a) {
   static_assert(NT * kPer == kChunk, "one key segment per thread");
   __shared__ int s_tmp[2 * NT / kWave + 2];
   __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
