@@ -12,7 +12,8 @@
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never allocates and
- *     keeps no state besides its loaded kernels. Calls that need scratch take (ws, ws_bytes),
+ *     keeps no state besides its loaded kernels (and the optional, lock-guarded kernel timing
+ *     below). Calls that need scratch take (ws, ws_bytes),
  *     sized by the matching *_workspace_bytes() query; ws may be NULL when that query returns 0.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
  *     returns. No call synchronises. Calls are safe from any host thread.
@@ -210,7 +211,9 @@ size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N)
  * it, with a HIP event pair recorded on the caller's stream around that kernel.
  *   csa_kernel_timing_enable(cap): record the next cap launches per slot (0 <= cap <= 1024);
  *     cap = 0 stops recording and releases the events. Creates HIP events: call outside graph
- *     capture. Not thread-safe: one host thread at a time.
+ *     capture. The timing state is the library's one piece of mutable state: it is guarded by a
+ *     mutex, and while timing is off an attention call only reads an atomic flag. Launches from
+ *     several host threads while timing is on are recorded in the order they take the lock.
  *   csa_kernel_timing_read(slot, &ms, &n): waits for the recorded launches of the slot, returns
  *     their total duration in milliseconds and their count, and clears the slot.
  *   Errors: CSA_EINVAL for a capacity or slot out of range or NULL outputs; CSA_EHIP otherwise.

@@ -28,9 +28,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   const int64_t max_keys = a.dense ? a.ent.rows : (int64_t)a.k + a.window;
   if (!force_generic() && attend_mfma_supported(a)) return launch_attend_mfma(a, max_keys, s);
   const int slot = a.dense ? 1 : 0;
-  const bool timed = timing_start(slot, s);
+  const int timed = timing_start(slot, s);
   const hipError_t e = launch_attend_generic(a, s);
-  if (timed) timing_stop(slot, s);
+  if (timed >= 0) timing_stop(slot, timed, s);
   return e;
 }
 

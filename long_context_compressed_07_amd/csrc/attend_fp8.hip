@@ -8,9 +8,8 @@
 // 2.2 Step 4 and 2.3 Step 2; jaylab-temp.pages.dev "DeepSeek-V4 — 百万 Token 上下文的高效 MoE 模型"
 // 其他技术细节 (fp8 latent with bf16 RoPE dims in the KV cache).
 //
-// The work split is that of the bf16 kernel with four 32-head row groups: a workgroup of 4 waves
-// serves 128 heads of one query (and one key range when a query's keys are split over workgroups);
-// in tiles of 32 keys, wave w computes S^T for row group w (QK) and then O^T for the value dims
+// A workgroup of 4 waves serves 128 heads (four 32-head row groups) of one query (and one key
+// range when a query's keys are split over workgroups); in tiles of 32 keys, wave w computes S^T for row group w (QK) and then O^T for the value dims
 // [128 w, 128 w + 128) of all 128 heads (PV), with P exchanged through LDS. What differs is the
 // staging: rows arrive by DMA in their compact cache format (512 B fp8 latent, 128 B bf16 RoPE,
 // 4 B scale) into one of three staging slots, three tiles ahead of use. While tile t's PV runs,
@@ -21,7 +20,7 @@
 // Numerics. The scale is applied in two exact-or-rounded-once steps: its power of two inside the
 // fp8 conversion (exact), its mantissa as an fp16 multiply (one rounding, relative 2^-11). Queries
 // are rounded bf16 -> fp16 (exact in fp16's normal range), P is fp16, accumulation is fp32. As in
-// the bf16 kernel, the softmax uses a fixed per-head reference and a non-finite output (overflow of
+// the bf16 kernel (attend_pp.hip), the softmax uses a fixed per-head reference and a non-finite output (overflow of
 // fp16 P or of a converted value) flags the workgroup for the fp32 fixup pass.
 #include "attend_generic.h"
 #include "attend_plan.h"
@@ -122,6 +121,8 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
   const int f = swz(r);
   const int rr = 8 * w + (lane >> 3), pr = lane & 7;
   // All six LDS reads in flight at once (one instruction block, so the waits cannot split them).
+  // They read only the staging slot, which nothing but DMA writes; the waits and barriers around
+  // the call order them, so no memory clobber constrains the interleave with the PV MFMAs.
   v4i lv[4], rv;
   int sb;
   asm volatile(

@@ -35,7 +35,8 @@
 // fp16's range; values below 2^-17 keep <= 2^-25 absolute error), accumulation is fp32; P is
 // rounded to fp16 (relative error 2^-11) and the softmax denominator sums the rounded values.
 #include <algorithm>
-#include <cstdlib>
+#include <atomic>
+#include <mutex>
 
 #include "attend_generic.h"
 #include "attend_plan.h"
@@ -468,8 +469,8 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
   }
 }
 
-// Work decomposition. bf16 caches with a multiple of 64 heads take the DMA kernel
-// (attend_bf16.hip): one workgroup per query and group of 64 or 128 heads. fp8 caches with a
+// Work decomposition. bf16 caches with a multiple of 64 heads take the two-role DMA kernel
+// (attend_pp.hip): one workgroup per query and group of 64 heads. fp8 caches with a
 // multiple of 128 heads take the fp8 DMA kernel (attend_fp8.hip): one workgroup per query and
 // group of 128 heads. Everything else takes the fp16-staging kernel here: many queries (prefill)
 // give one workgroup per query and head group, 4 head groups sharing each staged tile (ksw 1) or
@@ -478,15 +479,7 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
 // workgroups (n_split), merged by combine_kernel.
 enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 
-// CSA_ATTEND_PP=0 selects the single-role bf16 kernels (64 or 128 heads per workgroup) instead of
-// the two-role 64-head one (for comparisons and their tests).
-static bool pp_disabled() {
-  const char* e = std::getenv("CSA_ATTEND_PP");
-  return e != nullptr && e[0] == '0';
-}
-
-// two_role: bf16 heads in 64-head workgroups with the two wave roles (attend_pp.hip).
-MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind, bool two_role) {
+MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
   MfmaPlan p{};
   const int groups32 = H / 32;
   const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
@@ -496,13 +489,11 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind, bool two_role) {
     return (int)(ns < cap_ ? ns : cap_);
   };
   if (kind == kPlanBf16 && groups32 % 2 == 0) {
-    p.bf16_dma = 1;
     // 64-head workgroups with the two wave roles (attend_pp.hip) for every even number of 32-head
-    // groups (measured on 128 heads: 8.3 vs 9.2 ms for the HCA prefill, although each key tile is
-    // loaded once per 64 heads instead of once per 128); CSA_ATTEND_PP=0 selects the 4-wave kernel
-    // (128 heads per workgroup where they divide).
-    p.pp = two_role;
-    p.rg = (!p.pp && groups32 % 4 == 0) ? 4 : 2;
+    // groups (measured on 128 heads: 8.3 vs 9.2 ms for the HCA prefill against a 4-wave kernel
+    // with 128 heads per workgroup, although each key tile is loaded once per 64 heads).
+    p.pp = 1;
+    p.rg = 2;
     p.head_groups = groups32 / p.rg;
     p.n_split = splits_for(p.head_groups, cap);
     return p;
@@ -564,17 +555,17 @@ static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
 size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
   // The dtypes are not part of the workspace query: cover every plan kind.
   size_t part = 0, flags = 0;
-  for (int kind = 0; kind < 3; ++kind)
-    for (int two_role = 0; two_role < 2; ++two_role) {   // either choice of the bf16 kernel
-      const MfmaPlan p = make_plan(nq, H, max_keys, kind, two_role != 0);
-      part = std::max(part, plan_partial_bytes(p, nq, H));
-      flags = std::max(flags, plan_flag_bytes(p, nq));
-    }
+  for (int kind = 0; kind < 3; ++kind) {
+    const MfmaPlan p = make_plan(nq, H, max_keys, kind);
+    part = std::max(part, plan_partial_bytes(p, nq, H));
+    flags = std::max(flags, plan_flag_bytes(p, nq));
+  }
   return part + flags;
 }
 
 // Optional timing of the main attention kernel alone (slot 0: CSA, slot 1: HCA): a HIP event
-// pair recorded on the launch stream around it.
+// pair recorded on the launch stream around it. The state is guarded by a mutex; while timing is
+// off (the normal case) an attention call reads one atomic flag and touches nothing else.
 namespace {
 struct KernelTiming {
   int cap = 0;
@@ -582,9 +573,13 @@ struct KernelTiming {
   hipEvent_t ev[2][2][kTimingCap];   // [slot][start / end][launch]
 };
 KernelTiming g_timing;
+std::mutex g_timing_mu;
+std::atomic<int> g_timing_on{0};
 }  // namespace
 
 hipError_t kernel_timing_enable(int cap) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on.store(0, std::memory_order_release);
   for (int slot = 0; slot < 2; ++slot)
     for (int j = 0; j < 2; ++j)
       for (int i = 0; i < g_timing.cap; ++i) (void)hipEventDestroy(g_timing.ev[slot][j][i]);
@@ -599,6 +594,7 @@ hipError_t kernel_timing_enable(int cap) {
       }
     g_timing.cap = i + 1;
   }
+  g_timing_on.store(cap > 0 ? 1 : 0, std::memory_order_release);
   return hipSuccess;
 }
 
@@ -606,6 +602,7 @@ hipError_t kernel_timing_read(int slot, double* ms, int* n) {
   *ms = 0.0;
   *n = 0;
   if (slot < 0 || slot > 1) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
   for (int i = 0; i < g_timing.n[slot]; ++i) {
     hipError_t e = hipEventSynchronize(g_timing.ev[slot][1][i]);
     if (e != hipSuccess) return e;
@@ -619,18 +616,22 @@ hipError_t kernel_timing_read(int slot, double* ms, int* n) {
   return hipSuccess;
 }
 
-bool timing_start(int slot, hipStream_t s) {
-  if (g_timing.n[slot] >= g_timing.cap) return false;
-  (void)hipEventRecord(g_timing.ev[slot][0][g_timing.n[slot]], s);
-  return true;
+int timing_start(int slot, hipStream_t s) {
+  if (!g_timing_on.load(std::memory_order_acquire)) return -1;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (g_timing.n[slot] >= g_timing.cap) return -1;
+  const int i = g_timing.n[slot]++;
+  (void)hipEventRecord(g_timing.ev[slot][0][i], s);
+  return i;
 }
 
-void timing_stop(int slot, hipStream_t s) {
-  (void)hipEventRecord(g_timing.ev[slot][1][g_timing.n[slot]++], s);
+void timing_stop(int slot, int i, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (i < g_timing.cap) (void)hipEventRecord(g_timing.ev[slot][1][i], s);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a), !pp_disabled());
+  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
   if (p.n_split > 1) {
     p.ws_o = static_cast<_Float16*>(a.ws);
     p.ws_ml = reinterpret_cast<float*>(p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC);
@@ -639,16 +640,11 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   const bool fp8 = a.ent.dtype == CSA_E4M3;
   const int tslot = a.dense ? 1 : 0;
-  const bool timed = timing_start(tslot, s);
+  const int timed = timing_start(tslot, s);
   if (p.pp) {
-    hipError_t e = launch_attend_pp(a, p, s);
-    if (e != hipSuccess) return e;
-  } else if (p.bf16_dma) {
-    hipError_t e = launch_attend_bf16(a, p, s);
-    if (e != hipSuccess) return e;
+    (void)launch_attend_pp(a, p, s);
   } else if (p.f8_dma) {
-    hipError_t e = launch_attend_fp8(a, p, s);
-    if (e != hipSuccess) return e;
+    (void)launch_attend_fp8(a, p, s);
   } else switch (p.ksw * 2 + (fp8 ? 1 : 0)) {
     case 2: attend_mfma_kernel<CSA_BF16, 1><<<grid, 256, 0, s>>>(a, p); break;
     case 3: attend_mfma_kernel<CSA_E4M3, 1><<<grid, 256, 0, s>>>(a, p); break;
@@ -658,8 +654,8 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t
     default: attend_mfma_kernel<CSA_E4M3, 4><<<grid, 256, 0, s>>>(a, p); break;
   }
   hipError_t e = hipGetLastError();
+  if (timed >= 0) timing_stop(tslot, timed, s);   // closes the pair even after a failed launch
   if (e != hipSuccess) return e;
-  if (timed) timing_stop(tslot, s);
   if (p.n_split > 1) {
     combine_kernel<<<(unsigned)((int64_t)a.Q.nq * (a.H / kCombHeads)), kGenThreads, 0, s>>>(a, p);
   } else {

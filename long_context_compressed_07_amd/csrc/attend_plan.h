@@ -8,10 +8,9 @@ namespace csa {
 
 struct AttnPlan {
   int ksw;            // fp16-staging kernel: key splits inside a workgroup (4 / ksw head groups)
-  int rg;             // bf16 kernel: 32-head row groups per workgroup (2 or 4)
+  int rg;             // DMA kernels: 32-head row groups per workgroup (bf16: 2, fp8: 4)
   int head_groups;    // workgroups per query along heads
   int n_split;        // workgroups per query along keys
-  int bf16_dma;       // 1: bf16 rows staged by DMA (attend_bf16.hip); 0: fp16 staging
   int f8_dma;         // 1: fp8 rows staged by DMA and converted in LDS (attend_fp8.hip)
   int pp;             // 1: bf16, 64 heads per workgroup, QK and PV wave roles (attend_pp.hip)
   _Float16* ws_o;     // [nq][n_split][H][512] partial outputs normalised by their l, n_split > 1
@@ -38,7 +37,6 @@ __device__ __forceinline__ void store_partial4(_Float16* dst, float a, float b, 
                                    (_Float16)(d * inv)};
 }
 
-hipError_t launch_attend_bf16(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_fp8(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_pp(const AttendArgs& a, const AttnPlan& p, hipStream_t s);
 

@@ -25,9 +25,9 @@
 // the 64 heads' queries once by DMA (into the two buffers idle until the first tile) and the QK
 // waves read their fragments from there.
 //
-// Numerics as in attend_bf16.hip: bf16 products exact in fp32, V converted to fp16 (exact in
-// fp16's normal range), P fp16, fixed reference maximum from the first tile that holds a key, and a
-// non-finite output flags the workgroup for the fp32 fixup pass.
+// Numerics: bf16 products exact in fp32, V converted to fp16 (exact in fp16's normal range), P
+// fp16, fixed reference maximum from the first tile that holds a key, and a non-finite output
+// flags the workgroup for the fp32 fixup pass.
 #include "attend_generic.h"
 #include "attend_plan.h"
 #include "attend_tile.h"
@@ -88,63 +88,11 @@ __device__ __forceinline__ void dma_tile_regs(const KeyAddr& ka, char* buf, int 
   __builtin_amdgcn_global_load_lds(src, (lds_char*)(buf + kPpTK * 1024 + 1024 * wv), 16, 0, 0);
 }
 
-// Q^T fragments of a QK wave for mfma_f32_16x16x32_bf16: q[2 s + h] = Q[head 16 h + (lane & 15)]
-// [dims 32 s + 8 (lane >> 4) + (0..7)] of the row group. The 32 latent fragments go straight into
-// accumulation registers, in one block that waits for its loads.
-__device__ __forceinline__ void load_q16(const uint16_t* q0, const uint16_t* q1, v4i (&q)[36]) {
-  const int g = (threadIdx.x & 63) >> 4;
-  const uint16_t* p0 = q0 + 8 * g;
-  const uint16_t* p1 = q1 + 8 * g;
-  asm volatile(
-      "global_load_dwordx4 %0, %32, off offset:0\n"
-      "global_load_dwordx4 %1, %33, off offset:0\n"
-      "global_load_dwordx4 %2, %32, off offset:64\n"
-      "global_load_dwordx4 %3, %33, off offset:64\n"
-      "global_load_dwordx4 %4, %32, off offset:128\n"
-      "global_load_dwordx4 %5, %33, off offset:128\n"
-      "global_load_dwordx4 %6, %32, off offset:192\n"
-      "global_load_dwordx4 %7, %33, off offset:192\n"
-      "global_load_dwordx4 %8, %32, off offset:256\n"
-      "global_load_dwordx4 %9, %33, off offset:256\n"
-      "global_load_dwordx4 %10, %32, off offset:320\n"
-      "global_load_dwordx4 %11, %33, off offset:320\n"
-      "global_load_dwordx4 %12, %32, off offset:384\n"
-      "global_load_dwordx4 %13, %33, off offset:384\n"
-      "global_load_dwordx4 %14, %32, off offset:448\n"
-      "global_load_dwordx4 %15, %33, off offset:448\n"
-      "global_load_dwordx4 %16, %32, off offset:512\n"
-      "global_load_dwordx4 %17, %33, off offset:512\n"
-      "global_load_dwordx4 %18, %32, off offset:576\n"
-      "global_load_dwordx4 %19, %33, off offset:576\n"
-      "global_load_dwordx4 %20, %32, off offset:640\n"
-      "global_load_dwordx4 %21, %33, off offset:640\n"
-      "global_load_dwordx4 %22, %32, off offset:704\n"
-      "global_load_dwordx4 %23, %33, off offset:704\n"
-      "global_load_dwordx4 %24, %32, off offset:768\n"
-      "global_load_dwordx4 %25, %33, off offset:768\n"
-      "global_load_dwordx4 %26, %32, off offset:832\n"
-      "global_load_dwordx4 %27, %33, off offset:832\n"
-      "global_load_dwordx4 %28, %32, off offset:896\n"
-      "global_load_dwordx4 %29, %33, off offset:896\n"
-      "global_load_dwordx4 %30, %32, off offset:960\n"
-      "global_load_dwordx4 %31, %33, off offset:960\n"
-      "s_waitcnt vmcnt(0)\n"
-      : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]),
-        "=a"(q[7]), "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]),
-        "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]),
-        "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]),
-        "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
-      : "v"(p0), "v"(p1));
-#pragma unroll
-  for (int s = 16; s < 18; ++s) {
-    q[2 * s] = *reinterpret_cast<const v4i*>(p0 + 32 * s);
-    q[2 * s + 1] = *reinterpret_cast<const v4i*>(p1 + 32 * s);
-  }
-}
-
-// The Q^T fragments of load_q16 from LDS, where the workgroup's DMA has put fragment f of this
-// row group at base + 1 KB f (lane l's 16 bytes at 16 l): one block that waits for its reads,
-// the 32 latent fragments into accumulation registers (at most 15 reads outstanding).
+// Q^T fragments of a QK wave for mfma_f32_16x16x32_bf16 from LDS: q[2 s + h] = Q[head
+// 16 h + (lane & 15)][dims 32 s + 8 (lane >> 4) + (0..7)] of the row group, where the
+// workgroup's DMA has put fragment f of this row group at base + 1 KB f (lane l's 16 bytes at
+// 16 l). One block that waits for its reads, the 32 latent fragments into accumulation registers
+// (at most 15 reads outstanding).
 __device__ __forceinline__ void load_q16_lds(int base, v4i (&q)[36]) {
   asm volatile(
       "ds_read_b128 %0, %32 offset:0\n"
@@ -187,7 +135,8 @@ __device__ __forceinline__ void load_q16_lds(int base, v4i (&q)[36]) {
         "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]),
         "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]),
         "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
-      : "v"(base));
+      : "v"(base)
+      : "memory");
 }
 
 __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan plan) {
@@ -411,7 +360,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt][0] = o[mt][1] = floatx16{};
     bool have_ref = false;
-    int v_even, v_odd;   // V^T fragment addressing (the layout and key order of attend_bf16.hip)
+    int v_even, v_odd;   // V^T fragment addressing in the swizzled tile layout (attend_tile.h)
     {
       const int g = lane >> 4, la = lane & 15;
       const int f = 2 * (la >> 2) + hi;

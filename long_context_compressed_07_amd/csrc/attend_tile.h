@@ -1,6 +1,6 @@
 // Building blocks shared by the MFMA attention kernels that stage key tiles in LDS by DMA
-// (attend_bf16.hip, attend_fp8.hip): tile layout helpers, key codes, the barrier and wait
-// encodings, P^T exchange reads and the QK instruction block.
+// (attend_pp.hip, attend_fp8.hip): tile layout helpers, key codes, the barrier and wait
+// encodings, P^T exchange reads and the generated QK instruction blocks.
 //
 // LDS tile layout: rows stay unpadded, split into a latent region ([rows][1024 B]) and a RoPE
 // region ([rows][128 B]) of 16-bit values. 16-byte chunk c of row r sits at chunk position
@@ -87,12 +87,6 @@ __device__ __forceinline__ void dma_sel(const KeyList& kl, int64_t kk0, int64_t 
   const void* src = (lane < TK && kk < ke && kk < kl.n_sel) ? (const void*)(kl.sel + kk)
                                                            : (const void*)kZeroRow;
   __builtin_amdgcn_global_load_lds(src, (lds_char*)dst, 4, 0, 0);
-}
-
-__device__ __forceinline__ int key_code_of(const KeyList& kl, int64_t kk, int raw, int64_t ke) {
-  if (kk >= ke || raw < 0) return -1;
-  if (kk < kl.n_sel) return kl.sel != nullptr ? raw : (int)kk;          // entry row (store 0)
-  return (int)(kl.wlo + (kk - kl.n_sel) - kl.raw_base) | (1 << 30);   // raw-window row
 }
 
 // Output rows through LDS. The accumulators hold O^T in the MFMA layout (lane: one head, 4-dim
@@ -265,697 +259,270 @@ struct TileDmaF8 {
 
 // ---- BEGIN GENERATED QK BLOCKS ----
 // (written by gen_qk_asm.py; edit the generator, not these lines)
-template <bool QA, int NV, int NLAT, int NROPE, int TK>
-__device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int (&lb)[4],
-                                             const int (&rb)[4], int ve, int vo,
-                                             v2i (&vr)[NV > 0 ? 2 * NV : 1],
-                                             const TileDma<NLAT, NROPE>& dma) {
-  floatx16 acc;
-  v4i t0, t1, t2, t3, t4;
-  if constexpr (QA && NV == 16 && NLAT == 16 && NROPE == 2 && TK == 64) {
-    asm volatile(
-      "ds_read_b128 %1, %74\n"
-      "ds_read_b128 %2, %75\n"
-      "ds_read_b128 %3, %76\n"
-      "ds_read_b128 %4, %77\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %38, 0\n"
-      "ds_read_b128 %5, %74 offset:128\n"
-      "s_mov_b32 m0, %85\n"
-      "s_nop 0\n"
-      "global_load_lds_dword %84, off\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %39, %0\n"
-      "ds_read_b128 %1, %75 offset:128\n"
-      "s_mov_b32 m0, %88\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %87\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %40, %0\n"
-      "ds_read_b128 %2, %76 offset:128\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %41, %0\n"
-      "ds_read_b128 %3, %77 offset:128\n"
-      "s_add_u32 m0, %88, 4096\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %90\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %42, %0\n"
-      "ds_read_b128 %4, %74 offset:256\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %43, %0\n"
-      "ds_read_b128 %5, %75 offset:256\n"
-      "s_add_u32 m0, %88, 8192\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %91\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %44, %0\n"
-      "ds_read_b128 %1, %76 offset:256\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %45, %0\n"
-      "ds_read_b128 %2, %77 offset:256\n"
-      "s_add_u32 m0, %88, 12288\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %92\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %46, %0\n"
-      "ds_read_b128 %3, %74 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %47, %0\n"
-      "ds_read_b128 %4, %75 offset:384\n"
-      "s_add_u32 m0, %88, 16384\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %93\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %48, %0\n"
-      "ds_read_b128 %5, %76 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %49, %0\n"
-      "ds_read_b128 %1, %77 offset:384\n"
-      "s_add_u32 m0, %88, 20480\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %94\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %50, %0\n"
-      "ds_read_b128 %2, %74 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %51, %0\n"
-      "ds_read_b128 %3, %75 offset:512\n"
-      "s_add_u32 m0, %88, 24576\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %95\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %52, %0\n"
-      "ds_read_b128 %4, %76 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %53, %0\n"
-      "ds_read_b128 %5, %77 offset:512\n"
-      "s_add_u32 m0, %88, 28672\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %96\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %54, %0\n"
-      "ds_read_b128 %1, %74 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %55, %0\n"
-      "ds_read_b128 %2, %75 offset:640\n"
-      "s_add_u32 m0, %88, 32768\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %97\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %56, %0\n"
-      "ds_read_b128 %3, %76 offset:640\n"
-      "s_add_u32 m0, %88, 36864\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %98\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %57, %0\n"
-      "ds_read_b128 %4, %77 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %58, %0\n"
-      "ds_read_b128 %5, %74 offset:768\n"
-      "s_add_u32 m0, %88, 40960\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %99\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %59, %0\n"
-      "ds_read_b128 %1, %75 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %60, %0\n"
-      "ds_read_b128 %2, %76 offset:768\n"
-      "s_add_u32 m0, %88, 45056\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %100\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %61, %0\n"
-      "ds_read_b128 %3, %77 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %62, %0\n"
-      "ds_read_b128 %4, %74 offset:896\n"
-      "s_add_u32 m0, %88, 49152\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %101\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %63, %0\n"
-      "ds_read_b128 %5, %75 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %64, %0\n"
-      "ds_read_b128 %1, %76 offset:896\n"
-      "s_add_u32 m0, %88, 53248\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %102\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %65, %0\n"
-      "ds_read_b128 %2, %77 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %66, %0\n"
-      "ds_read_b128 %3, %78\n"
-      "s_add_u32 m0, %88, 57344\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %86, %103\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %67, %0\n"
-      "ds_read_b128 %4, %79\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %68, %0\n"
-      "ds_read_b128 %5, %80\n"
-      "s_add_u32 m0, %88, 61440\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %89, %104\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %69, %0\n"
-      "ds_read_b128 %1, %81\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %70, %0\n"
-      "s_add_u32 m0, %88, 65536\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %105, off\n"
-      "ds_read_b64_tr_b16 %6, %82 offset:0\n"
-      "ds_read_b64_tr_b16 %7, %82 offset:8192\n"
-      "ds_read_b64_tr_b16 %8, %83 offset:64\n"
-      "ds_read_b64_tr_b16 %9, %83 offset:8256\n"
-      "ds_read_b64_tr_b16 %10, %82 offset:128\n"
-      "ds_read_b64_tr_b16 %11, %82 offset:8320\n"
-      "s_waitcnt lgkmcnt(8)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %71, %0\n"
-      "ds_read_b64_tr_b16 %12, %83 offset:192\n"
-      "ds_read_b64_tr_b16 %13, %83 offset:8384\n"
-      "ds_read_b64_tr_b16 %14, %82 offset:16384\n"
-      "ds_read_b64_tr_b16 %15, %82 offset:24576\n"
-      "ds_read_b64_tr_b16 %16, %83 offset:16448\n"
-      "ds_read_b64_tr_b16 %17, %83 offset:24640\n"
-      "s_waitcnt lgkmcnt(13)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %72, %0\n"
-      "s_add_u32 m0, %88, 69632\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %106, off\n"
-      "ds_read_b64_tr_b16 %18, %82 offset:16512\n"
-      "ds_read_b64_tr_b16 %19, %82 offset:24704\n"
-      "s_waitcnt lgkmcnt(14)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %73, %0\n"
-      "ds_read_b64_tr_b16 %20, %83 offset:16576\n"
-      "ds_read_b64_tr_b16 %21, %83 offset:24768\n"
-      "ds_read_b64_tr_b16 %22, %82 offset:32768\n"
-      "ds_read_b64_tr_b16 %23, %82 offset:40960\n"
-      "ds_read_b64_tr_b16 %24, %83 offset:32832\n"
-      "ds_read_b64_tr_b16 %25, %83 offset:41024\n"
-      "ds_read_b64_tr_b16 %26, %82 offset:32896\n"
-      "ds_read_b64_tr_b16 %27, %82 offset:41088\n"
-      "ds_read_b64_tr_b16 %28, %83 offset:32960\n"
-      "ds_read_b64_tr_b16 %29, %83 offset:41152\n"
-      "ds_read_b64_tr_b16 %30, %82 offset:49152\n"
-      "ds_read_b64_tr_b16 %31, %82 offset:57344\n"
-      "ds_read_b64_tr_b16 %32, %83 offset:49216\n"
-      "ds_read_b64_tr_b16 %33, %83 offset:57408\n"
-      "ds_read_b64_tr_b16 %34, %82 offset:49280\n"
-      "ds_read_b64_tr_b16 %35, %82 offset:57472\n"
-      "ds_read_b64_tr_b16 %36, %83 offset:49344\n"
-      "ds_read_b64_tr_b16 %37, %83 offset:57536\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 4\n"
-      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15]), "=&v"(vr[16]), "=&v"(vr[17]), "=&v"(vr[18]), "=&v"(vr[19]), "=&v"(vr[20]), "=&v"(vr[21]), "=&v"(vr[22]), "=&v"(vr[23]), "=&v"(vr[24]), "=&v"(vr[25]), "=&v"(vr[26]), "=&v"(vr[27]), "=&v"(vr[28]), "=&v"(vr[29]), "=&v"(vr[30]), "=&v"(vr[31])
-      : "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "a"(q[4]), "a"(q[5]), "a"(q[6]), "a"(q[7]), "a"(q[8]), "a"(q[9]), "a"(q[10]), "a"(q[11]), "a"(q[12]), "a"(q[13]), "a"(q[14]), "a"(q[15]), "a"(q[16]), "a"(q[17]), "a"(q[18]), "a"(q[19]), "a"(q[20]), "a"(q[21]), "a"(q[22]), "a"(q[23]), "a"(q[24]), "a"(q[25]), "a"(q[26]), "a"(q[27]), "a"(q[28]), "a"(q[29]), "a"(q[30]), "a"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]), "v"(rb[2]), "v"(rb[3]), "v"(ve), "v"(vo), "v"(dma.sel), "s"(dma.m0_sel), "v"(dma.off[0]), "s"(dma.lat[0]), "s"(dma.m0_rows), "v"(dma.off[1]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "s"(dma.lat[8]), "s"(dma.lat[9]), "s"(dma.lat[10]), "s"(dma.lat[11]), "s"(dma.lat[12]), "s"(dma.lat[13]), "s"(dma.lat[14]), "s"(dma.lat[15]), "v"(dma.rope[0]), "v"(dma.rope[1])
-      : "m0");
-  } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {
-    asm volatile(
-      "ds_read_b128 %1, %42\n"
-      "ds_read_b128 %2, %43\n"
-      "ds_read_b128 %3, %44\n"
-      "ds_read_b128 %4, %45\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %6, 0\n"
-      "ds_read_b128 %5, %42 offset:128\n"
-      "s_mov_b32 m0, %51\n"
-      "s_nop 0\n"
-      "global_load_lds_dword %50, off\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %7, %0\n"
-      "ds_read_b128 %1, %43 offset:128\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %8, %0\n"
-      "ds_read_b128 %2, %44 offset:128\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %9, %0\n"
-      "ds_read_b128 %3, %45 offset:128\n"
-      "s_mov_b32 m0, %54\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %53\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %10, %0\n"
-      "ds_read_b128 %4, %42 offset:256\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %11, %0\n"
-      "ds_read_b128 %5, %43 offset:256\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %12, %0\n"
-      "ds_read_b128 %1, %44 offset:256\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %13, %0\n"
-      "ds_read_b128 %2, %45 offset:256\n"
-      "s_add_u32 m0, %54, 4096\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %55, %56\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %14, %0\n"
-      "ds_read_b128 %3, %42 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %15, %0\n"
-      "ds_read_b128 %4, %43 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %16, %0\n"
-      "ds_read_b128 %5, %44 offset:384\n"
-      "s_add_u32 m0, %54, 8192\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %57\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %17, %0\n"
-      "ds_read_b128 %1, %45 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %18, %0\n"
-      "ds_read_b128 %2, %42 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %19, %0\n"
-      "ds_read_b128 %3, %43 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %20, %0\n"
-      "ds_read_b128 %4, %44 offset:512\n"
-      "s_add_u32 m0, %54, 12288\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %55, %58\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %21, %0\n"
-      "ds_read_b128 %5, %45 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %22, %0\n"
-      "ds_read_b128 %1, %42 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %23, %0\n"
-      "ds_read_b128 %2, %43 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %24, %0\n"
-      "ds_read_b128 %3, %44 offset:640\n"
-      "s_add_u32 m0, %54, 16384\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %59\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %25, %0\n"
-      "ds_read_b128 %4, %45 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %26, %0\n"
-      "ds_read_b128 %5, %42 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %27, %0\n"
-      "ds_read_b128 %1, %43 offset:768\n"
-      "s_add_u32 m0, %54, 20480\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %55, %60\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
-      "ds_read_b128 %2, %44 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %29, %0\n"
-      "ds_read_b128 %3, %45 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %30, %0\n"
-      "ds_read_b128 %4, %42 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %31, %0\n"
-      "ds_read_b128 %5, %43 offset:896\n"
-      "s_add_u32 m0, %54, 24576\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %61\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %32, %0\n"
-      "ds_read_b128 %1, %44 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %33, %0\n"
-      "ds_read_b128 %2, %45 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %34, %0\n"
-      "ds_read_b128 %3, %46\n"
-      "s_add_u32 m0, %54, 28672\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %55, %62\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %35, %0\n"
-      "ds_read_b128 %4, %47\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %36, %0\n"
-      "ds_read_b128 %5, %48\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %37, %0\n"
-      "ds_read_b128 %1, %49\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %38, %0\n"
-      "s_add_u32 m0, %54, 32768\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %63, off\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %39, %0\n"
-      "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %40, %0\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %41, %0\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 4\n"
-      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
-      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]), "v"(rb[2]), "v"(rb[3]), "v"(dma.sel), "s"(dma.m0_sel), "v"(dma.off[0]), "s"(dma.lat[0]), "s"(dma.m0_rows), "v"(dma.off[1]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "v"(dma.rope[0])
-      : "m0");
-  } else {
-    static_assert(QA && NV == 16, "unsupported configuration");
-  }
-  return acc;
-}
-
 __device__ __forceinline__ void qk16_chain(const v4i (&q)[36], int lbe, int lbo, int rbe,
                                            int rbo, const TileDma<8, 1>& dma,
                                            floatx4& acc0, floatx4& acc1) {
   v4i t0, t1, t2, t3, t4;
+  int m0s;
     asm volatile(
-      "ds_read_b128 %2, %43\n"
-      "ds_read_b128 %3, %44\n"
-      "ds_read_b128 %4, %43 offset:128\n"
-      "ds_read_b128 %5, %44 offset:128\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %7, 0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %2, %8, 0\n"
-      "ds_read_b128 %6, %43 offset:256\n"
-      "s_mov_b32 m0, %48\n"
-      "s_nop 0\n"
-      "global_load_lds_dword %47, off\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %9, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %3, %10, %1\n"
-      "ds_read_b128 %2, %44 offset:256\n"
-      "s_mov_b32 m0, %51\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %49, %50\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %11, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %12, %1\n"
-      "ds_read_b128 %3, %43 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %5, %14, %1\n"
-      "ds_read_b128 %4, %44 offset:384\n"
-      "s_add_u32 m0, %51, 4096\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %53\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %6, %15, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %6, %16, %1\n"
-      "ds_read_b128 %5, %43 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %17, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %2, %18, %1\n"
-      "ds_read_b128 %6, %44 offset:512\n"
-      "s_add_u32 m0, %51, 8192\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %49, %54\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %19, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %3, %20, %1\n"
-      "ds_read_b128 %2, %43 offset:640\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %21, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %22, %1\n"
-      "ds_read_b128 %3, %44 offset:640\n"
-      "s_add_u32 m0, %51, 12288\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %55\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %5, %23, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %5, %24, %1\n"
-      "ds_read_b128 %4, %43 offset:768\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %6, %25, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %6, %26, %1\n"
-      "ds_read_b128 %5, %44 offset:768\n"
-      "s_add_u32 m0, %51, 16384\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %49, %56\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %27, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %2, %28, %1\n"
-      "ds_read_b128 %6, %43 offset:896\n"
-      "s_add_u32 m0, %51, 20480\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %57\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %29, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %3, %30, %1\n"
-      "ds_read_b128 %2, %44 offset:896\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %31, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %32, %1\n"
+      "s_mov_b32 %7, m0\n"
+      "ds_read_b128 %2, %44\n"
       "ds_read_b128 %3, %45\n"
-      "s_add_u32 m0, %51, 24576\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %49, %58\n"
+      "ds_read_b128 %4, %44 offset:128\n"
+      "ds_read_b128 %5, %45 offset:128\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %5, %33, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %5, %34, %1\n"
-      "ds_read_b128 %4, %46\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %6, %35, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %6, %36, %1\n"
-      "s_add_u32 m0, %51, 28672\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %8, 0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %9, 0\n"
+      "ds_read_b128 %6, %44 offset:256\n"
+      "s_mov_b32 m0, %49\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, %59\n"
+      "global_load_lds_dword %48, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %10, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %11, %1\n"
+      "ds_read_b128 %2, %45 offset:256\n"
+      "s_mov_b32 m0, %52\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %50, %51\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %13, %1\n"
+      "ds_read_b128 %3, %44 offset:384\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %14, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %15, %1\n"
+      "ds_read_b128 %4, %45 offset:384\n"
+      "s_add_u32 m0, %52, 4096\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %53, %54\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %16, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %17, %1\n"
+      "ds_read_b128 %5, %44 offset:512\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %18, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %19, %1\n"
+      "ds_read_b128 %6, %45 offset:512\n"
+      "s_add_u32 m0, %52, 8192\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %50, %55\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %20, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %21, %1\n"
+      "ds_read_b128 %2, %44 offset:640\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %22, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %23, %1\n"
+      "ds_read_b128 %3, %45 offset:640\n"
+      "s_add_u32 m0, %52, 12288\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %53, %56\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %24, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %25, %1\n"
+      "ds_read_b128 %4, %44 offset:768\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %26, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %27, %1\n"
+      "ds_read_b128 %5, %45 offset:768\n"
+      "s_add_u32 m0, %52, 16384\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %50, %57\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %28, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %29, %1\n"
+      "ds_read_b128 %6, %44 offset:896\n"
+      "s_add_u32 m0, %52, 20480\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %53, %58\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %30, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %31, %1\n"
+      "ds_read_b128 %2, %45 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %32, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %33, %1\n"
+      "ds_read_b128 %3, %46\n"
+      "s_add_u32 m0, %52, 24576\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %50, %59\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %34, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %35, %1\n"
+      "ds_read_b128 %4, %47\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %36, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %37, %1\n"
+      "s_add_u32 m0, %52, 28672\n"
+      "s_nop 0\n"
+      "global_load_lds_dwordx4 %53, %60\n"
       "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %37, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %2, %38, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %38, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %39, %1\n"
       "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %39, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %3, %40, %1\n"
-      "s_add_u32 m0, %51, 32768\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %3, %40, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %41, %1\n"
+      "s_add_u32 m0, %52, 32768\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %60, off\n"
+      "global_load_lds_dwordx4 %61, off\n"
       "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %41, %0\n"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %42, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %42, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %43, %1\n"
+      "s_mov_b32 m0, %7\n"
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 4\n"
-      : "=&v"(acc0), "=&v"(acc1), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
+      : "=&v"(acc0), "=&v"(acc1), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&s"(m0s)
       : "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "a"(q[4]), "a"(q[5]), "a"(q[6]), "a"(q[7]), "a"(q[8]), "a"(q[9]), "a"(q[10]), "a"(q[11]), "a"(q[12]), "a"(q[13]), "a"(q[14]), "a"(q[15]), "a"(q[16]), "a"(q[17]), "a"(q[18]), "a"(q[19]), "a"(q[20]), "a"(q[21]), "a"(q[22]), "a"(q[23]), "a"(q[24]), "a"(q[25]), "a"(q[26]), "a"(q[27]), "a"(q[28]), "a"(q[29]), "a"(q[30]), "a"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lbe), "v"(lbo), "v"(rbe), "v"(rbo), "v"(dma.sel), "s"(dma.m0_sel), "v"(dma.off[0]), "s"(dma.lat[0]), "s"(dma.m0_rows), "v"(dma.off[1]), "s"(dma.lat[1]), "s"(dma.lat[2]), "s"(dma.lat[3]), "s"(dma.lat[4]), "s"(dma.lat[5]), "s"(dma.lat[6]), "s"(dma.lat[7]), "v"(dma.rope[0])
-      : "m0");
+      : "scc", "memory");
 }
 
 __device__ __forceinline__ floatx16 qk_chain_f16(const v4i (&q)[kKSteps], const int (&lb)[4],
                                                  const int (&rb)[4], const TileDmaF8& dma) {
   floatx16 acc;
   v4i t0, t1, t2, t3, t4;
+  int m0s;
     asm volatile(
-      "ds_read_b128 %1, %42\n"
-      "ds_read_b128 %2, %43\n"
-      "ds_read_b128 %3, %44\n"
-      "ds_read_b128 %4, %45\n"
+      "s_mov_b32 %6, m0\n"
+      "ds_read_b128 %1, %43\n"
+      "ds_read_b128 %2, %44\n"
+      "ds_read_b128 %3, %45\n"
+      "ds_read_b128 %4, %46\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %6, 0\n"
-      "ds_read_b128 %5, %42 offset:128\n"
-      "s_mov_b32 m0, %51\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %7, 0\n"
+      "ds_read_b128 %5, %43 offset:128\n"
+      "s_mov_b32 m0, %52\n"
       "s_nop 0\n"
-      "global_load_lds_dword %50, off\n"
+      "global_load_lds_dword %51, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %7, %0\n"
-      "ds_read_b128 %1, %43 offset:128\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %8, %0\n"
+      "ds_read_b128 %1, %44 offset:128\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %8, %0\n"
-      "ds_read_b128 %2, %44 offset:128\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %9, %0\n"
+      "ds_read_b128 %2, %45 offset:128\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %9, %0\n"
-      "ds_read_b128 %3, %45 offset:128\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %10, %0\n"
+      "ds_read_b128 %3, %46 offset:128\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %10, %0\n"
-      "ds_read_b128 %4, %42 offset:256\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %11, %0\n"
+      "ds_read_b128 %4, %43 offset:256\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %11, %0\n"
-      "ds_read_b128 %5, %43 offset:256\n"
-      "s_mov_b32 m0, %53\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %12, %0\n"
+      "ds_read_b128 %5, %44 offset:256\n"
+      "s_mov_b32 m0, %54\n"
       "s_nop 0\n"
-      "global_load_lds_dwordx4 %52, off\n"
+      "global_load_lds_dwordx4 %53, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %12, %0\n"
-      "ds_read_b128 %1, %44 offset:256\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %13, %0\n"
+      "ds_read_b128 %1, %45 offset:256\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %13, %0\n"
-      "ds_read_b128 %2, %45 offset:256\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %14, %0\n"
+      "ds_read_b128 %2, %46 offset:256\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %14, %0\n"
-      "ds_read_b128 %3, %42 offset:384\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %15, %0\n"
+      "ds_read_b128 %3, %43 offset:384\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %15, %0\n"
-      "ds_read_b128 %4, %43 offset:384\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %16, %0\n"
+      "ds_read_b128 %4, %44 offset:384\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %16, %0\n"
-      "ds_read_b128 %5, %44 offset:384\n"
-      "s_add_u32 m0, %53, 4160\n"
-      "s_nop 0\n"
-      "global_load_lds_dwordx4 %54, off\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %17, %0\n"
-      "ds_read_b128 %1, %45 offset:384\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %18, %0\n"
-      "ds_read_b128 %2, %42 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %19, %0\n"
-      "ds_read_b128 %3, %43 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %20, %0\n"
-      "ds_read_b128 %4, %44 offset:512\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %21, %0\n"
-      "ds_read_b128 %5, %45 offset:512\n"
-      "s_add_u32 m0, %53, 8320\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %17, %0\n"
+      "ds_read_b128 %5, %45 offset:384\n"
+      "s_add_u32 m0, %54, 4160\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %55, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %22, %0\n"
-      "ds_read_b128 %1, %42 offset:640\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %18, %0\n"
+      "ds_read_b128 %1, %46 offset:384\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %23, %0\n"
-      "ds_read_b128 %2, %43 offset:640\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %19, %0\n"
+      "ds_read_b128 %2, %43 offset:512\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %24, %0\n"
-      "ds_read_b128 %3, %44 offset:640\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %20, %0\n"
+      "ds_read_b128 %3, %44 offset:512\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %25, %0\n"
-      "ds_read_b128 %4, %45 offset:640\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %21, %0\n"
+      "ds_read_b128 %4, %45 offset:512\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %26, %0\n"
-      "ds_read_b128 %5, %42 offset:768\n"
-      "s_add_u32 m0, %53, 12480\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %22, %0\n"
+      "ds_read_b128 %5, %46 offset:512\n"
+      "s_add_u32 m0, %54, 8320\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %56, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %27, %0\n"
-      "ds_read_b128 %1, %43 offset:768\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %23, %0\n"
+      "ds_read_b128 %1, %43 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %28, %0\n"
-      "ds_read_b128 %2, %44 offset:768\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %24, %0\n"
+      "ds_read_b128 %2, %44 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %29, %0\n"
-      "ds_read_b128 %3, %45 offset:768\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %25, %0\n"
+      "ds_read_b128 %3, %45 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %30, %0\n"
-      "ds_read_b128 %4, %42 offset:896\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %26, %0\n"
+      "ds_read_b128 %4, %46 offset:640\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %31, %0\n"
-      "ds_read_b128 %5, %43 offset:896\n"
-      "s_mov_b32 m0, %58\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %27, %0\n"
+      "ds_read_b128 %5, %43 offset:768\n"
+      "s_add_u32 m0, %54, 12480\n"
       "s_nop 0\n"
       "global_load_lds_dwordx4 %57, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %32, %0\n"
-      "ds_read_b128 %1, %44 offset:896\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %28, %0\n"
+      "ds_read_b128 %1, %44 offset:768\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %33, %0\n"
-      "ds_read_b128 %2, %45 offset:896\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %29, %0\n"
+      "ds_read_b128 %2, %45 offset:768\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %34, %0\n"
-      "ds_read_b128 %3, %46\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %30, %0\n"
+      "ds_read_b128 %3, %46 offset:768\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %35, %0\n"
-      "ds_read_b128 %4, %47\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %31, %0\n"
+      "ds_read_b128 %4, %43 offset:896\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %36, %0\n"
-      "ds_read_b128 %5, %48\n"
-      "s_mov_b32 m0, %60\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %32, %0\n"
+      "ds_read_b128 %5, %44 offset:896\n"
+      "s_mov_b32 m0, %59\n"
       "s_nop 0\n"
-      "global_load_lds_dword %59, off\n"
+      "global_load_lds_dwordx4 %58, off\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %2, %37, %0\n"
-      "ds_read_b128 %1, %49\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %33, %0\n"
+      "ds_read_b128 %1, %45 offset:896\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %3, %38, %0\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %34, %0\n"
+      "ds_read_b128 %2, %46 offset:896\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %35, %0\n"
+      "ds_read_b128 %3, %47\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %36, %0\n"
+      "ds_read_b128 %4, %48\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %37, %0\n"
+      "ds_read_b128 %5, %49\n"
+      "s_mov_b32 m0, %61\n"
+      "s_nop 0\n"
+      "global_load_lds_dword %60, off\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_f16 %0, %2, %38, %0\n"
+      "ds_read_b128 %1, %50\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_f16 %0, %3, %39, %0\n"
       "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %4, %39, %0\n"
+      "v_mfma_f32_32x32x16_f16 %0, %4, %40, %0\n"
       "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %5, %40, %0\n"
+      "v_mfma_f32_32x32x16_f16 %0, %5, %41, %0\n"
       "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_f16 %0, %1, %41, %0\n"
+      "v_mfma_f32_32x32x16_f16 %0, %1, %42, %0\n"
+      "s_mov_b32 m0, %6\n"
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 4\n"
-      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4)
+      : "=&v"(acc), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&s"(m0s)
       : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]), "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]), "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]), "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]), "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35]), "v"(lb[0]), "v"(lb[1]), "v"(lb[2]), "v"(lb[3]), "v"(rb[0]), "v"(rb[1]), "v"(rb[2]), "v"(rb[3]), "v"(dma.sel), "s"(dma.m0_sel), "v"(dma.lat[0]), "s"(dma.m0_lat), "v"(dma.lat[1]), "v"(dma.lat[2]), "v"(dma.lat[3]), "v"(dma.rope), "s"(dma.m0_rope), "v"(dma.scl), "s"(dma.m0_scl)
-      : "m0");
+      : "scc", "memory");
   return acc;
 }
 // ---- END GENERATED QK BLOCKS ----
-
-// Q^T fragments of one head (bf16, as stored): fragment s holds dims 16 s + 8 hi + [0, 8). With QA
-// the 32 latent fragments are loaded straight into accumulation registers, in one block that
-// waits for its loads.
-template <bool QA>
-__device__ __forceinline__ void load_q(const uint16_t* qrow, int hi, v4i (&q)[kKSteps]) {
-  const uint16_t* p = qrow + 8 * hi;
-  if constexpr (QA) {
-    asm volatile(
-        "global_load_dwordx4 %0, %32, off offset:0\n"
-        "global_load_dwordx4 %1, %32, off offset:32\n"
-        "global_load_dwordx4 %2, %32, off offset:64\n"
-        "global_load_dwordx4 %3, %32, off offset:96\n"
-        "global_load_dwordx4 %4, %32, off offset:128\n"
-        "global_load_dwordx4 %5, %32, off offset:160\n"
-        "global_load_dwordx4 %6, %32, off offset:192\n"
-        "global_load_dwordx4 %7, %32, off offset:224\n"
-        "global_load_dwordx4 %8, %32, off offset:256\n"
-        "global_load_dwordx4 %9, %32, off offset:288\n"
-        "global_load_dwordx4 %10, %32, off offset:320\n"
-        "global_load_dwordx4 %11, %32, off offset:352\n"
-        "global_load_dwordx4 %12, %32, off offset:384\n"
-        "global_load_dwordx4 %13, %32, off offset:416\n"
-        "global_load_dwordx4 %14, %32, off offset:448\n"
-        "global_load_dwordx4 %15, %32, off offset:480\n"
-        "global_load_dwordx4 %16, %32, off offset:512\n"
-        "global_load_dwordx4 %17, %32, off offset:544\n"
-        "global_load_dwordx4 %18, %32, off offset:576\n"
-        "global_load_dwordx4 %19, %32, off offset:608\n"
-        "global_load_dwordx4 %20, %32, off offset:640\n"
-        "global_load_dwordx4 %21, %32, off offset:672\n"
-        "global_load_dwordx4 %22, %32, off offset:704\n"
-        "global_load_dwordx4 %23, %32, off offset:736\n"
-        "global_load_dwordx4 %24, %32, off offset:768\n"
-        "global_load_dwordx4 %25, %32, off offset:800\n"
-        "global_load_dwordx4 %26, %32, off offset:832\n"
-        "global_load_dwordx4 %27, %32, off offset:864\n"
-        "global_load_dwordx4 %28, %32, off offset:896\n"
-        "global_load_dwordx4 %29, %32, off offset:928\n"
-        "global_load_dwordx4 %30, %32, off offset:960\n"
-        "global_load_dwordx4 %31, %32, off offset:992\n"
-        "s_waitcnt vmcnt(0)\n"
-        : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]), "=a"(q[7]), "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]), "=a"(q[14]), "=a"(q[15]), "=a"(q[16]), "=a"(q[17]), "=a"(q[18]), "=a"(q[19]), "=a"(q[20]), "=a"(q[21]), "=a"(q[22]), "=a"(q[23]), "=a"(q[24]), "=a"(q[25]), "=a"(q[26]), "=a"(q[27]), "=a"(q[28]), "=a"(q[29]), "=a"(q[30]), "=a"(q[31])
-        : "v"(p));
-  } else {
-#pragma unroll
-    for (int s = 0; s < 32; ++s) q[s] = *reinterpret_cast<const v4i*>(p + 16 * s);
-  }
-#pragma unroll
-  for (int s = 32; s < kKSteps; ++s) q[s] = *reinterpret_cast<const v4i*>(p + 16 * s);
-}
-
-// The P^T fragments of one tile (8 of them: k-step ks and row group r at index ks * RG + r), read
-// from the exchange buffer in one block that waits for its reads.
-__device__ __forceinline__ void load_p8(int addr, v4i (&p)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:0\n"
-      "ds_read_b128 %1, %8 offset:1024\n"
-      "ds_read_b128 %2, %8 offset:2048\n"
-      "ds_read_b128 %3, %8 offset:3072\n"
-      "ds_read_b128 %4, %8 offset:4096\n"
-      "ds_read_b128 %5, %8 offset:5120\n"
-      "ds_read_b128 %6, %8 offset:6144\n"
-      "ds_read_b128 %7, %8 offset:7168\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]), "=v"(p[7])
-      : "v"(addr));
-}
 
 // Four P^T fragments (consecutive 1 KB slots from addr), read in one block that waits for them.
 __device__ __forceinline__ void load_p4(int addr, v4i (&p)[4]) {
@@ -966,7 +533,8 @@ __device__ __forceinline__ void load_p4(int addr, v4i (&p)[4]) {
       "ds_read_b128 %3, %4 offset:3072\n"
       "s_waitcnt lgkmcnt(0)\n"
       : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3])
-      : "v"(addr));
+      : "v"(addr)
+      : "memory");
 }
 
 }  // namespace

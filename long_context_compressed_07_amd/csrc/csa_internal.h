@@ -94,8 +94,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 constexpr int kTimingCap = 1024;
 hipError_t kernel_timing_enable(int cap);
 hipError_t kernel_timing_read(int slot, double* ms, int* n);
-bool timing_start(int slot, hipStream_t s);   // true: an event pair is open for this launch
-void timing_stop(int slot, hipStream_t s);
+int timing_start(int slot, hipStream_t s);   // >= 0: index of the event pair opened for this launch
+void timing_stop(int slot, int i, hipStream_t s);
 
 // ---- attention -----------------------------------------------------------------------------
 struct AttendArgs {

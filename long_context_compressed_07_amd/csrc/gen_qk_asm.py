@@ -1,40 +1,32 @@
 """Generates the QK instruction blocks of attend_tile.h (between the GENERATED markers).
 
-The blocks are long, regular instruction sequences (36 MFMAs with K-fragment reads kept four ahead,
-optional transposed V^T reads at the tail, and the next tile's DMA interleaved between the MFMAs);
+The blocks are long, regular instruction sequences (36 MFMAs, or 18 pairs of 16x16 MFMAs, with
+K-fragment reads kept four ahead and the next tile's DMA interleaved between the MFMAs);
 writing them by hand would be error-prone, so they are produced here and committed. Run
 `python gen_qk_asm.py` from this directory after changing the sequences below.
 """
 from __future__ import annotations
 
 import os
-import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TARGET = os.path.join(HERE, "attend_tile.h")
 NL = "\\n"
 N = 36      # k-steps of a 576-dim row (16 dims each)
-D = 4       # K-fragment reads in flight (default)
-D_RG2 = 4        # K-fragment reads in flight in the 64-head bf16 block
+D = 4       # K-fragment reads in flight
 C_QK = 1         # independent accumulation chains per QK block (summed on return)
 ST_PAIR = 1040   # fp8 staging: bytes between latent row pairs (kStPair in attend_fp8.hip)
 
 
-class Ops:
-    """Operand numbering of one asm statement."""
-
-    def __init__(self):
-        self.n = 0
-        self.outs, self.ins = [], []
-
-    def out(self, expr, cons="=&v"):
-        self.outs.append('"%s"(%s)' % (cons, expr))
-        self.n += 1
-        return "%%%d" % (self.n - 1)
-
-    def inp(self, expr, cons="v"):
-        self.ins.append((cons, expr))
-        return None  # numbered after outputs
+def _statement(lines, outs, ins):
+    """The asm statement. M0 is a reserved register: each block saves it into an SGPR operand
+    (m0s) before its first DMA and restores it after the last one, so the compiler's view of M0
+    is intact and it need not (and cannot) be declared clobbered. The s_add_u32 forming the DMA
+    bases writes SCC, and the block reads LDS and writes it by DMA: both are declared."""
+    out_s = ", ".join('"=&%s"(%s)' % ("s" if o == "m0s" else "v", o) for o in outs)
+    in_s = ", ".join('"%s"(%s)' % (c, n) for n, c in ins)
+    return "    asm volatile(\n      " + "\n      ".join(lines) + "\n      : " + out_s + \
+        "\n      : " + in_s + "\n      : \"scc\", \"memory\");"
 
 
 def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
@@ -44,7 +36,7 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
     are symbolic names resolved below."""
     T = D + 1   # rotating K-fragment registers
     accs = ["acc"] if C == 1 else ["acc", "acc2"]   # C independent accumulation chains
-    outs = accs + ["t%d" % i for i in range(T)] + ["vr[%d]" % i for i in range(2 * nv)]
+    outs = accs + ["t%d" % i for i in range(T)] + ["vr[%d]" % i for i in range(2 * nv)] + ["m0s"]
     ins = [("q[%d]" % i, q_lat_cons if i < 32 else "v") for i in range(36)]
     ins += [("lb[%d]" % i, "v") for i in range(4)] + [("rb[%d]" % i, "v") for i in range(4)]
     if nv:
@@ -72,6 +64,7 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
         L.append('"%s%s"' % (x, NL))
 
     t = ["t%d" % i for i in range(T)]
+    emit("s_mov_b32 %s, m0" % op("m0s"))
     for j in range(D):
         emit("ds_read_b128 %s, %s%s" % (op(t[j]), op("lb[%d]" % (j & 3)),
                                         "" if j < 4 else " offset:%d" % (128 * (j >> 2))))
@@ -123,14 +116,11 @@ def block(mnemonic, q_lat_cons, nv, dmas, tk_rows_v, D=D, C=1):
     assert di == nd
     if nv:
         emit("s_waitcnt lgkmcnt(0)")
+    emit("s_mov_b32 m0, %s" % op("m0s"))
     emit("s_nop 7")
     emit("s_nop 7")
     emit("s_nop 4")
-    out_s = ", ".join('"=&v"(%s)' % o for o in outs)
-    in_s = ", ".join('"%s"(%s)' % (c, n) for n, c in ins)
-    text = "    asm volatile(\n      " + "\n      ".join(L) + "\n      : " + out_s + "\n      : " + \
-        in_s + "\n      : \"m0\");"
-    return text
+    return _statement(L, outs, ins)
 
 
 def block16(dmas, D=4):
@@ -141,7 +131,7 @@ def block16(dmas, D=4):
     q[2 s + h] (latent ones from accumulation registers)."""
     NS = 18
     T = D + 1
-    outs = ["acc0", "acc1"] + ["t%d" % i for i in range(T)]
+    outs = ["acc0", "acc1"] + ["t%d" % i for i in range(T)] + ["m0s"]
     ins = [("q[%d]" % i, "a" if i < 32 else "v") for i in range(36)]
     ins += [("lbe", "v"), ("lbo", "v"), ("rbe", "v"), ("rbo", "v")]
     dma_names = []
@@ -176,6 +166,7 @@ def block16(dmas, D=4):
         return "%s%s" % (base, "" if off == 0 else " offset:%d" % off)
 
     t = ["t%d" % i for i in range(T)]
+    emit("s_mov_b32 %s, m0" % op("m0s"))
     for j in range(D):
         emit("ds_read_b128 %s, %s" % (op(t[j]), kread(j)))
     nd = len(dmas)
@@ -204,13 +195,11 @@ def block16(dmas, D=4):
                                           for a in [x[0] for x in addr] + (["off"] if len(addr) == 1 else []))))
             di += 1
     assert di == nd
+    emit("s_mov_b32 m0, %s" % op("m0s"))
     emit("s_nop 7")
     emit("s_nop 7")
     emit("s_nop 4")
-    out_s = ", ".join('"=&v"(%s)' % o for o in outs)
-    in_s = ", ".join('"%s"(%s)' % (c, n) for n, c in ins)
-    return "    asm volatile(\n      " + "\n      ".join(L) + "\n      : " + out_s + "\n      : " + \
-        in_s + "\n      : \"m0\");"
+    return _statement(L, outs, ins)
 
 
 def bf16_dmas(nlat, nrope, tk):
@@ -240,27 +229,11 @@ def main():
     b1 = src.index("// ---- END GENERATED QK BLOCKS ----")
     gen = ["// ---- BEGIN GENERATED QK BLOCKS ----",
            "// (written by gen_qk_asm.py; edit the generator, not these lines)",
-           "template <bool QA, int NV, int NLAT, int NROPE, int TK>",
-           "__device__ __forceinline__ floatx16 qk_chain(const v4i (&q)[kKSteps], const int (&lb)[4],",
-           "                                             const int (&rb)[4], int ve, int vo,",
-           "                                             v2i (&vr)[NV > 0 ? 2 * NV : 1],",
-           "                                             const TileDma<NLAT, NROPE>& dma) {",
-           "  floatx16 acc" + (", acc2" if C_QK == 2 else "") + ";",
-           "  v4i " + ", ".join("t%d" % i for i in range(D_RG2 + 1)) + ";",
-           "  if constexpr (QA && NV == 16 && NLAT == 16 && NROPE == 2 && TK == 64) {",
-           block("v_mfma_f32_32x32x16_bf16", "a", 16, bf16_dmas(16, 2, 64), 64, D=D_RG2, C=C_QK),
-           "  } else if constexpr (!QA && NV == 0 && NLAT == 8 && NROPE == 1 && TK == 32) {",
-           block("v_mfma_f32_32x32x16_bf16", "v", 0, bf16_dmas(8, 1, 32), 32, C=C_QK),
-           "  } else {",
-           "    static_assert(QA && NV == 16, \"unsupported configuration\");",
-           "  }",
-           "  return acc" + (" + acc2" if C_QK == 2 else "") + ";",
-           "}",
-           "",
            "__device__ __forceinline__ void qk16_chain(const v4i (&q)[36], int lbe, int lbo, int rbe,",
            "                                           int rbo, const TileDma<8, 1>& dma,",
            "                                           floatx4& acc0, floatx4& acc1) {",
            "  v4i t0, t1, t2, t3, t4;",
+           "  int m0s;",
            block16(bf16_dmas(8, 1, 32)),
            "}",
            "",
@@ -268,6 +241,7 @@ def main():
            "                                                 const int (&rb)[4], const TileDmaF8& dma) {",
            "  floatx16 acc" + (", acc2" if C_QK == 2 else "") + ";",
            "  v4i t0, t1, t2, t3, t4;",
+           "  int m0s;",
            block("v_mfma_f32_32x32x16_f16", "v", 0, f8_dmas(), 32, C=C_QK),
            "  return acc" + (" + acc2" if C_QK == 2 else "") + ";",
            "}",

@@ -273,22 +273,3 @@ def lse_merge(parts):
     o = sum(wts[i][:, None] * parts[i][0] for i in range(len(parts)))
     o = o / np.where(tot > 0, tot, 1.0)[:, None]
     return o, lse
-
-
-# --------------------------------------------------------------------------------------------
-# Whole-layer drivers (loops over queries; slow on purpose)
-# --------------------------------------------------------------------------------------------
-def csa_layer(queries, q, q_i, w_i, k_i, entries, raw, m: int, k: int, window: int,
-              sm_scale: float):
-    """Index -> top-k -> attend for each query. queries: list of (seq, pos); q [nq, H, d];
-    q_i [nq, H_I, d_I]; w_i [nq, H_I]; k_i [B, N, d_I]; entries/raw: per-sequence lists of
-    (c, r, scale, pos0) tuples. Returns (o [nq, H, d_c], lse [nq, H], idx [nq, k], gap [nq])."""
-    outs, lses, idxs, gaps = [], [], [], []
-    for qi, (b, pos) in enumerate(queries):
-        n_entries = k_i[b].shape[0]
-        nv = n_visible(pos, m, n_entries)
-        s = index_scores(q_i[qi], w_i[qi], k_i[b], nv)
-        idx, gap = topk(s, nv, k)
-        o, lse = csa_attend_one(q[qi], entries[b], idx, raw[b], pos, window, sm_scale)
-        outs.append(o); lses.append(lse); idxs.append(idx); gaps.append(gap)
-    return np.stack(outs), np.stack(lses), np.stack(idxs), np.array(gaps)

@@ -3,8 +3,9 @@ on (samples of) a workload, and compare with the GPU path by the acceptance rule
 
 * index sets: bit-exact where the relative gap at the k-th boundary exceeds 1e-4, otherwise a valid
   top-k within 1e-4 of the k-th score;
-* attention outputs: max |gpu - ref| / max |ref| over the call <= 2e-3 for fp32/bf16 caches,
-  2e-2 for fp8 caches;
+* attention outputs: per query, max |gpu - ref| / max |ref| over that query's heads and dims,
+  and the largest of these over the queries checked <= 2e-3 for fp32/bf16 caches, 2e-2 for fp8
+  caches (the call-wide ratio is kept as a statistic);
 * top-k on identical scores: bit-exact (integer work).
 """
 from __future__ import annotations
@@ -45,6 +46,17 @@ def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+def rel_err_per_query(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per query (leading axis): max |gpu - ref| / max |ref| over the query's other axes. A query
+    whose reference is all zero (no keys) reports its absolute error."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    n = ref.shape[0]
+    num = np.abs(gpu - ref).reshape(n, -1).max(axis=1) if ref.size else np.zeros(n)
+    den = np.abs(ref).reshape(n, -1).max(axis=1) if ref.size else np.zeros(n)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
 def store_f64(c, r, scale, pos0=0):
     """(c, r, scale, pos0) tuple of float64 arrays for one sequence (the oracle's store form)."""
     return (c, r, scale, pos0)
@@ -52,7 +64,8 @@ def store_f64(c, r, scale, pos0=0):
 
 def check_topk_valid(idx_gpu: np.ndarray, scores64: np.ndarray, n_vis: int, k: int):
     """A valid top-k when the boundary is a near-tie: right size, distinct, visible, ascending,
-    -1 padded, and every selected score within 1e-4 (relative) of the k-th largest."""
+    -1 padded, every selected score within 1e-4 (relative) of the k-th largest, and every visible
+    entry scoring more than 1e-4 (relative) above the k-th largest selected."""
     take = min(k, n_vis)
     sel = idx_gpu[:take]
     assert (idx_gpu[take:] == -1).all()
@@ -61,4 +74,7 @@ def check_topk_valid(idx_gpu: np.ndarray, scores64: np.ndarray, n_vis: int, k: i
     assert (np.diff(sel) > 0).all()
     if n_vis > k:
         kth = np.sort(scores64[:n_vis])[::-1][k - 1]
-        assert (scores64[sel] >= kth - GAP_EXACT * max(abs(kth), 1e-30)).all()
+        tol = GAP_EXACT * max(abs(kth), 1e-30)
+        assert (scores64[sel] >= kth - tol).all()
+        must = np.nonzero(scores64[:n_vis] > kth + tol)[0]
+        assert np.isin(must, sel).all(), "an entry clearly above the k-th score was dropped"

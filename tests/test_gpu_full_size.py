@@ -1,9 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
 The whole step runs at full size; the oracle then recomputes a sample of its outputs one query at
-a time (first and last queries, queries near the start of the visible range, and seeded random
-ones) and of its compressed entries one block at a time, to the same acceptance rules as the
-scaled-down tests.
+a time and of its compressed entries one block at a time, to the same acceptance rules as the
+scaled-down tests: 512 position-stratified queries of the 32K CSA prefill, 128 of the HCA prefill,
+every query of the two fp8 decode workloads and of the fp32 decode workload. The prefill
+workloads are also checked end to end against the oracle run from the raw inputs alone (its own
+pooled entries, scores and selection).
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ from long_context_compressed_07_amd.inputs import make_inputs
 from long_context_compressed_07_amd.layer import Step
 
 import parity
+from oracle_io import to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -26,11 +29,15 @@ def _gpu():
     lib.load()
 
 
-def _sample(nq: int, n: int, seed: int) -> np.ndarray:
+def _stratified(nq: int, n: int, seed: int) -> np.ndarray:
+    """n queries, one drawn from each of n equal position strata, plus the first two and the
+    last two (a prefill's work per query grows with its position)."""
+    if n >= nq:
+        return np.arange(nq)
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, nq // 2, nq - 2, nq - 1]
-    extra = rng.choice(nq, min(nq, n), replace=False)
-    return np.unique(np.clip(np.concatenate([fixed, extra]), 0, nq - 1))
+    edges = np.linspace(0, nq, n + 1).astype(np.int64)
+    pick = [rng.integers(edges[i], max(edges[i] + 1, edges[i + 1])) for i in range(n)]
+    return np.unique(np.concatenate([[0, 1, nq - 2, nq - 1], pick]))
 
 
 def _run_full(cfg: str):
@@ -44,33 +51,72 @@ def _run_full(cfg: str):
     return wl, host, step
 
 
+def test_csa_decode_f32_full_size():
+    wl, host, step = _run_full("C1")
+    print("[full] C1: compress check", flush=True)
+    parity.check_compress(wl, host, step)
+    stats = {}
+    parity.check_csa(wl, host, step, stats=stats)
+    parity.check_end_to_end(wl, host, step, stats=stats)
+    print(stats, flush=True)
+
+
 def test_csa_prefill_full_size_sampled():
     wl, host, step = _run_full("C2")
     print("[full] C2: compress check", flush=True)
-    parity.check_compress(wl, host, step, sample_blocks=128, seed=1)
+    parity.check_compress(wl, host, step, sample_blocks=256, seed=1)
     print("[full] C2: csa check", flush=True)
     stats = {}
-    parity.check_csa(wl, host, step, qsel=_sample(wl.B * wl.nq, 6, 2), stats=stats)
+    qsel = _stratified(wl.B * wl.nq, 512, 2)
+    parity.check_csa(wl, host, step, qsel=qsel, stats=stats)
     print(stats, flush=True)
+    print("[full] C2: end to end", flush=True)
+    parity.check_end_to_end(wl, host, step, qsel=qsel, stats=stats)
+    print(stats, flush=True)
+
+
+def test_csa_prefill_full_size_e4m3_entries():
+    # csa_compress of the 32K prefill's token rows into an fp8 entry store (e4m3 latent with a row
+    # scale, bf16 RoPE part), sampled blocks against the oracle's pooling and storage step.
+    wl = FULL["C2"]
+    host = make_inputs(wl, SEED_BASE["C2"])
+    N = wl.n_entries
+    dev = "cuda"
+    x = torch.from_numpy(host["x"].view(np.int16)).to(dev)
+    g = torch.from_numpy(host["g"].view(np.int16)).to(dev)
+    bias = torch.from_numpy(host["bias"]).to(dev)
+    c = torch.empty((wl.B, N, wl.d_c), dtype=torch.uint8, device=dev)
+    r = torch.empty((wl.B, N, wl.d_r), dtype=torch.int16, device=dev)
+    sc = torch.empty((wl.B, N), dtype=torch.float32, device=dev)
+    st = lib.Store(c, lib.E4M3, wl.d_c, wl.d_r, N, wl.d_c, r=r, ld_r=wl.d_r, scale=sc)
+    print("[full] C2: e4m3 compress", flush=True)
+    lib.csa_compress(x, g, lib.BF16, bias, wl.m, wl.B, wl.T, wl.d_c, wl.d_r, st)
+    torch.cuda.synchronize()
+    parity.check_compress_e4m3(wl, host, to_np(c), to_np(r), sc.cpu().numpy(),
+                               sample_blocks=512, seed=3)
 
 
 def test_hca_prefill_full_size_sampled():
     wl, host, step = _run_full("C3")
     print("[full] C3: compress check", flush=True)
-    parity.check_compress(wl, host, step, sample_blocks=64, seed=3)
+    parity.check_compress(wl, host, step, sample_blocks=128, seed=3)
     print("[full] C3: hca check", flush=True)
     stats = {}
-    parity.check_hca(wl, host, step, qsel=_sample(wl.B * wl.nq, 6, 4), stats=stats)
+    qsel = _stratified(wl.B * wl.nq, 128, 4)
+    parity.check_hca(wl, host, step, qsel=qsel, stats=stats)
+    print(stats, flush=True)
+    print("[full] C3: end to end", flush=True)
+    parity.check_end_to_end(wl, host, step, qsel=qsel, stats=stats)
     print(stats, flush=True)
 
 
 @pytest.mark.parametrize("cfg", ["C4", "C5"])
-def test_decode_full_size_sampled(cfg):
+def test_decode_full_size_all_queries(cfg):
     wl, host, step = _run_full(cfg)
-    print(f"[full] {cfg}: csa check", flush=True)
+    print(f"[full] {cfg}: csa check ({wl.B * wl.nq} queries)", flush=True)
     stats = {}
-    parity.check_csa(wl, host, step, qsel=_sample(wl.B * wl.nq, 4, 5), stats=stats)
+    parity.check_csa(wl, host, step, stats=stats)
     if wl.kind == "hybrid_decode":
         print(f"[full] {cfg}: hca check", flush=True)
-        parity.check_hca(wl, host, step, qsel=_sample(wl.B * wl.nq, 4, 6), stats=stats)
+        parity.check_hca(wl, host, step, stats=stats)
     print(stats, flush=True)

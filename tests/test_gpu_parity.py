@@ -52,6 +52,40 @@ def test_csa_layer_small(cfg, sharp):
     print(stats)
 
 
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3"])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_end_to_end_small(cfg, sharp):
+    # The GPU's outputs against the oracle run from the raw inputs alone: its own pooled and
+    # stored entries, fp64 index scores and selection (queries with a clear selection gap).
+    wl = SMALL[cfg]
+    print(f"[parity] end to end {cfg} {wl.name} sharp={sharp}", flush=True)
+    host, step = _run(wl, sharp, _cfg_seed(cfg) + 20)
+    stats = {}
+    parity.check_end_to_end(wl, host, step, stats=stats)
+    print(stats)
+    assert stats["e2e_queries"] > 0
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3"])
+def test_compress_e4m3_store(cfg):
+    # csa_compress into an fp8 entry store: e4m3 latent with one fp32 scale per row, bf16 RoPE.
+    from oracle_io import to_np
+    wl = SMALL[cfg]
+    print(f"[parity] e4m3 compress {cfg} {wl.name}", flush=True)
+    host = make_inputs(wl, _cfg_seed(cfg) + 30, sharp=True)
+    N, dev = wl.n_entries, "cuda"
+    x = torch.from_numpy(host["x"].view(np.int16)).to(dev)
+    g = torch.from_numpy(host["g"].view(np.int16)).to(dev)
+    bias = torch.from_numpy(host["bias"]).to(dev)
+    c = torch.full((wl.B, N, wl.d_c), 0x7f, dtype=torch.uint8, device=dev)
+    r = torch.zeros((wl.B, N, wl.d_r), dtype=torch.int16, device=dev)
+    sc = torch.full((wl.B, N), -1.0, dtype=torch.float32, device=dev)
+    st = lib.Store(c, lib.E4M3, wl.d_c, wl.d_r, N, wl.d_c, r=r, ld_r=wl.d_r, scale=sc)
+    lib.csa_compress(x, g, lib.BF16, bias, wl.m, wl.B, wl.T, wl.d_c, wl.d_r, st)
+    torch.cuda.synchronize()
+    parity.check_compress_e4m3(wl, host, to_np(c), to_np(r), sc.cpu().numpy())
+
+
 @pytest.mark.parametrize("cfg", ["C2", "C3", "C4", "C5"])
 def test_fp16_overflow_recompute(cfg):
     # Unit-scale queries with a softmax scale of 40: logits spread over tens of nats, so later key
@@ -163,17 +197,15 @@ def test_csa_prefill_128_heads(sharp):
     parity.check_csa(wl, host, step)
 
 
-@pytest.mark.parametrize("H", [64, 128])
-def test_single_role_bf16_kernels(H, monkeypatch):
-    # CSA_ATTEND_PP=0: the 4-wave bf16 kernel, 64 heads (two row groups, 64-key tiles) or 128
-    # heads (four row groups, three tile buffers, selection copied three tiles ahead).
-    monkeypatch.setenv("CSA_ATTEND_PP", "0")
-    wl = SMALL["C2"].replace(H=H, T=901, nq=901, k=160)
-    print(f"[parity] csa prefill single-role kernel H={H}", flush=True)
+def test_bf16_two_role_kernel_other_head_counts():
+    # The 64-head two-role kernel for 128 heads of a CSA prefill (two workgroups per query) and
+    # 64 heads of an HCA prefill (one per query), sharp logits.
+    wl = SMALL["C2"].replace(H=128, T=901, nq=901, k=160)
+    print("[parity] csa prefill 128 heads", flush=True)
     host, step = _run(wl, True, 23)
     parity.check_csa(wl, host, step)
-    wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=300, H=H)
-    print(f"[parity] hca prefill single-role kernel H={H}", flush=True)
+    wl = SMALL["C3"].replace(T=128 * 40 + 100, nq=300, H=64)
+    print("[parity] hca prefill 64 heads", flush=True)
     host, step = _run(wl, True, 24)
     parity.check_hca(wl, host, step)
 

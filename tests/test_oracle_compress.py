@@ -101,9 +101,50 @@ def test_e4m3_row_store():
     # The largest magnitude of each nonzero row maps exactly onto +-448.
     for r in (0, 1, 2, 4, 5):
         assert np.max(np.abs(q[r])) == 448.0
-        assert sigma[r] == np.float32(np.abs(e_c[r]).max() / 448.0)
+        # 448 sigma recovers the row's largest magnitude to fp32 rounding of the scale.
+        amax = np.abs(e_c[r]).max()
+        assert abs(448.0 * sigma[r] - amax) <= 2.0 ** -23 * amax
         # Relative error of a stored value is within half an e4m3 ulp (2^-4) plus the scale's.
         big = np.abs(e_c[r]) > 2.0 ** -6 * sigma[r]
         rel = np.abs(q[r] * sigma[r] - e_c[r])[big] / np.abs(e_c[r])[big]
         assert rel.max() <= 2.0 ** -4 + 1e-7
     assert sigma[3] == 0.0 and (q[3] == 0).all()
+
+
+# ---- projection (fp32 workload): x = hidden . W_x, g = hidden . W_g -------------------------
+# deepseek.csdn.net "一文搞懂 DeepSeek" section "V3 看家本领一：MLA": the cached latent is a
+# down-projection of the token's input; the gate logits come from a second projection.
+
+def test_project_hand_worked():
+    # Worked by hand: row 0 of x = 1*[1,0] + 2*[0,1] + 0*[2,3] = [1, 2];
+    # row 1 of x = 0*[1,0] + 1*[0,1] - 1*[2,3] = [-2, -2];
+    # row 0 of g = 1*[0,1] + 2*[1,0] + 0*[1,1] = [2, 1]; row 1 of g = [1,0] - [1,1] = [0, -1].
+    hidden = np.array([[1.0, 2.0, 0.0], [0.0, 1.0, -1.0]])
+    w_x = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 3.0]])
+    w_g = np.array([[0.0, 1.0], [1.0, 0.0], [1.0, 1.0]])
+    x, g = o.project(hidden, w_x, w_g)
+    assert x.tolist() == [[1.0, 2.0], [-2.0, -2.0]]
+    assert g.tolist() == [[2.0, 1.0], [0.0, -1.0]]
+
+
+def test_project_permutation_weights():
+    # W_x a 3-cycle permutation: column j of x is column pi(j) of hidden. A transposed weight
+    # gives the inverse cycle, and swapping W_x and W_g gives the other matrix: both fail.
+    hidden = _rand((5, 3), 30)
+    pi = [2, 0, 1]
+    w_x = np.zeros((3, 3))
+    for j, s in enumerate(pi):
+        w_x[s, j] = 1.0
+    w_g = 2.0 * np.eye(3)
+    x, g = o.project(hidden, w_x, w_g)
+    np.testing.assert_array_equal(x, hidden[:, pi])
+    np.testing.assert_array_equal(g, 2.0 * hidden)
+
+
+def test_project_brute_force_loops():
+    hidden, w_x, w_g = _rand((4, 6), 31), _rand((6, 3), 32), _rand((6, 3), 33)
+    x, g = o.project(hidden, w_x, w_g)
+    for t in range(4):
+        for c in range(3):
+            assert abs(x[t, c] - sum(hidden[t, i] * w_x[i, c] for i in range(6))) < 1e-13
+            assert abs(g[t, c] - sum(hidden[t, i] * w_g[i, c] for i in range(6))) < 1e-13
