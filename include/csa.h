@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
   CSA_OK = 0,
@@ -60,7 +60,11 @@ typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_E4M3 = 2 } csa_dtype;
  *          NULL iff d_r == 0.
  *   scale  [B][rows] fp32 dequantisation scale of c; required iff dtype_c == CSA_E4M3, else NULL.
  *          The dequantised row is (scale * c, r) ([jaylab] mixed-precision cache row).
- *   pos0   [B] int64 absolute position of row 0 (raw-token stores); NULL means 0. */
+ *   pos0   [B] int64 ring offset of a raw-token store; NULL means 0. A raw store is a ring:
+ *          position p of sequence b lives in row (p - pos0[b]) mod rows, so a store that holds
+ *          every position from pos0 on (rows >= positions held) reads row p - pos0, and a window
+ *          store of rows >= window rows is rolled by writing each new token over the oldest row
+ *          (csa_cache_append does), with no copy of the others. */
 typedef struct {
   const void* c;
   const void* r;
@@ -124,18 +128,26 @@ csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const fl
  * fp8 latent with a row scale, bf16 RoPE dims). For every sequence b, with its new token at the
  * absolute position p = pos[b] (int64, device, p >= 0):
  *   - stage_x[b][p % m] = x_new[b] and stage_g[b][p % m] = g_new[b], widened to fp32;
- *   - raw row p - raw_pos0[b] (raw_pos0 NULL: p) of `raw` = x_new[b], stored like a csa_compress
- *     output row (f32 / bf16 / e4m3 latent with sigma = max|latent| / 448; RoPE bf16, or f32 in
- *     an f32 store); not written when that row lies outside [0, raw->rows);
+ *   - raw ring row (p - raw_pos0[b]) mod raw->rows (raw_pos0 NULL: 0) of `raw` = x_new[b], stored
+ *     like a csa_compress output row (f32 / bf16 / e4m3 latent with sigma = max|latent| / 448;
+ *     RoPE bf16, or f32 in an f32 store). raw may be NULL (or have 0 rows): no raw row is stored.
+ *     With raw->rows >= the attention window this keeps the window of csa_attend current with
+ *     one row written per token;
  *   - when p + 1 is a multiple of m: entry row (p + 1) / m - 1 of `entries` = the pooling of the
- *     m staged rows of the block (csa_compress's e[j,c] = sum_i softmax_i(g[i,c] + bias[i]) x[i,c]),
- *     stored by the same rules; not written outside [0, entries->rows).
+ *     m staged rows of the block, bitwise the entry csa_compress builds from the same rows
+ *     (e[j,c] = sum_i softmax_i(g[i,c] + bias[i]) x[i,c], same arithmetic and order), stored by
+ *     the same rules; not written outside [0, entries->rows).
+ *   Indexer keys ([hongke] 4.1: a cache of their own; reading: pooled like the rows they index):
+ *     a second call with x_new = the token's indexer key, g_new = its gate logits, d_c = d_I,
+ *     d_r = 0, raw = NULL, and an E4M3 key store as `entries` keeps the csa_index key cache
+ *     (scale = its sigma_k) in step.
  *   x_new, g_new [B][d] in in_dtype (F32 or BF16), d = d_c + d_r <= 1024. bias [m] fp32.
  *   stage_x, stage_g [B][m][d] fp32: caller-owned staging ring, kept between calls (the rows of
  *     earlier positions of the open block must hold those tokens). Store rows are per sequence
  *     (batch stride rows); the raw store is the window store csa_attend reads with pos0 = raw_pos0.
- *   Errors: CSA_EINVAL for a bad dtype, m <= 0, B < 0, non-positive d_c, NULL arguments or store
- *     fields inconsistent with d_c / d_r / dtype; CSA_EUNSUPPORTED for d > 1024.
+ *   Errors: CSA_EINVAL for a bad dtype, m <= 0, B < 0, non-positive d_c, NULL arguments (other
+ *     than raw, raw_pos0) or store fields inconsistent with d_c / d_r / dtype; CSA_EUNSUPPORTED
+ *     for d > 1024.
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dtype,
                             const float* bias, int32_t m, int32_t B, const int64_t* pos,
@@ -161,17 +173,45 @@ csa_status csa_index(const csa_queries_t* Q, const void* q_i, const float* q_i_s
                      float* scores, int64_t ld_scores, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_index_mxfp4 -- the low-precision indexer: MXFP4 queries and keys, bf16 scores.
+ * [csdn] V4 的其他升级 (FP4 paragraph: the indexer's QK path in FP4 with fine-grained scales, which
+ * widen losslessly to FP8; index scores in BF16) and [jaylab] 其他技术细节 (FP4 for the indexer QK
+ * path). Same score as csa_index: s[i][j] = sum_h w[i][h] * max(0, qI[i][h] . kI[seq[i]][j]) for
+ * j < n_vis(pos[i]), stored as bf16 (round to nearest even of the fp32 value).
+ *   MXFP4 vectors (OCP Microscaling): E2M1 codes, two per byte, element 2e in the low nibble of
+ *   byte e; one E8M0 scale byte per 32 consecutive elements (value = E2M1 * 2^(scale - 127)).
+ *   q_i  [nq][H_I][d_I / 2] codes, q_i_scale [nq][H_I][d_I / 32] scales.
+ *   k_i  [B][N][d_I / 2] codes, k_i_scale [B][N][d_I / 32] scales.
+ *   w    [nq][H_I] fp32 head weights.
+ *   scores [nq][ld_scores] bf16 codes, ld_scores >= N; columns >= n_vis are not written.
+ *   Constraints: H_I == 8, d_I == 64 (CSA_EUNSUPPORTED otherwise); q_i and k_i 16-byte aligned.
+ *   Per-block dot products are exact (E2M1 products are exact); head sums fp32.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_index_mxfp4(const csa_queries_t* Q, const uint8_t* q_i, const uint8_t* q_i_scale,
+                           const float* w, int32_t H_I, int32_t d_I, const uint8_t* k_i,
+                           const uint8_t* k_i_scale, int32_t B, int64_t N, int32_t m,
+                           uint16_t* scores, int64_t ld_scores, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_topk -- per-query selection of the k highest-scoring visible entries.
  * [csdn] V4 改进一 and [yudong] 2.2 Step 3 (top-k; the pages use k = 64 and k = 1024).
  *   Among j < n_vis(pos[i]), order by score descending then index ascending (ties go to the lower
  *   index); take the first min(k, n_vis); write them to idx[i][0..) in ascending index order and
  *   pad with -1. -0.0 and +0.0 compare equal. Scores must not be NaN.
  *   scores [nq][ld_scores] fp32 (columns >= n_vis are not read); idx [nq][k] int32.
+ *   Rows longer than 32768 need k <= 2048 and ceil(N / 32768) * k <= 32768 (CSA_EUNSUPPORTED).
  *   Workspace: csa_topk_workspace_bytes(nq, N, k). Deterministic (integer work only).
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scores, int64_t N,
                     int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 size_t csa_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+
+/* csa_topk_bf16 -- csa_topk on bf16 scores (csa_index_mxfp4's output), same rule and workspace
+ * ([csdn] V4 的其他升级: bf16 index scores make the selection faster). scores [nq][ld_scores] bf16
+ * codes; ties (far more frequent at bf16's 8 significant bits) go to the lower index. */
+csa_status csa_topk_bf16(const csa_queries_t* Q, const uint16_t* scores, int64_t ld_scores,
+                         int64_t N, int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * csa_attend -- CSA attention: the selected entries plus the raw sliding window, one softmax.
@@ -183,8 +223,10 @@ size_t csa_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
  *     out[i][h] = sum p * c_key,  lse[i][h] = log sum exp(l)   (natural log).
  *   An empty key set gives out = 0, lse = -inf.
  *   q      [nq][H][d_c + d_r] in q_dtype (CSA_F32 with F32 stores, else CSA_BF16).
- *   entries, raw  stores with identical dtype_c, d_c, d_r; raw must hold every window position
- *          (row = pos - pos0[seq]).
+ *   entries, raw  stores with identical dtype_c, d_c, d_r; raw (a ring, see csa_kv_t) must hold
+ *          every window position of every query: positions pos - window + 1 .. pos must be among
+ *          the last raw->rows positions written to it. Selected slots holding a row at or past
+ *          entries->rows are skipped like -1 slots.
  *   out    [nq][H][d_c] fp32; lse [nq][H] fp32 (may be NULL).
  *   Workspace: csa_attend_workspace_bytes(nq, H, d_c, k + window).
  * ------------------------------------------------------------------------------------------- */
@@ -193,6 +235,29 @@ csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
                       const csa_kv_t* raw, int32_t window, float sm_scale, float* out,
                       float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t csa_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t max_keys);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_attend_tokens -- CSA attention over the original tokens of the selected blocks plus the
+ * raw window, one softmax (the token-selection variant).
+ * [hongke] 2.2 (item 3: fine-grained attention over the original tokens of each retrieved block)
+ * and [yudong] 2.2 Steps 3-4 (the top-1024 blocks stand for 4096 original tokens, attended in
+ * full); [csdn] V4 改进一 for the window and the MQA form.
+ *   Keys of query i: for each slot s of idx[i][0..k) holding a block j >= 0 (-1 slots skipped),
+ *   the raw rows of positions j*m .. j*m + m - 1 in that order; then the window positions
+ *   max(0, pos - window + 1) .. pos (no de-duplication). Logits, softmax, out and lse as in
+ *   csa_attend (K = [c; r], V = c).
+ *   raw    the store of raw token rows (dtype_c BF16 or E4M3 with scale; F32 with F32 q). Token
+ *          rows are read at row p - pos0[seq]: the store must hold every position of the selected
+ *          blocks and of the window without wrapping (rows > every such p - pos0); a token row
+ *          outside [0, rows) is skipped. The window follows the ring rule of csa_kv_t.
+ *   idx    [nq][k] int32 block indices of the m-fold compression (csa_topk's output).
+ *   Workspace: csa_attend_workspace_bytes(nq, H, d_c, k * m + window).
+ *   Errors: as csa_attend; CSA_EINVAL also when k * m + window exceeds 2^30.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_attend_tokens(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                             const csa_kv_t* raw, int32_t m, const int32_t* idx, int32_t k,
+                             int32_t window, float sm_scale, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * hca_attend -- HCA attention: dense attention over every visible m'-compressed entry.

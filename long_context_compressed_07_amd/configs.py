@@ -75,13 +75,14 @@ FULL = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
 
 # Scaled-down variants: same dtypes and layouts, sizes the oracle finishes in seconds, chosen to
 # span several kernel tiles and to leave ragged tails (T not a multiple of m, n_vis not a
-# multiple of any tile, k not a power of two where allowed).
+# multiple of any tile, k not a power of two where allowed), and, for the fp8 decode variants, key
+# lists long enough to be split over workgroups (584 CSA keys, 600 HCA entries: 2 splits each).
 SMALL = {
     "C1": C1.replace(name="csa_decode_f32_small", T=1027, d_model=256),
     "C2": C2.replace(name="csa_prefill_bf16_small", T=1502, nq=1502, k=96, window=40, H=64),
     "C3": C3.replace(name="hca_prefill_bf16_small", T=128 * 300 + 77, nq=37, H=128),
-    "C4": C4.replace(name="csa_decode_fp8_small", B=3, T=4 * 1500 + 2, k=200, window=64),
-    "C5": C5.replace(name="hybrid_decode_fp8_small", B=2, T=128 * 90 + 5, k=128, window=128),
+    "C4": C4.replace(name="csa_decode_fp8_small", B=3, T=4 * 1500 + 2, k=520, window=64),
+    "C5": C5.replace(name="hybrid_decode_fp8_small", B=2, T=128 * 600 + 5, k=128, window=128),
 }
 
 SEED_BASE = {"C1": 7001, "C2": 7002, "C3": 7003, "C4": 7004, "C5": 7005}

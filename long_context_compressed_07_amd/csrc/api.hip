@@ -145,11 +145,45 @@ csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scor
   if (k < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
   if (Q->nq > 0 && (scores == nullptr || idx == nullptr)) return fail(CSA_EINVAL, "null scores/idx");
   if (!csa::topk_supported(N, k))
-    return fail(CSA_EUNSUPPORTED, "rows longer than 8192 need k <= 2048 and N * k <= 2^28");
+    return fail(CSA_EUNSUPPORTED,
+                "rows longer than 32768 need k <= 2048 and ceil(N / 32768) * k <= 32768");
   const size_t need = csa::topk_workspace(Q->nq, N, k);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
-  csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, ld_scores, N, m, k, idx, ws, ws_bytes};
+  csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, 0, ld_scores, N, m, k, idx, ws,
+                  ws_bytes};
   return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_topk_bf16(const csa_queries_t* Q, const uint16_t* scores, int64_t ld_scores,
+                         int64_t N, int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (k < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
+  if (Q->nq > 0 && (scores == nullptr || idx == nullptr)) return fail(CSA_EINVAL, "null scores/idx");
+  if (!csa::topk_supported(N, k))
+    return fail(CSA_EUNSUPPORTED,
+                "rows longer than 32768 need k <= 2048 and ceil(N / 32768) * k <= 32768");
+  const size_t need = csa::topk_workspace(Q->nq, N, k);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
+  csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, 1, ld_scores, N, m, k, idx, ws,
+                  ws_bytes};
+  return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_index_mxfp4(const csa_queries_t* Q, const uint8_t* q_i, const uint8_t* q_i_scale,
+                           const float* w, int32_t H_I, int32_t d_I, const uint8_t* k_i,
+                           const uint8_t* k_i_scale, int32_t B, int64_t N, int32_t m,
+                           uint16_t* scores, int64_t ld_scores, void* stream) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (B < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
+  if (H_I != 8 || d_I != 64) return fail(CSA_EUNSUPPORTED, "the MXFP4 indexer takes 8 heads x 64");
+  if (Q->nq > 0 && (q_i == nullptr || q_i_scale == nullptr || w == nullptr || scores == nullptr))
+    return fail(CSA_EINVAL, "null query-side argument");
+  if (N > 0 && (k_i == nullptr || k_i_scale == nullptr)) return fail(CSA_EINVAL, "null keys");
+  if (((uintptr_t)q_i | (uintptr_t)k_i) & 15u) return fail(CSA_EINVAL, "q_i / k_i not 16-byte aligned");
+  csa::IndexFp4Args a{csa::Queries{Q->seq, Q->pos, Q->nq}, q_i, q_i_scale, w, k_i, k_i_scale, B,
+                      N, m, scores, ld_scores};
+  return hip_status(csa::launch_index_fp4(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t max_keys) {
@@ -187,6 +221,8 @@ csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
     if (csa_status st = check_store(raw, "raw")) return st;
     if (raw->dtype_c != entries->dtype_c || raw->d_c != entries->d_c || raw->d_r != entries->d_r)
       return fail(CSA_EINVAL, "raw and entries stores differ in dtype or dims");
+    if (raw->rows <= 0 && Q->nq > 0)
+      return fail(CSA_EINVAL, "a window needs a raw store with rows > 0");
   }
   const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, (int64_t)k + window);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
@@ -201,6 +237,39 @@ csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
   a.idx = idx;
   a.k = k;
   if (window > 0) a.raw = to_store(*raw);
+  a.window = window;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return hip_status(csa::launch_attend(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_attend_tokens(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,
+                             const csa_kv_t* raw, int32_t m, const int32_t* idx, int32_t k,
+                             int32_t window, float sm_scale, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (csa_status st = check_attend_common(Q, q, q_dtype, H, raw, m, out)) return st;
+  if (k < 0 || window < 0) return fail(CSA_EINVAL, "negative k or window");
+  if (k > 0 && Q->nq > 0 && idx == nullptr) return fail(CSA_EINVAL, "null idx");
+  if (raw->rows <= 0 && Q->nq > 0 && (k > 0 || window > 0))
+    return fail(CSA_EINVAL, "token selection needs a raw store with rows > 0");
+  if ((int64_t)k * m + window > (int64_t)1 << 30) return fail(CSA_EINVAL, "k * m + window too large");
+  const size_t need = csa::attend_workspace(Q->nq, H, raw->d_c, (int64_t)k * m + window);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
+  csa::AttendArgs a{};
+  a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.H = H;
+  a.ent = to_store(*raw);    // unused by token selection (every key is a raw row)
+  a.m = m;
+  a.dense = 0;
+  a.idx = idx;
+  a.k = k;
+  a.tok_m = m;
+  a.raw = to_store(*raw);
   a.window = window;
   a.sm_scale = sm_scale;
   a.out = out;
@@ -250,10 +319,11 @@ csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dty
   if (d_c + d_r > 1024) return fail(CSA_EUNSUPPORTED, "d_c + d_r > 1024");
   if (B == 0) return CSA_OK;
   if (x_new == nullptr || g_new == nullptr || bias == nullptr || pos == nullptr ||
-      stage_x == nullptr || stage_g == nullptr || entries == nullptr || raw == nullptr)
+      stage_x == nullptr || stage_g == nullptr || entries == nullptr)
     return fail(CSA_EINVAL, "null argument");
   const csa_kv_out_t* st[2] = {entries, raw};
   for (const csa_kv_out_t* o : st) {
+    if (o == nullptr) continue;   // no raw store
     if (!valid_dtype(o->dtype_c)) return fail(CSA_EINVAL, "bad store dtype");
     if (o->d_c != d_c || o->d_r != d_r) return fail(CSA_EINVAL, "store dims differ from d_c/d_r");
     if (o->rows < 0 || o->ld_c < d_c || (d_r > 0 && o->ld_r < d_r))
@@ -277,8 +347,9 @@ csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dty
   a.stage_g = stage_g;
   a.ent = csa::OutStore{entries->c, entries->r, entries->scale, entries->dtype_c, d_c, d_r,
                         entries->rows, entries->ld_c, entries->ld_r};
-  a.raw = csa::OutStore{raw->c, raw->r, raw->scale, raw->dtype_c, d_c, d_r, raw->rows, raw->ld_c,
-                        raw->ld_r};
+  if (raw != nullptr && raw->rows > 0)
+    a.raw = csa::OutStore{raw->c, raw->r, raw->scale, raw->dtype_c, d_c, d_r, raw->rows,
+                          raw->ld_c, raw->ld_r};
   a.raw_pos0 = raw_pos0;
   return hip_status(csa::launch_append(a, static_cast<hipStream_t>(stream)));
 }

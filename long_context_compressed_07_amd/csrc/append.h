@@ -16,8 +16,8 @@ struct AppendArgs {
   float* stage_x;           // [B][m][d] fp32 staging ring of the block being filled
   float* stage_g;
   OutStore ent;             // entry store (rows = entries per sequence)
-  OutStore raw;             // raw window store (rows = window rows per sequence)
-  const int64_t* raw_pos0;  // [B] position of raw row 0 (device), or null for 0
+  OutStore raw;             // raw store, a ring of rows per sequence (c == null: none)
+  const int64_t* raw_pos0;  // [B] ring offset: position p goes to row (p - pos0) mod rows; null: 0
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);

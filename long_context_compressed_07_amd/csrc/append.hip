@@ -5,14 +5,18 @@
 // yudonglee.me "DeepSeek-V4 详解" 2.2 Step 1 / 2.3 Step 1; jaylab-temp.pages.dev "DeepSeek-V4 —
 // 百万 Token 上下文的高效 MoE 模型" 其他技术细节 (cache rows: fp8 latent, bf16 RoPE dims). Reading: the
 // tokens of the block being filled wait in a caller-owned fp32 staging ring; the token that
-// completes a block turns it into that block's entry, pooled and stored exactly as csa_compress
-// pools and stores a block; the raw window row of the token is stored in the same row format.
+// completes a block turns it into that block's entry, pooled (pool.h: the arithmetic and order of
+// csa_compress, so the entry is bitwise the one csa_compress would build) and stored by the same
+// rules; the raw row of the token goes to the raw store, a ring addressed (p - pos0) mod rows, in
+// the same row format. Indexer keys (hongke120.com/20112.html 4.1 lists them as their own cache)
+// are maintained by a second call with d_r = 0, no raw store, and an e4m3 key store.
 //
 // One workgroup per sequence; thread t owns channels t, t + 256, ... of the row, so the pooled
 // value of a channel needs only that thread's registers and the staged rows of earlier calls.
 // The row maxima for the fp8 scales are reduced through LDS.
 #include "append.h"
-#include "common.h"
+#include "attend_keys.h"
+#include "pool.h"
 
 namespace csa {
 namespace {
@@ -46,8 +50,7 @@ __device__ __forceinline__ void store_value(const OutStore& o, int64_t row, int 
   } else if (o.dtype == CSA_BF16) {
     static_cast<uint16_t*>(o.c)[row * o.ld_c + c] = f32_to_bf16(v);
   } else {
-    static_cast<uint8_t*>(o.c)[row * o.ld_c + c] =
-        (uint8_t)(sigma > 0.0f ? f32_to_e4m3(__fdiv_rn(v, sigma)) : 0u);
+    static_cast<uint8_t*>(o.c)[row * o.ld_c + c] = e4m3_code(v, sigma);
   }
 }
 
@@ -59,8 +62,9 @@ __global__ void __launch_bounds__(kAppThreads) append_kernel(AppendArgs a) {
   const int64_t p = a.pos[b];
   const int slot = (int)(p % a.m);
   const bool close = (p + 1) % a.m == 0;
-  const int64_t rrow = p - (a.raw_pos0 != nullptr ? a.raw_pos0[b] : 0);
-  const bool raw_ok = rrow >= 0 && rrow < a.raw.rows;
+  const bool raw_ok = a.raw.c != nullptr && a.raw.rows > 0;
+  const int64_t rrow = raw_ok ? ring_row(p, a.raw_pos0 != nullptr ? a.raw_pos0[b] : 0, a.raw.rows)
+                              : 0;
   const int64_t erow = (p + 1) / a.m - 1;
   const bool ent_ok = close && erow >= 0 && erow < a.ent.rows;
   if (t < 2) s_amax[t] = 0u;
@@ -83,42 +87,27 @@ __global__ void __launch_bounds__(kAppThreads) append_kernel(AppendArgs a) {
   for (int u = 0; u < kAppMaxCh; ++u)
     if (t + u * kAppThreads < a.d_c) am_x = fmaxf(am_x, fabsf(xv[u]));
   if (ent_ok) {
-    // Phase 2: the block's pooling, per channel a softmax over its m positions of g + bias
-    // (max-subtracted) and the weighted sum of x; the new token's row comes from registers.
-    float mx[kAppMaxCh], den[kAppMaxCh], num[kAppMaxCh];
+    // Phase 2: the block's pooling in the shared order (chunks of 4 positions); the new token's
+    // row comes from registers, the earlier ones from the staging ring.
 #pragma unroll
     for (int u = 0; u < kAppMaxCh; ++u) {
-      mx[u] = gv[u] + a.bias[slot];
-      den[u] = 0.f;
-      num[u] = 0.f;
-    }
-    for (int i = 0; i < a.m; ++i) {
-      if (i == slot) continue;
-      const float bi = a.bias[i];
+      const int c = t + u * kAppThreads;
+      const int cc = c < d ? c : d - 1;
+      PoolAcc pa = pool_start();
+      for (int i0 = 0; i0 < a.m; i0 += 4) {
+        const int cnt = a.m - i0 < 4 ? a.m - i0 : 4;
+        float ai[4], xi[4];
 #pragma unroll
-      for (int u = 0; u < kAppMaxCh; ++u) {
-        const int c = t + u * kAppThreads;
-        const int cc = c < d ? c : d - 1;
-        mx[u] = fmaxf(mx[u], sg[(int64_t)i * d + cc] + bi);
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + (q < cnt ? q : 0);
+          const bool mine = i == slot;
+          ai[q] = (mine ? gv[u] : sg[(int64_t)i * d + cc]) + a.bias[i];
+          xi[q] = mine ? xv[u] : sx[(int64_t)i * d + cc];
+        }
+        pool_fold(pa, ai, xi, cnt);
       }
-    }
-    for (int i = 0; i < a.m; ++i) {
-      const float bi = a.bias[i];
-#pragma unroll
-      for (int u = 0; u < kAppMaxCh; ++u) {
-        const int c = t + u * kAppThreads;
-        const int cc = c < d ? c : d - 1;
-        const float gi = i == slot ? gv[u] : sg[(int64_t)i * d + cc];
-        const float xi = i == slot ? xv[u] : sx[(int64_t)i * d + cc];
-        const float w = __expf(gi + bi - mx[u]);
-        den[u] += w;
-        num[u] = fmaf(w, xi, num[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kAppMaxCh; ++u) {
-      ev[u] = num[u] / den[u];
-      if (t + u * kAppThreads < a.d_c) am_e = fmaxf(am_e, fabsf(ev[u]));
+      ev[u] = pool_value(pa);
+      if (c < a.d_c) am_e = fmaxf(am_e, fabsf(ev[u]));
     }
   }
   // Phase 3: the stores.
@@ -132,8 +121,8 @@ __global__ void __launch_bounds__(kAppThreads) append_kernel(AppendArgs a) {
   atomicMax(&s_amax[0], __float_as_uint(am_x));
   atomicMax(&s_amax[1], __float_as_uint(am_e));
   __syncthreads();
-  const float sig_x = __fdiv_rn(__uint_as_float(s_amax[0]), 448.0f);
-  const float sig_e = __fdiv_rn(__uint_as_float(s_amax[1]), 448.0f);
+  const float sig_x = e4m3_row_scale(__uint_as_float(s_amax[0]));
+  const float sig_e = e4m3_row_scale(__uint_as_float(s_amax[1]));
   const int64_t rg = (int64_t)b * a.raw.rows + rrow;
   const int64_t eg = (int64_t)b * a.ent.rows + erow;
   if (t == 0 && raw_ok && a.raw.dtype == CSA_E4M3) a.raw.scale[rg] = sig_x;

@@ -25,7 +25,8 @@ static bool force_generic() {
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.Q.nq == 0 || a.H == 0) return hipSuccess;
-  const int64_t max_keys = a.dense ? a.ent.rows : (int64_t)a.k + a.window;
+  const int64_t max_keys =
+      a.dense ? a.ent.rows : (int64_t)a.k * (a.tok_m > 0 ? a.tok_m : 1) + a.window;
   if (!force_generic() && attend_mfma_supported(a)) return launch_attend_mfma(a, max_keys, s);
   const int slot = a.dense ? 1 : 0;
   const int timed = timing_start(slot, s);

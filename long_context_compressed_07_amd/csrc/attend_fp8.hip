@@ -274,7 +274,7 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
     {
       const int64_t kk = t0 + (kAheadF8 + 3) * kTK + lane;
       dma.sel = (sel_dma && lane < kTK && kk < ke && kk < kl.n_sel)
-                    ? reinterpret_cast<const char*>(kl.sel + kk)
+                    ? reinterpret_cast<const char*>(kl.sel + sel_index(kl, kk))
                     : reinterpret_cast<const char*>(kZeroRow);
       const KeyAddr8* ad = s_addr[(it + kAheadF8) % kSlotsF8];
 #pragma unroll

@@ -469,25 +469,31 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
   }
 }
 
-// Work decomposition. bf16 caches with a multiple of 64 heads take the two-role DMA kernel
-// (attend_pp.hip): one workgroup per query and group of 64 heads. fp8 caches with a
-// multiple of 128 heads take the fp8 DMA kernel (attend_fp8.hip): one workgroup per query and
-// group of 128 heads. Everything else takes the fp16-staging kernel here: many queries (prefill)
-// give one workgroup per query and head group, 4 head groups sharing each staged tile (ksw 1) or
-// 2 head groups x 2 key halves (ksw 2); few queries (decode) take ksw 4, one 32-head group each.
-// When there are too few workgroups to fill the chip, each query's keys are also split over
-// workgroups (n_split), merged by combine_kernel.
+// Work decomposition (the split rule is make_plan's). bf16 caches with a multiple of 64 heads
+// take the two-role DMA kernel (attend_pp.hip): one workgroup per query and group of 64 heads.
+// fp8 caches with a multiple of 128 heads take the fp8 DMA kernel (attend_fp8.hip): one workgroup
+// per query and group of 128 heads. Everything else takes the fp16-staging kernel here: 4 head
+// groups sharing each staged tile (ksw 1), 2 head groups x 2 key halves (ksw 2) or one 32-head
+// group x 4 key quarters (ksw 4), by the head count. Each query's keys may also be split over
+// workgroups (n_split), merged by combine_kernel in split order.
 enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 
-MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
+// Split rule. The number of key splits per query depends only on the call's longest key list
+// (max_keys: k + window for CSA, the entry rows for HCA) and on the kernel, never on the number of
+// queries, and the merge takes the splits in a fixed order: a query's outputs are bitwise the same
+// whatever batch it is in and wherever in the batch it sits (deepseek.csdn.net "一文搞懂
+// DeepSeek", V4 的其他升级: deterministic, batch-invariant kernels). keys_per_split is the
+// kernel's granularity: fp8 (the decode cache) 256 keys, so that a 1152-key CSA list takes 4 splits
+// and an 8192-entry HCA list 32; bf16 (the prefill path, many queries per call) 8192, so that the
+// prefill workloads run unsplit; at most 64 splits.
+int splits_by_keys(int64_t max_keys, int64_t keys_per_split) {
+  const int64_t ns = max_keys / keys_per_split;
+  return (int)(ns < 1 ? 1 : (ns > 64 ? 64 : ns));
+}
+
+MfmaPlan make_plan(int H, int64_t max_keys, int kind) {
   MfmaPlan p{};
   const int groups32 = H / 32;
-  const int64_t cap = max_keys / 512 > 1 ? max_keys / 512 : 1;   // >= 512 keys per split
-  auto splits_for = [&](int64_t wgs_per_split, int64_t cap_) {
-    const int64_t wgs = (int64_t)nq * wgs_per_split;
-    const int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-    return (int)(ns < cap_ ? ns : cap_);
-  };
   if (kind == kPlanBf16 && groups32 % 2 == 0) {
     // 64-head workgroups with the two wave roles (attend_pp.hip) for every even number of 32-head
     // groups (measured on 128 heads: 8.3 vs 9.2 ms for the HCA prefill against a 4-wave kernel
@@ -495,29 +501,20 @@ MfmaPlan make_plan(int nq, int H, int64_t max_keys, int kind) {
     p.pp = 1;
     p.rg = 2;
     p.head_groups = groups32 / p.rg;
-    p.n_split = splits_for(p.head_groups, cap);
+    p.n_split = splits_by_keys(max_keys, 8192);
     return p;
   }
   if (kind == kPlanF8 && groups32 % 4 == 0) {
     p.f8_dma = 1;
     p.rg = 4;
     p.head_groups = groups32 / 4;
-    p.n_split = splits_for(p.head_groups, max_keys / 128 > 1 ? max_keys / 128 : 1);
+    p.n_split = splits_by_keys(max_keys, 256);
     return p;
   }
-  if (groups32 % 4 == 0 && (int64_t)nq * (groups32 / 4) >= 512) {
-    p.ksw = 1;
-    p.head_groups = groups32 / 4;
-    p.n_split = 1;
-  } else if (groups32 % 2 == 0 && (int64_t)nq * (groups32 / 2) >= 512) {
-    p.ksw = 2;
-    p.head_groups = groups32 / 2;
-    p.n_split = 1;
-  } else {
-    p.ksw = 4;
-    p.head_groups = groups32;
-    p.n_split = splits_for(p.head_groups, cap);
-  }
+  // fp16-staging kernel: as many 32-head groups per staged tile as the head count allows.
+  p.ksw = groups32 % 4 == 0 ? 1 : (groups32 % 2 == 0 ? 2 : 4);
+  p.head_groups = groups32 / (4 / p.ksw);
+  p.n_split = splits_by_keys(max_keys, 1024);
   return p;
 }
 
@@ -556,7 +553,7 @@ size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
   // The dtypes are not part of the workspace query: cover every plan kind.
   size_t part = 0, flags = 0;
   for (int kind = 0; kind < 3; ++kind) {
-    const MfmaPlan p = make_plan(nq, H, max_keys, kind);
+    const MfmaPlan p = make_plan(H, max_keys, kind);
     part = std::max(part, plan_partial_bytes(p, nq, H));
     flags = std::max(flags, plan_flag_bytes(p, nq));
   }
@@ -631,7 +628,7 @@ void timing_stop(int slot, int i, hipStream_t s) {
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.Q.nq, a.H, max_keys, plan_kind(a));
+  MfmaPlan p = make_plan(a.H, max_keys, plan_kind(a));
   if (p.n_split > 1) {
     p.ws_o = static_cast<_Float16*>(a.ws);
     p.ws_ml = reinterpret_cast<float*>(p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC);

@@ -52,8 +52,11 @@ __device__ __forceinline__ v2i lds_tr16(const char* p) {
 // key_code32 and key_addr as selects (no branches), so that the PV waves' code arithmetic can
 // be scheduled among their MFMAs.
 __device__ __forceinline__ int key_code_sel(const KeyCodes32& c, int kk, int raw) {
-  const int v = kk < c.n_sel ? (c.has_sel ? raw : kk) : ((kk + c.woff) | (1 << 30));
-  return (kk >= c.ke || raw < 0) ? -1 : v;
+  if (c.tok_m > 0) return key_code32(c, kk, raw);   // token selection: the general form
+  const int r = kk + c.woff;
+  const int v = kk < c.n_sel ? (c.has_sel ? raw : kk) : ((r < c.wrap ? r : r - c.wrap) | (1 << 30));
+  const bool empty = kk >= c.ke || raw < 0 || (kk < c.n_sel && c.has_sel && raw >= c.ent_rows);
+  return empty ? -1 : v;
 }
 
 __device__ __forceinline__ KeyAddr key_addr_sel(const RowBases& rb, int code) {
@@ -221,7 +224,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       {
         const int64_t kk = t0 + 5 * TK + lane;
         dma.sel = (sel_dma && lane < TK && kk < ke && kk < kl.n_sel)
-                      ? reinterpret_cast<const char*>(kl.sel + kk)
+                      ? reinterpret_cast<const char*>(kl.sel + sel_index(kl, kk))
                       : reinterpret_cast<const char*>(kZeroRow);
         const KeyAddr* ad = s_addr[(i + 2) % kPpBuf];
         const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
@@ -332,7 +335,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       for (int j = 0; j < 3; ++j) {
         const int kk = (int)k0 + j * TK + kl32;
         const int32_t* src = (sel_dma && kk < kc.ke && kk < kc.n_sel)
-                                 ? kl.sel + kk
+                                 ? kl.sel + sel_index(kl, kk)
                                  : reinterpret_cast<const int32_t*>(kZeroRow);
         raw[j] = *src;
       }

@@ -84,7 +84,7 @@ template <int TK>
 __device__ __forceinline__ void dma_sel(const KeyList& kl, int64_t kk0, int64_t ke, int* dst) {
   const int lane = threadIdx.x & 63;
   const int64_t kk = kk0 + lane;
-  const void* src = (lane < TK && kk < ke && kk < kl.n_sel) ? (const void*)(kl.sel + kk)
+  const void* src = (lane < TK && kk < ke && kk < kl.n_sel) ? (const void*)(kl.sel + sel_index(kl, kk))
                                                            : (const void*)kZeroRow;
   __builtin_amdgcn_global_load_lds(src, (lds_char*)dst, 4, 0, 0);
 }
@@ -198,22 +198,40 @@ __device__ __forceinline__ void dma_tile(const KeyAddr* addr, char* buf, int w =
   }
 }
 
-// key_code_of in 32-bit arithmetic, for the tile loops (key indices and rows fit in 31 bits).
+// Key codes in 32-bit arithmetic, for the tile loops (key indices and rows fit in 31 bits): the
+// row of key kk in its store, with bit 30 set for the raw (window) store, or -1 for an empty slot.
 struct KeyCodes32 {
   int ke;        // end of this workgroup's key range
   int n_sel;     // entry slots before the window rows
-  int woff;      // raw row of window key kk: kk + woff
+  int woff;      // ring row of window key kk: kk + woff, less wrap when that reaches wrap
+  int wrap;      // raw-store rows (the ring length)
+  int ent_rows;  // entry-store rows: selected slots at or past it are empty
   int has_sel;   // 1: entry slots map through the selection
+  int tok_m;     // token selection: tokens per selected block (0: the slots are entries)
+  int tok_base;  // token selection: raw row of position p is p + tok_base
 };
 
 __device__ __forceinline__ KeyCodes32 key_codes32(const KeyList& kl, int64_t ke) {
-  return {(int)ke, (int)kl.n_sel, (int)(kl.wlo - kl.n_sel - kl.raw_base), kl.sel != nullptr};
+  return {(int)ke, (int)kl.n_sel, (int)(kl.w_row0 - kl.n_sel), (int)kl.raw_rows,
+          (int)(kl.ent_rows < 0x40000000 ? kl.ent_rows : 0x40000000), kl.sel != nullptr,
+          (int)kl.tok_m, (int)kl.tok_base};
+}
+
+// Raw row of token kk (kk < n_sel) of selected block `blk` in token selection, or -1.
+__device__ __forceinline__ int token_row32(const KeyCodes32& c, int kk, int blk) {
+  const int64_t r = (int64_t)blk * c.tok_m + kk % c.tok_m + c.tok_base;
+  return r >= 0 && r < c.wrap ? (int)r : -1;
 }
 
 __device__ __forceinline__ int key_code32(const KeyCodes32& c, int kk, int raw) {
   if (kk >= c.ke || raw < 0) return -1;
-  if (kk < c.n_sel) return c.has_sel ? raw : kk;
-  return (kk + c.woff) | (1 << 30);
+  if (kk < c.n_sel && c.tok_m > 0) {
+    const int r = token_row32(c, kk, raw);
+    return r < 0 ? -1 : r | (1 << 30);
+  }
+  if (kk < c.n_sel) return c.has_sel ? (raw < c.ent_rows ? raw : -1) : kk;
+  const int r = kk + c.woff;
+  return (r < c.wrap ? r : r - c.wrap) | (1 << 30);
 }
 
 // S^T[32 keys x 32 heads] = K . Q^T over the 36 k-steps of a 576-dim row, as one instruction

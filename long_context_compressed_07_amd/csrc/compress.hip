@@ -7,11 +7,11 @@
 //
 // pool_kernel streams x and g once (HBM-bound): one thread owns VEC consecutive channels of one
 // entry (16-byte loads, consecutive threads on consecutive channels of a row) and folds the m
-// positions in chunks of 4 with a running max, so each element costs 1 + 1/4 exponentials.
+// positions in chunks of 4 with a running max (pool.h, the order every pooling kernel shares).
 // project_pool_kernel is the fp32 projection mode: x = hidden * w_x and g = hidden * w_g are
 // formed tile by tile in LDS and pooled in registers, so x and g never reach HBM (only the raw x
 // rows the sliding window needs are written).
-#include "common.h"
+#include "pool.h"
 
 namespace csa {
 namespace {
@@ -69,8 +69,7 @@ __device__ void store_entry(const OutStore& o, int64_t b, int64_t j, int ch, con
   } else {
     uint8_t* p = static_cast<uint8_t*>(o.c) + row * o.ld_c + ch;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v)
-      p[v] = (uint8_t)(sigma > 0.0f ? f32_to_e4m3(__fdiv_rn(e[v], sigma)) : 0u);
+    for (int v = 0; v < VEC; ++v) p[v] = e4m3_code(e[v], sigma);
   }
 }
 
@@ -88,13 +87,14 @@ __global__ void __launch_bounds__(256) pool_kernel(CompressArgs a, int cpr, int 
   const int ch = cv * VEC;
   if (tid < rows_per_wg) s_amax[tid] = 0u;
 
-  float acc[VEC], sum[VEC], mx[VEC];
+  float acc[VEC];
   int64_t b = 0, j = 0;
   if (active) {
     b = gr / nb;
     j = gr - b * nb;
+    PoolAcc pa[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) { acc[v] = 0.f; sum[v] = 0.f; mx[v] = -INFINITY; }
+    for (int v = 0; v < VEC; ++v) pa[v] = pool_start();
     const int64_t base = (b * a.T + j * a.m) * d + ch;
     for (int i0 = 0; i0 < a.m; i0 += 4) {
       float xv[4][VEC], av[4][VEC];
@@ -111,28 +111,13 @@ __global__ void __launch_bounds__(256) pool_kernel(CompressArgs a, int cpr, int 
       }
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        float cm = av[0][v];
-#pragma unroll
-        for (int p = 1; p < 4; ++p)
-          if (p < cnt) cm = fmaxf(cm, av[p][v]);
-        const float nm = fmaxf(mx[v], cm);
-        const float c1 = __expf(mx[v] - nm);
-        float s = sum[v] * c1, ac = acc[v] * c1;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (p < cnt) {
-            const float e = __expf(av[p][v] - nm);
-            s += e;
-            ac = fmaf(e, xv[p][v], ac);
-          }
-        }
-        sum[v] = s;
-        acc[v] = ac;
-        mx[v] = nm;
+        const float ai[4] = {av[0][v], av[1][v], av[2][v], av[3][v]};
+        const float xi[4] = {xv[0][v], xv[1][v], xv[2][v], xv[3][v]};
+        pool_fold(pa[v], ai, xi, cnt);
       }
     }
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = __fdiv_rn(acc[v], sum[v]);
+    for (int v = 0; v < VEC; ++v) acc[v] = pool_value(pa[v]);
   }
   float sigma = 0.f;
   if (a.out.dtype == CSA_E4M3) {
@@ -145,7 +130,7 @@ __global__ void __launch_bounds__(256) pool_kernel(CompressArgs a, int cpr, int 
     }
     __syncthreads();
     if (active) {
-      sigma = __fdiv_rn(__uint_as_float(s_amax[lr]), 448.0f);
+      sigma = e4m3_row_scale(__uint_as_float(s_amax[lr]));
       if (cv == 0) a.out.scale[b * a.out.rows + j] = sigma;
     }
   }
@@ -222,15 +207,16 @@ __global__ void __launch_bounds__(256) project_pool_kernel(CompressArgs a) {
     float e[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float mxv = -INFINITY;
-      for (int i = 0; i < m; ++i) mxv = fmaxf(mxv, ag[blk * m + i][c] + a.bias[i]);
-      float s = 0.f, acc = 0.f;
-      for (int i = 0; i < m; ++i) {
-        const float w = __expf(ag[blk * m + i][c] + a.bias[i] - mxv);
-        s += w;
-        acc = fmaf(w, ax[blk * m + i][c], acc);
+      float ai[4], xi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = blk * m + (i < m ? i : 0);
+        ai[i] = ag[t][c] + a.bias[i < m ? i : 0];
+        xi[i] = ax[t][c];
       }
-      e[c] = __fdiv_rn(acc, s);
+      PoolAcc pa = pool_start();
+      pool_fold(pa, ai, xi, m);
+      e[c] = pool_value(pa);
     }
     store_entry<4>(a.out, b, tb / m, ch, e, 0.f);
   }

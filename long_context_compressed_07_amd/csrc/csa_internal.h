@@ -74,10 +74,28 @@ struct IndexArgs {
 };
 hipError_t launch_index(const IndexArgs& a, hipStream_t s);
 
+// MXFP4 indexer with bf16 scores (index_fp4.hip): E2M1 codes, two per byte (low nibble first),
+// with one E8M0 scale per 32 values; d_I = 64, H_I = 8.
+struct IndexFp4Args {
+  Queries Q;
+  const uint8_t* q_i;        // [nq][8][32] packed codes
+  const uint8_t* q_i_scale;  // [nq][8][2]
+  const float* w;            // [nq][8]
+  const uint8_t* k_i;        // [B][N][32]
+  const uint8_t* k_i_scale;  // [B][N][2]
+  int B;
+  int64_t N;
+  int m;
+  uint16_t* scores;          // [nq][ld_scores] bf16
+  int64_t ld_scores;
+};
+hipError_t launch_index_fp4(const IndexFp4Args& a, hipStream_t s);
+
 // ---- top-k ---------------------------------------------------------------------------------
 struct TopkArgs {
   Queries Q;
-  const float* scores;
+  const void* scores;   // fp32, or bf16 codes when bf16 != 0
+  int bf16;
   int64_t ld_scores;
   int64_t N;
   int m;
@@ -108,6 +126,7 @@ struct AttendArgs {
   int dense;            // 1: HCA, every visible entry is a key; 0: CSA, the k slots of idx
   const int32_t* idx;   // [nq][k] selected entries (CSA); unused when dense or k == 0
   int k;
+  int tok_m;            // > 0: token selection, each slot's block contributes its tok_m raw rows
   Store raw;            // raw.c == NULL or window == 0: no window
   int window;
   float sm_scale;

@@ -3,9 +3,10 @@
 // Method: deepseek.csdn.net "一文搞懂 DeepSeek" V4 改进一 and yudonglee.me "DeepSeek-V4 详解" 2.2
 // Step 2 (lightning indexer, FP8 accelerated); score s = sum_h w_h ReLU(qI_h . kI_j).
 //
-// index_bf16_mfma_kernel (many queries, bf16): a workgroup takes 32 consecutive queries of one
-// sequence; rows of the contraction are (query, head) pairs, 4 queries x 8 heads per 32-row
-// MFMA tile, columns are entries. The rows are ordered so that in the 32x32 output tile a lane
+// index_bf16_mfma_kernel (bf16, any number of queries): a workgroup takes 32 consecutive queries
+// (a prefill's are of one sequence; queries of several sequences take one pass per sequence);
+// rows of the contraction are (query, head) pairs, 4 queries x 8 heads per 32-row MFMA tile,
+// columns are entries. The rows are ordered so that in the 32x32 output tile a lane
 // holds all 8 heads of two queries for one entry: the ReLU-weighted head sum stays in registers.
 // Entry blocks of 128 rows are staged once in LDS and read as B fragments by all four waves. Only
 // visible entries (j < n_vis of each query) are computed and written.
@@ -29,52 +30,36 @@ constexpr int kRowK = 64 + 8;   // LDS row stride of a staged key (bf16 elements
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ void index_one_query_generic(const IndexArgs& a, int qi) {
-  const int64_t b = a.Q.seq[qi];
-  const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
-  for (int64_t j = threadIdx.x; j < nv; j += blockDim.x) {
-    float s = 0.f;
-    for (int h = 0; h < a.H_I; ++h) {
-      float dot = 0.f;
-      for (int e = 0; e < a.d_I; ++e)
-        dot = fmaf(load_vec(a.q_i, a.dtype, ((int64_t)qi * a.H_I + h) * a.d_I + e),
-                   load_vec(a.k_i, a.dtype, (b * a.N + j) * a.d_I + e), dot);
-      s = fmaf(a.w[(int64_t)qi * a.H_I + h], fmaxf(dot, 0.f), s);
-    }
-    a.scores[(int64_t)qi * a.ld_scores + j] = s;
-  }
-}
-
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// MULTI = false: workgroups whose queries all belong to one sequence (every prefill workgroup),
+// one pass; the others return at once. MULTI = true: the others, one pass per distinct sequence
+// (a separate kernel: the pass loop costs registers the single pass does not need). Both compute
+// every score with the same MFMA contraction and the same head-sum order.
+template <bool MULTI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MULTI ? 2 : 3, MULTI ? 2 : 3)))
 index_bf16_mfma_kernel(IndexArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kE * kRowK];
   __shared__ float s_w[kQ * 8];
-  __shared__ int64_t s_nv[kQ];
-  __shared__ int s_uniform;
+  __shared__ int s_nv[kQ];      // visible entries of each query (N < 2^31)
+  __shared__ int s_seq[kQ];
+  __shared__ int s_pass[3];   // sequence, query mask and entry count of the current pass
   // The last query blocks first: under causality they see the most entries, and starting them
   // first shortens the tail of the grid.
   const int q0 = (gridDim.x - 1 - blockIdx.x) * kQ;
   const int nqw = a.Q.nq - q0 < kQ ? a.Q.nq - q0 : kQ;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, hi = lane >> 5;
-  const int64_t b = a.Q.seq[q0];
-  if (tid == 0) s_uniform = 1;
-  __syncthreads();
-  if (tid < nqw) {
-    if (a.Q.seq[q0 + tid] != b) s_uniform = 0;
-    s_nv[tid] = n_visible(a.Q.pos[q0 + tid], a.m, a.N);
-  } else if (tid < kQ) {
-    s_nv[tid] = 0;
+  if (tid < kQ) {
+    s_nv[tid] = tid < nqw ? (int)n_visible(a.Q.pos[q0 + tid], a.m, a.N) : 0;
+    s_seq[tid] = tid < nqw ? a.Q.seq[q0 + tid] : -1;
   }
   for (int i = tid; i < kQ * 8; i += 256)
     s_w[i] = (i / 8) < nqw ? a.w[(int64_t)(q0 + i / 8) * 8 + (i % 8)] : 0.f;
   __syncthreads();
-  if (!s_uniform) {  // queries of several sequences: no shared key blocks
-    for (int qq = 0; qq < nqw; ++qq) index_one_query_generic(a, q0 + qq);
-    return;
+  {
+    bool uniform = true;
+    for (int i = 1; i < nqw; ++i) uniform = uniform && s_seq[i] == s_seq[0];
+    if (uniform == MULTI) return;   // uniform across the workgroup
   }
-  int64_t nmax = 0;
-  for (int i = 0; i < kQ; ++i) nmax = s_nv[i] > nmax ? s_nv[i] : nmax;
 
   // A fragments: wave w owns queries q0 + 8 w + [0, 8) as two 32-row tiles. Row r of a tile
   // holds head 4 ((r >> 3) & 1) + (r & 3) of query 2 ((r >> 2) & 1) + (r >> 4), so that in the
@@ -94,57 +79,97 @@ index_bf16_mfma_kernel(IndexArgs a) {
       af[rt][s] = as_bf16x8(v);
     }
   }
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_i) + b * a.N * 64;
-  // Entries [e0, e0 + 128): 128 rows x 128 bytes, 16 bytes per thread-task; the next block's
-  // loads are issued before the current block's MFMAs, so their latency hides behind them.
-  uint4 pre[4];
-  auto load_block = [&](int64_t e0) {
+  __syncthreads();
+  // One pass: stage sequence b's key blocks and write the scores of the queries in `cur`.
+  auto pass = [&](int64_t b, uint32_t cur, int nmax) {
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_i) + b * a.N * 64;
+    // Entries [e0, e0 + 128): 128 rows x 128 bytes, 16 bytes per thread-task; the next block's
+    // loads are issued before the current block's MFMAs, so their latency hides behind them.
+    uint4 pre[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int t = tid + 256 * it;
-      const int r = t >> 3, c = t & 7;
-      pre[it] = e0 + r < a.N ? *reinterpret_cast<const uint4*>(kbase + (e0 + r) * 64 + 8 * c)
-                             : make_uint4(0u, 0u, 0u, 0u);
+      const int r = (tid + 256 * it) >> 3, c = tid & 7;
+      pre[it] = r < a.N ? *reinterpret_cast<const uint4*>(kbase + (int64_t)r * 64 + 8 * c)
+                        : make_uint4(0u, 0u, 0u, 0u);
     }
-  };
-  load_block(0);
-  for (int64_t e0 = 0; e0 < nmax; e0 += kE) {
+    for (int e0 = 0; e0 < nmax; e0 += kE) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = tid + 256 * it;
-      const int r = t >> 3, c = t & 7;
-      *reinterpret_cast<uint4*>(s_k + r * kRowK + 8 * c) = pre[it];
-    }
-    __syncthreads();
-    if (e0 + kE < nmax) load_block(e0 + kE);
+      for (int it = 0; it < 4; ++it) {
+        const int t = tid + 256 * it;
+        const int r = t >> 3, c = t & 7;
+        *reinterpret_cast<uint4*>(s_k + r * kRowK + 8 * c) = pre[it];
+      }
+      __syncthreads();
+      if (e0 + kE < nmax) {
 #pragma unroll
-    for (int ct = 0; ct < kE / 32; ++ct) {
-      if (e0 + 32 * ct >= nmax) break;
-      bf16x8 bfr[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        bfr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(s_k + (32 * ct + (lane & 31)) * kRowK +
-                                                           16 * s + 8 * hi));
-      const int64_t ent = e0 + 32 * ct + (lane & 31);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        floatx16 acc = floatx16{};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][s], bfr[s], acc, 0, 0, 0);
-        // acc[8 u + e] = head e of query 8 w + 4 rt + 2 hi + u (u = 0, 1), entry `ent`.
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int ql = 8 * w + 4 * rt + 2 * hi + u;
-          const float* wq = s_w + ql * 8;
-          float p = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p = fmaf(wq[e], fmaxf(acc[8 * u + e], 0.f), p);
-          if (ql < nqw && ent < s_nv[ql]) a.scores[(int64_t)(q0 + ql) * a.ld_scores + ent] = p;
+        for (int it = 0; it < 4; ++it) {
+          const int r = e0 + kE + ((tid + 256 * it) >> 3), c = tid & 7;
+          pre[it] = r < a.N ? *reinterpret_cast<const uint4*>(kbase + (int64_t)r * 64 + 8 * c)
+                            : make_uint4(0u, 0u, 0u, 0u);
         }
       }
+#pragma unroll
+      for (int ct = 0; ct < kE / 32; ++ct) {
+        if (e0 + 32 * ct >= nmax) break;
+        bf16x8 bfr[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bfr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(s_k + (32 * ct + (lane & 31)) * kRowK +
+                                                             16 * s + 8 * hi));
+        const int ent = e0 + 32 * ct + (lane & 31);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          floatx16 acc = floatx16{};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][s], bfr[s], acc, 0, 0, 0);
+          // acc[8 u + e] = head e of query 8 w + 4 rt + 2 hi + u (u = 0, 1), entry `ent`.
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int ql = 8 * w + 4 * rt + 2 * hi + u;
+            const float* wq = s_w + ql * 8;
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p = fmaf(wq[e], fmaxf(acc[8 * u + e], 0.f), p);
+            if (((cur >> ql) & 1u) && ent < s_nv[ql])
+              a.scores[(int64_t)(q0 + ql) * a.ld_scores + ent] = p;
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
+  };
+  if constexpr (!MULTI) {
+    int nm = 0;
+    for (int i = 0; i < kQ; ++i) nm = s_nv[i] > nm ? s_nv[i] : nm;
+    pass(__builtin_amdgcn_readfirstlane(s_seq[0]), ~0u, __builtin_amdgcn_readfirstlane(nm));
+  } else {
+    // One pass per distinct sequence among the workgroup's queries.
+    // done: bit qq set once query qq is written (queries past nqw count as written).
+    uint32_t done = nqw < kQ ? ~0u << nqw : 0u;
+    while (done != ~0u) {
+      if (tid == 0) {
+        int first = 0;
+        while ((done >> first) & 1u) ++first;
+        const int bs = s_seq[first];
+        uint32_t mask = 0u;
+        int nm = 0;
+        for (int i = 0; i < kQ; ++i)
+          if (!((done >> i) & 1u) && s_seq[i] == bs) {
+            mask |= 1u << i;
+            nm = s_nv[i] > nm ? s_nv[i] : nm;
+          }
+        s_pass[0] = bs;
+        s_pass[1] = (int)mask;
+        s_pass[2] = nm;
+      }
+      __syncthreads();
+      // Uniform values: kept in scalar registers, so the key addressing stays scalar.
+      const uint32_t cur = (uint32_t)__builtin_amdgcn_readfirstlane(s_pass[1]);
+      pass(__builtin_amdgcn_readfirstlane(s_pass[0]), cur, __builtin_amdgcn_readfirstlane(s_pass[2]));
+      done |= cur;
+      __syncthreads();   // s_pass is rewritten by the next pass
+    }
   }
 }
 
@@ -228,8 +253,10 @@ __global__ void __launch_bounds__(256) index_fp8_stream_kernel(IndexArgs a, int6
 bool index_fast(const IndexArgs& a, hipStream_t s, hipError_t* err) {
   if (a.H_I != 8 || a.d_I != 64) return false;
   if (((uintptr_t)a.q_i | (uintptr_t)a.k_i) & 15u) return false;   // 16-byte vector loads
-  if (a.dtype == CSA_BF16 && a.Q.nq >= 64) {
-    index_bf16_mfma_kernel<<<(unsigned)((a.Q.nq + kQ - 1) / kQ), 256, 0, s>>>(a);
+  if (a.dtype == CSA_BF16) {
+    const unsigned grid = (unsigned)((a.Q.nq + kQ - 1) / kQ);
+    index_bf16_mfma_kernel<false><<<grid, 256, 0, s>>>(a);
+    index_bf16_mfma_kernel<true><<<grid, 256, 0, s>>>(a);
     *err = hipGetLastError();
     return true;
   }

@@ -17,18 +17,22 @@
 // give every segment its output offset; selected positions are staged in LDS and written out with
 // coalesced stores.
 //
-// Rows of up to kChunk visible entries: one workgroup per row. Longer rows: stage 1 runs the same
-// selection on chunks of kChunk entries (many workgroups per row) and writes each chunk's local
-// top-k (ascending); stage 2 selects the row's top-k among the concatenated candidates. The union
-// of the chunks' top-k contains the row's top-k under the same tie rule, so the result is exact.
-// Every chunk before a row's last visible one holds kChunk >= k entries and so yields exactly k
-// candidates: a row's candidates are the first n slots of its [chunks][k] block, in entry order.
+// Rows of up to kChunk (8192) visible entries: one 256-thread workgroup per row. Rows of up to
+// kWideChunk (32768): one 1024-thread workgroup per row (the same code, 32 keys per thread).
+// Longer rows: stage 1 runs the same selection on chunks of kWideChunk entries (several
+// 1024-thread workgroups per row) and writes each chunk's local top-k (ascending); stage 2
+// selects the row's top-k among the concatenated candidates, with the 256-thread form when they
+// fit in it. The union of the chunks' top-k contains the row's top-k under the same tie rule, so
+// the result is exact. Every chunk before a row's last visible one holds kWideChunk >= k entries
+// and so yields exactly k candidates: a row's candidates are the first n slots of its [chunks][k]
+// block, in entry order.
 #include "common.h"
 
 namespace csa {
 namespace {
 
-constexpr int kChunk = 8192;      // entries per stage-1 chunk (and single-stage limit)
+constexpr int kChunk = 8192;      // single-stage limit of the 256-thread row kernel
+constexpr int kWideChunk = 32768; // 1024-thread row kernel limit and entries per stage-1 chunk
 constexpr int kCandMax = 32768;   // candidates per row in stage 2
 constexpr int kPer = 32;          // keys per thread
 constexpr int kBins = 2048;       // LDS ints per histogram (11-bit digits); two per workgroup
@@ -352,6 +356,12 @@ __device__ void compact(const uint32_t (&kv)[kPer], uint32_t K, int need_eq, int
   lds_sync();
 }
 
+// Score value of element j of a row: fp32, or bf16 (widened exactly to fp32).
+__device__ __forceinline__ float score_at(const float* row, int64_t j) { return row[j]; }
+__device__ __forceinline__ float score_at(const uint16_t* row, int64_t j) {
+  return __uint_as_float((uint32_t)row[j] << 16);
+}
+
 // Loads keys [PER t, PER t + PER) of a row of n scores (0 beyond n): 16-byte loads for whole,
 // aligned segments, element by element only for the segment holding the row's end.
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[kPer]) {
@@ -370,6 +380,28 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv
     const int m = n - j0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
+  }
+}
+
+// bf16 scores: 16-byte loads of 8 codes; each code is the high half of its fp32 value.
+__device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (&kv)[kPer]) {
+  const int j0 = threadIdx.x * kPer;
+  const uint16_t* src = row + j0;
+  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+#pragma unroll
+    for (int q = 0; q < kPer / 8; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        kv[8 * q + 2 * h] = score_key(__uint_as_float(w[h] << 16));
+        kv[8 * q + 2 * h + 1] = score_key(__uint_as_float(w[h] & 0xffff0000u));
+      }
+    }
+  } else {
+    const int m = n - j0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? score_key(score_at(src, i)) : 0u;
   }
 }
 
@@ -393,12 +425,12 @@ __device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_
   }
 }
 
-// Single stage: one workgroup per query row (n_vis <= kChunk = NT * kPer). Six waves per SIMD (at
-// most 80 VGPRs, no spills): 370 -> 336 us for 32768 rows of up to 8192 scores against five.
-template <int NT>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 6)))
+// Single stage: one workgroup per query row (n_vis <= NT * kPer). For 256 threads, six waves per
+// SIMD (at most 80 VGPRs, no spills): 370 -> 336 us for 32768 rows of up to 8192 scores against
+// five.
+template <int NT, typename S>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 6 : 4, NT == 256 ? 6 : 4)))
 topk_row_kernel(TopkArgs a) {
-  static_assert(NT * kPer == kChunk, "one key segment per thread");
   __shared__ int s_tmp[2 * NT / kWave + 2];
   __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
   const int qi = blockIdx.x;
@@ -409,7 +441,7 @@ topk_row_kernel(TopkArgs a) {
     return;
   }
   uint32_t kv[kPer];
-  load_keys(a.scores + (int64_t)qi * a.ld_scores, n, kv);
+  load_keys(static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores, n, kv);
   clear_hist(s_hist, NT);
   lds_sync();
   int need_eq;
@@ -424,25 +456,25 @@ topk_row_kernel(TopkArgs a) {
 
 // Stage 1: chunk c of query row qi; writes the chunk's local top-k (or all of its visible
 // entries) as (key, index) pairs in ascending index order.
-template <int NT>
+template <int NT, typename S>
 __global__ void __launch_bounds__(NT) topk_chunk_kernel(TopkArgs a, int n_chunks,
                                                         uint32_t* cand_key, int32_t* cand_idx) {
-  static_assert(NT * kPer == kChunk, "one key segment per thread");
+  constexpr int kChunkN = NT * kPer;   // entries per chunk: one key segment per thread
   __shared__ int s_tmp[2 * NT / kWave + 2];
   __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
   const int qi = blockIdx.x / n_chunks;
   const int c = blockIdx.x - qi * n_chunks;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
-  const int64_t base = (int64_t)c * kChunk;
+  const int64_t base = (int64_t)c * kChunkN;
   const int64_t slot = (int64_t)qi * n_chunks + c;
   int32_t* oi = cand_idx + slot * a.k;
   uint32_t* ok = cand_key + slot * a.k;
-  const int n = base >= nv ? 0 : (int)(nv - base < kChunk ? nv - base : kChunk);
-  const float* row = a.scores + (int64_t)qi * a.ld_scores + base;
+  const int n = base >= nv ? 0 : (int)(nv - base < kChunkN ? nv - base : kChunkN);
+  const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores + base;
   if (n <= a.k) {
     for (int j = threadIdx.x; j < n; j += NT) {
       oi[j] = (int32_t)(base + j);
-      ok[j] = score_key(row[j]);
+      ok[j] = score_key(score_at(row, j));
     }
     return;
   }
@@ -476,8 +508,8 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
   int n = 0;
   if (nv > 0) {
-    const int64_t last = (nv - 1) / kChunk;
-    const int64_t in_last = nv - last * kChunk;
+    const int64_t last = (nv - 1) / kWideChunk;
+    const int64_t in_last = nv - last * kWideChunk;
     n = (int)(last * a.k + (in_last < a.k ? in_last : a.k));
   }
   const int32_t* cidx = cand_idx + (int64_t)qi * n_chunks * a.k;
@@ -490,7 +522,7 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   clear_hist(s_hist, NT);
   lds_sync();
   int need_eq;
-  const uint32_t K = kth_key<NT, false>(kv, a.k, s_hist, s_tmp, &need_eq);
+  const uint32_t K = kth_key<NT, NT == 256>(kv, a.k, s_hist, s_tmp, &need_eq);
   compact<NT>(kv, K, need_eq, a.k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = j; });
   // Entry indices of the selected candidates, gathered eight at a time.
   for (int i0 = 0; i0 < a.k; i0 += 8 * NT) {
@@ -509,38 +541,42 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   }
 }
 
-int n_chunks_for(int64_t N) { return (int)((N + kChunk - 1) / kChunk); }
+int n_chunks_for(int64_t N) { return (int)((N + kWideChunk - 1) / kWideChunk); }
 
 }  // namespace
 
 size_t topk_workspace(int nq, int64_t N, int k) {
-  if (N <= kChunk) return 0;
+  if (N <= kWideChunk) return 0;
   const int nc = n_chunks_for(N);
   return (size_t)nq * nc * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
 bool topk_supported(int64_t N, int k) {
-  return N <= kChunk || (k <= kMaxK && (int64_t)n_chunks_for(N) * k <= kCandMax);
+  return N <= kWideChunk || (k <= kMaxK && (int64_t)n_chunks_for(N) * k <= kCandMax);
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.Q.nq == 0) return hipSuccess;
+namespace {
+
+template <typename S>
+hipError_t launch_topk_t(const TopkArgs& a, hipStream_t s) {
   if (a.N <= kChunk) {
-    topk_row_kernel<256><<<a.Q.nq, 256, 0, s>>>(a);
+    topk_row_kernel<256, S><<<a.Q.nq, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (a.N <= kWideChunk) {
+    topk_row_kernel<1024, S><<<a.Q.nq, 1024, 0, s>>>(a);
     return hipGetLastError();
   }
   const int nc = n_chunks_for(a.N);
   uint32_t* cand_key = static_cast<uint32_t*>(a.ws);
   int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_key + (size_t)a.Q.nq * nc * a.k);
-  topk_chunk_kernel<256><<<(unsigned)((int64_t)a.Q.nq * nc), 256, 0, s>>>(a, nc, cand_key,
-                                                                         cand_idx);
+  topk_chunk_kernel<1024, S><<<(unsigned)((int64_t)a.Q.nq * nc), 1024, 0, s>>>(a, nc, cand_key,
+                                                                              cand_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Stage 2 block size: kPer candidate keys per thread.
   const int64_t cand = (int64_t)nc * a.k;
-  if (cand <= 128 * kPer) {
-    topk_merge_kernel<128><<<a.Q.nq, 128, 0, s>>>(a, nc, cand_key, cand_idx);
-  } else if (cand <= 256 * kPer) {
+  if (cand <= 256 * kPer) {
     topk_merge_kernel<256><<<a.Q.nq, 256, 0, s>>>(a, nc, cand_key, cand_idx);
   } else if (cand <= 512 * kPer) {
     topk_merge_kernel<512><<<a.Q.nq, 512, 0, s>>>(a, nc, cand_key, cand_idx);
@@ -548,6 +584,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     topk_merge_kernel<1024><<<a.Q.nq, 1024, 0, s>>>(a, nc, cand_key, cand_idx);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.Q.nq == 0) return hipSuccess;
+  return a.bf16 ? launch_topk_t<uint16_t>(a, s) : launch_topk_t<float>(a, s);
 }
 
 }  // namespace csa

@@ -13,6 +13,10 @@ the projection weights) and cast to the storage dtype:
   * e4m3 rows: codes = e4m3(clip(z, +-3.9) * 112) (never saturates), one fp32 scale per row
     drawn from the same stream as (sigma / 112) * U(0.75, 1.25), so the dequantised rows have
     std ~ sigma.
+  * MXFP4 rows (the low-precision indexer): float32 draws cast per block of 32 consecutive values
+    to a shared power-of-two scale 2^(floor(log2 amax) - 2) (E8M0 code) and E2M1 codes of
+    value / scale, round to nearest even with saturation to +-6 (the OCP MX conversion), two
+    codes per byte, low nibble first.
 "Sharp" inputs (parity only) draw q with std 1 and gate logits and bias with std 1; used with
 sm_scale = 1 they give attention logits of std ~1 instead of ~1/d.
 """
@@ -60,6 +64,31 @@ def _e4m3_rows(rng: np.random.Generator, shape, std: float):
     u = rng.uniform(0.75, 1.25, size=shape[:-1]).astype(np.float32)
     scale = (np.float32(std / 112.0) * u).astype(np.float32)
     return codes, scale
+
+
+def to_mxfp4(x: np.ndarray):
+    """float32 [..., d] (d % 32 == 0) -> (packed E2M1 codes uint8 [..., d/2], E8M0 scales uint8
+    [..., d/32]): the storage cast of MXFP4 rows."""
+    x = np.asarray(x, dtype=np.float32)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32)).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    y = np.abs(blk) / np.ldexp(1.0, e)[..., None]
+    # nearest E2M1 magnitude, ties to the even fraction bit: steps of 0.5 below 2, 1 below 4, 2 up
+    # to 6 (saturating)
+    q = np.where(y < 2, np.rint(2 * y) / 2, np.where(y < 4, np.rint(y), 2 * np.rint(y / 2)))
+    q = np.minimum(q, 6.0)
+    mag_code = np.select([q == v for v in (0, .5, 1, 1.5, 2, 3, 4, 6)], np.arange(8), 0)
+    code = (mag_code + 8 * ((blk < 0) & (q > 0))).astype(np.uint8)
+    code = code.reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
+def mxfp4_rows(rng: np.random.Generator, shape, std: float):
+    """MXFP4 rows of Gaussian draws with the given std: (packed codes, scales)."""
+    return to_mxfp4(_normal(rng, shape, std))
 
 
 def _vec(wl_dtype: str, rng, shape, std):

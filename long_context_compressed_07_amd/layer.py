@@ -3,8 +3,9 @@
 `Step(wl, host_inputs)` uploads the storage-format inputs (from `inputs.make_inputs`) to the GPU,
 allocates every output and workspace once, and `run()` enqueues the whole hot path on the current
 stream: compress (when it is part of the workload) -> index -> top-k -> attend for CSA, compress ->
-dense attend for HCA, both layers for the hybrid decode. Only marshalling happens here; every step
-runs in the library's kernels.
+dense attend for HCA, both layers for the hybrid decode (the HCA layer on a second stream, since
+it depends on none of the CSA layer's results). Only marshalling and stream ordering happen here;
+every step runs in the library's kernels.
 """
 from __future__ import annotations
 
@@ -80,6 +81,11 @@ class Step:
             self.hca_lse = torch.empty((self.nq, wl.H), **f32)
             need = lib.hca_attend_workspace_bytes(self.nq, wl.H, d_c, nh)
             self.ws["hca"] = torch.empty(max(need, 1), dtype=torch.uint8, device=self.dev)
+            # The HCA layer reads nothing the CSA layer writes: it runs on a second stream (default
+            # priority, like every stream here) beside the CSA index, top-k and attention.
+            self._side = torch.cuda.Stream(device=self.dev)
+            self._fork = torch.cuda.Event()
+            self._join = torch.cuda.Event()
 
     def _given_store(self, pfx: str, rows: int, pos0=None) -> lib.Store:
         wl = self.wl
@@ -126,16 +132,24 @@ class Step:
                            self.hca_lse, ws=self.ws["hca"])
 
     def run(self):
-        """Enqueue one whole step of the workload's hot path."""
+        """Enqueue one whole step of the workload's hot path on the current stream (the hybrid
+        decode's HCA layer on a second stream that the current one waits for at the end)."""
         wl = self.wl
         if wl.kind == "hca_prefill":
             self.compress()
             self.hca()
             return
+        if wl.kind == "hybrid_decode":
+            main = torch.cuda.current_stream(self.dev)
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            with torch.cuda.stream(self._side):
+                self.hca()
+            self._join.record(self._side)
         if wl.compress_on_path:
             self.compress()
         self.index()
         self.topk()
         self.attend()
         if wl.kind == "hybrid_decode":
-            self.hca()
+            main.wait_event(self._join)

@@ -26,7 +26,7 @@ EXPORTS = ("csa_compress", "csa_index", "csa_topk", "csa_topk_workspace_bytes", 
            "csa_attend_workspace_bytes", "hca_attend", "hca_attend_workspace_bytes",
            "csa_status_str", "csa_last_error", "csa_abi_version", "csa_kernel_timing_enable",
            "csa_kernel_timing_read", "csa_peak_mfma_bf16", "csa_peak_sink_floats",
-           "csa_cache_append")
+           "csa_cache_append", "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16")
 
 
 class KV(ctypes.Structure):
@@ -64,10 +64,15 @@ def load(path: str = LIB_PATH):
                               vp, i64, vp]
     lib.csa_topk.argtypes = [P(Queries), vp, i64, i64, i32, i32, vp, vp, sz, vp]
     lib.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
+    lib.csa_topk_bf16.argtypes = [P(Queries), vp, i64, i64, i32, i32, vp, vp, sz, vp]
+    lib.csa_index_mxfp4.argtypes = [P(Queries), vp, vp, vp, i32, i32, vp, vp, i32, i64, i32, vp,
+                                    i64, vp]
     lib.csa_attend.argtypes = [P(Queries), vp, i32, i32, P(KV), i32, vp, i32, P(KV), i32, f32,
                                vp, vp, vp, sz, vp]
     lib.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i64]
     lib.hca_attend.argtypes = [P(Queries), vp, i32, i32, P(KV), i32, f32, vp, vp, vp, sz, vp]
+    lib.csa_attend_tokens.argtypes = [P(Queries), vp, i32, i32, P(KV), i32, vp, i32, i32, f32,
+                                      vp, vp, vp, sz, vp]
     lib.hca_attend_workspace_bytes.argtypes = [i32, i32, i32, i64]
     lib.csa_kernel_timing_enable.argtypes = [i32]
     lib.csa_kernel_timing_read.argtypes = [i32, P(ctypes.c_double), P(i32)]
@@ -77,7 +82,8 @@ def load(path: str = LIB_PATH):
                                      P(KVOut), vp, vp]
     for fn in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend",
                "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read",
-               "csa_peak_mfma_bf16", "csa_peak_sink_floats", "csa_cache_append"):
+               "csa_peak_mfma_bf16", "csa_peak_sink_floats", "csa_cache_append",
+               "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16"):
         getattr(lib, fn).restype = ctypes.c_int32
     for fn in ("csa_topk_workspace_bytes", "csa_attend_workspace_bytes",
                "hca_attend_workspace_bytes"):
@@ -153,17 +159,19 @@ def _queries(seq: torch.Tensor, pos: torch.Tensor) -> Queries:
 
 
 def csa_cache_append(x_new, g_new, in_dtype: int, bias, m: int, pos, d_c: int, d_r: int,
-                     stage_x, stage_g, entries: Store, raw: Store, raw_pos0=None, stream=None):
-    """One new token per sequence: staging ring, raw window row, and the entry of a completed
-    block (csa_cache_append in include/csa.h)."""
+                     stage_x, stage_g, entries: Store, raw: Optional[Store], raw_pos0=None,
+                     stream=None):
+    """One new token per sequence: staging ring, raw ring row (raw may be None), and the entry of
+    a completed block (csa_cache_append in include/csa.h)."""
     lib = load()
     if pos.dtype != torch.int64 or (raw_pos0 is not None and raw_pos0.dtype != torch.int64):
         raise ValueError("pos and raw_pos0 must be int64")
-    e, r = entries.as_out(), raw.as_out()
+    e = entries.as_out()
+    r = raw.as_out() if raw is not None else None
     _check(lib.csa_cache_append(_ptr(x_new), _ptr(g_new), in_dtype, _ptr(bias), m, pos.numel(),
                                 _ptr(pos), d_c, d_r, _ptr(stage_x), _ptr(stage_g),
-                                ctypes.byref(e), ctypes.byref(r), _ptr(raw_pos0),
-                                _stream(stream)), "csa_cache_append")
+                                ctypes.byref(e), ctypes.byref(r) if r is not None else None,
+                                _ptr(raw_pos0), _stream(stream)), "csa_cache_append")
 
 
 def csa_compress(x, g, in_dtype: int, bias, m: int, B: int, T: int, d_c: int, d_r: int,
@@ -203,6 +211,32 @@ def csa_topk(seq, pos, scores, idx, N: int, m: int, k: int, ld_scores: Optional[
                         0 if ws is None else ws.numel(), _stream(stream)), "csa_topk")
 
 
+def csa_index_mxfp4(seq, pos, q_i, q_i_scale, w, k_i, k_i_scale, scores, H_I: int, d_I: int,
+                    B: int, N: int, m: int, ld_scores: Optional[int] = None, stream=None):
+    """MXFP4 indexer with bf16 scores (csa_index_mxfp4 in include/csa.h); scores are int16/uint16
+    (bf16 codes) or torch.bfloat16."""
+    lib = load()
+    Q = _queries(seq, pos)
+    ld = N if ld_scores is None else ld_scores
+    _check(lib.csa_index_mxfp4(ctypes.byref(Q), _ptr(q_i), _ptr(q_i_scale), _ptr(w), H_I, d_I,
+                               _ptr(k_i), _ptr(k_i_scale), B, N, m, _ptr(scores), ld,
+                               _stream(stream)), "csa_index_mxfp4")
+
+
+def csa_topk_bf16(seq, pos, scores, idx, N: int, m: int, k: int,
+                  ld_scores: Optional[int] = None, ws: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Top-k on bf16 scores (csa_topk_bf16 in include/csa.h)."""
+    lib = load()
+    Q = _queries(seq, pos)
+    need = lib.csa_topk_workspace_bytes(Q.nq, N, k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ld = N if ld_scores is None else ld_scores
+    _check(lib.csa_topk_bf16(ctypes.byref(Q), _ptr(scores), ld, N, m, k, _ptr(idx), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(stream)), "csa_topk_bf16")
+
+
 def csa_attend_workspace_bytes(nq: int, H: int, d_c: int, max_keys: int) -> int:
     return load().csa_attend_workspace_bytes(nq, H, d_c, max_keys)
 
@@ -225,6 +259,23 @@ def csa_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m: int, idx, k
                           ctypes.byref(r) if r is not None else None, window, sm_scale,
                           _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(stream)), "csa_attend")
+
+
+def csa_attend_tokens(seq, pos, q, q_dtype: int, H: int, raw: Store, m: int, idx, k: int,
+                      window: int, sm_scale: float, out, lse=None,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    """Attention over the m raw tokens of each selected block plus the window
+    (csa_attend_tokens in include/csa.h)."""
+    lib = load()
+    Q = _queries(seq, pos)
+    need = lib.csa_attend_workspace_bytes(Q.nq, H, raw.d_c, k * m + window)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    r = raw.as_c()
+    _check(lib.csa_attend_tokens(ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(r), m,
+                                 _ptr(idx), k, window, sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)),
+           "csa_attend_tokens")
 
 
 def hca_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m_prime: int,

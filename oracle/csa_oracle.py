@@ -138,6 +138,32 @@ def index_scores(q_i: np.ndarray, w: np.ndarray, k_i: np.ndarray, n_vis: int) ->
     return s
 
 
+def store_scores_bf16(s: np.ndarray) -> np.ndarray:
+    """Storage step of the low-precision indexer's scores: round each visible score to bf16
+    (nearest, ties to even); invisible entries stay -inf.
+
+    [csdn] V4 的其他升级 (FP4 paragraph): with the indexer's QK path in FP4, the index scores drop
+    to BF16. The scores themselves are index_scores() of the dequantised MXFP4 vectors (an E2M1
+    value times its block's power-of-two scale is exact in float64).
+    """
+    s = np.asarray(s, np.float64)
+    out = s.copy()
+    fin = np.isfinite(s)
+    out[fin] = bf16_round(s[fin])
+    return out
+
+
+def recall(sel: np.ndarray, ref: np.ndarray) -> float:
+    """Fraction of the reference selection's entries (-1 slots ignored) that a selection keeps:
+    the "KV recall" by which [csdn] V4 的其他升级 rates the low-precision indexer (99.7%)."""
+    ref = np.asarray(ref)
+    ref = ref[ref >= 0]
+    if ref.size == 0:
+        return 1.0
+    sel = np.asarray(sel)
+    return float(np.isin(ref, sel[sel >= 0]).mean())
+
+
 # --------------------------------------------------------------------------------------------
 # a5. Per-query top-k
 # --------------------------------------------------------------------------------------------
@@ -213,19 +239,19 @@ def kv_rows(c: np.ndarray, r: np.ndarray | None, scale: np.ndarray | None, rows:
 
 
 def window_rows(pos: int, window: int, pos0: int, n_rows: int) -> np.ndarray:
-    """Row numbers, in a raw-row store whose row 0 holds position pos0, of the sliding window.
+    """Row numbers, in a raw-row store, of the sliding window of a query at position pos.
 
     [csdn] V4 改进一: besides the selected rows, CSA keeps a short stretch of the most recent raw
     KV uncompressed. Reading: the window is positions [max(0, pos - window + 1), pos], the query's
-    own token included; every one of them must be held by the store.
+    own token included. The store is a ring of n_rows rows: position p sits in row
+    (p - pos0) mod n_rows (a store holding every position from pos0 on is the case without wrap;
+    a window store rolls by overwriting its oldest row). The window must fit in the ring.
     """
     lo = max(0, int(pos) - int(window) + 1)
     p = np.arange(lo, int(pos) + 1) if window > 0 else np.arange(0)
-    rows = p - int(pos0)
-    if rows.size and (rows.min() < 0 or rows.max() >= n_rows):
-        raise ValueError("window position not held by the raw store")
-    return rows
-
+    if p.size > n_rows:
+        raise ValueError("the window is longer than the raw store's ring")
+    return np.mod(p - int(pos0), int(n_rows)) if p.size else p
 
 def csa_attend_one(q, entries, idx_row, raw, pos: int, window: int, sm_scale: float):
     """CSA attention of one query: selected entries plus the raw sliding window, one softmax.
@@ -246,6 +272,31 @@ def csa_attend_one(q, entries, idx_row, raw, pos: int, window: int, sm_scale: fl
     keys = np.concatenate([k1, k2], axis=0)
     vals = np.concatenate([v1, v2], axis=0)
     return softmax_attention(q, keys, vals, sm_scale)
+
+
+def csa_attend_tokens_one(q, raw, idx_row, m: int, pos: int, window: int, sm_scale: float):
+    """Token-selection CSA attention of one query: the original tokens of the selected blocks plus
+    the raw sliding window, one softmax.
+
+    [hongke] 2.2 (item 3): after retrieval, attention runs at token granularity over the original
+    tokens of each selected block; [yudong] 2.2 Steps 3-4: the top 1024 blocks stand for 4096
+    original tokens, attended in full. Readings: block j (a slot of idx_row, -1 = empty) covers
+    positions j*m .. j*m + m - 1, taken in that order; the window follows as in csa_attend_one,
+    with no de-duplication; keys [c; r], values c. raw is a (c, r, scale, pos0) store holding
+    every position it is asked for at row p - pos0.
+    """
+    rc, rr, rs, rpos0 = raw
+    n_rows = np.asarray(rc).shape[0]
+    sel = np.asarray(idx_row, dtype=np.int64)
+    sel = sel[sel >= 0]
+    tok = (sel[:, None] * int(m) + np.arange(int(m))[None, :]).reshape(-1) - int(rpos0)
+    if tok.size and (tok.min() < 0 or tok.max() >= n_rows):
+        raise ValueError("a selected token is not held by the raw store")
+    k1, v1 = kv_rows(rc, rr, rs, tok)
+    wr = window_rows(pos, window, rpos0, n_rows)
+    k2, v2 = kv_rows(rc, rr, rs, wr)
+    return softmax_attention(q, np.concatenate([k1, k2], axis=0),
+                             np.concatenate([v1, v2], axis=0), sm_scale)
 
 
 def hca_attend_one(q, entries, pos: int, m_prime: int, sm_scale: float):

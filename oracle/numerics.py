@@ -13,6 +13,12 @@ Formats
   magnitude 1.75 * 2^8 = 448, smallest normal 2^-6, subnormal step 2^-9. Conversion here is
   RNE with saturation to +-448 ("satfinite"), the mode used for the fp8 KV cache rows.
 
+* E2M1 (OCP Microscaling (MX) specification, "FP4"): 1 sign bit, 2 exponent bits (bias 1), 1
+  fraction bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; no infinities or NaN. Two
+  codes per byte, element 2i in the low nibble of byte i.
+* E8M0 (the same specification's shared scale): an 8-bit biased exponent, value 2^(code - 127);
+  code 255 is NaN. One scale multiplies each block of 32 consecutive E2M1 elements (MXFP4).
+
 The mixed-precision cache row (RoPE dims in bf16, the rest in fp8) is described on
 jaylab-temp.pages.dev "DeepSeek-V4 — 百万 Token 上下文的高效 MoE 模型", section 其他技术细节
 (KV cache 混合精度); the per-row fp32 scale is this library's reading of that row format.
@@ -107,3 +113,40 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 def f32_round(x: np.ndarray) -> np.ndarray:
     """Round float64 to the nearest float32 (RNE) and return it as float64."""
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _e2m1_table() -> np.ndarray:
+    """Value of each of the 16 E2M1 codes."""
+    vals = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        s = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        f = code & 0x1
+        vals[code] = s * (f / 2.0) if e == 0 else s * (1.0 + f / 2.0) * 2.0 ** (e - 1)
+    return vals
+
+
+E2M1_VALUES = _e2m1_table()
+
+
+def fp4_unpack(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] holding two E2M1 codes each -> codes uint8 [..., 2n] (low nibble first)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & np.uint8(0x0F)
+    out[..., 1::2] = p >> np.uint8(4)
+    return out
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 E8M0 codes -> float64 2^(code - 127) (NaN for 255)."""
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def mxfp4_decode(packed: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """MXFP4 rows -> float64: packed E2M1 codes [..., d/2] and E8M0 scales [..., d/block]; element
+    i of a row is E2M1(code_i) * 2^(scale[i // block] - 127)."""
+    v = E2M1_VALUES[fp4_unpack(packed)]
+    sc = e8m0_decode(scales)
+    return v * np.repeat(sc, block, axis=-1)

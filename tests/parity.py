@@ -39,6 +39,12 @@ def check_compress(wl: Workload, host: dict, step, sample_blocks: int | None = N
             x, g = orc.project(hid, host["w_x"], host["w_g"])
             raw_gpu = to_np(step.raw_x)[b].astype(np.float64)
             assert rel_err(raw_gpu, x) <= 1e-5, "projected raw rows"
+            # fp32 projection error (recursive summation over d_model terms: n 2^-24 sum |h w|)
+            # of the pooling's inputs x and g; an error dg in a gate logit moves the entry by at
+            # most max|x| |dg| (the softmax weights' derivative is below 1).
+            un = wl.d_model * 2.0 ** -24
+            dx = un * (np.abs(hid) @ np.abs(host["w_x"].astype(np.float64)))
+            dg = un * (np.abs(hid) @ np.abs(host["w_g"].astype(np.float64)))
         for j0 in range(0, len(blocks), 256):
             bl = blocks[j0:j0 + 256]
             rows = (bl[:, None] * m + np.arange(m)[None, :]).reshape(-1)
@@ -54,6 +60,9 @@ def check_compress(wl: Workload, host: dict, step, sample_blocks: int | None = N
             # (covers cancellation when the pooled value is far smaller than its inputs).
             xmax = np.abs(xs).reshape(len(bl), m, -1).max(axis=1)
             fp32_abs = 8.0 * m * 2.0 ** -24 * xmax
+            if wl.d_model:
+                fp32_abs = fp32_abs + dx[rows].reshape(len(bl), m, -1).max(axis=1) + \
+                    2.0 * xmax * dg[rows].reshape(len(bl), m, -1).max(axis=1)
             if wl.kv_dtype == "bf16":
                 # Half a bf16 ulp of the exact value (RNE of the fp32 result) plus fp32 error.
                 bound = BF16_ULP_REL * np.abs(e) + fp32_abs

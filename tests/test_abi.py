@@ -36,7 +36,7 @@ def test_header_declares_the_five_ops():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == 2
     assert L.csa_status_str(0) == b"ok"
     assert L.csa_status_str(3) == b"workspace too small"
 
@@ -132,3 +132,34 @@ def test_cache_append_validation(L):
     assert call(d_c=1024, d_r=64, ent=out(d_c=1024, ld_c=1024),
                 raw=out(d_c=1024, ld_c=1024)) == 2             # d > 1024
     assert call(B=0) == 0                                      # nothing to do
+
+
+def test_attend_tokens_validation(L):
+    Q = _q()
+    raw = _kv(rows=1000)
+    args = lambda r, k=4, w=8, m=4, idx=0x600: (ctypes.byref(Q), 0x500, 1, 64, ctypes.byref(r),
+                                                m, idx, k, w, 0.1, 0x700, None, None, 0, None)
+    assert L.csa_attend_tokens(*args(raw, idx=None)) == 1           # k > 0 without idx
+    assert L.csa_attend_tokens(*args(raw, k=-1)) == 1
+    assert L.csa_attend_tokens(*args(raw, m=0)) == 1
+    assert L.csa_attend_tokens(*args(_kv(rows=0))) == 1             # no token rows
+    assert L.csa_attend_tokens(*args(raw, k=1 << 20, m=4096)) == 1  # key list too long
+    assert L.csa_attend_tokens(*args(_kv(rows=1000, scale=0x9))) == 1   # scale on bf16 rows
+
+
+def test_attend_window_needs_raw_rows(L):
+    Q = _q()
+    args = (ctypes.byref(Q), 0x500, 1, 64, ctypes.byref(_kv()), 4, 0x600, 4,
+            ctypes.byref(_kv(rows=0)), 8, 0.1, 0x700, None, None, 0, None)
+    assert L.csa_attend(*args) == 1
+
+
+def test_cache_append_without_raw_store(L):
+    # Indexer-key maintenance: d_r = 0 and no raw store. Validation passes; B = 0 enqueues
+    # nothing, so no device memory is touched.
+    e = lib.KVOut(0x100, None, 0x300, 2, 64, 0, 10, 64, 0)
+    assert L.csa_cache_append(0x10, 0x20, 1, 0x30, 4, 0, 0x40, 64, 0, 0x50, 0x60,
+                              ctypes.byref(e), None, None, None) == 0
+    bad = lib.KVOut(0x100, None, None, 2, 64, 0, 10, 64, 0)     # e4m3 key store without scales
+    assert L.csa_cache_append(0x10, 0x20, 1, 0x30, 4, 1, 0x40, 64, 0, 0x50, 0x60,
+                              ctypes.byref(bad), None, None, None) == 1

@@ -3,8 +3,11 @@
 Each sequence appends T tokens one decode step at a time, starting at its own position (mid-block
 starts have the open block's earlier tokens pre-staged, as earlier calls would have left them).
 Afterwards the entry store must hold the oracle's pooling of every completed block (the same
-`compress` and storage rules that pin csa_compress), the raw window store the stored tokens at
-rows pos - pos0 (rows outside the store untouched), and the staging ring the open block's tokens.
+`compress` and storage rules that pin csa_compress), the raw window store (a ring) the last tokens
+at rows (pos - pos0) mod rows, and the staging ring the open block's tokens. Entries built by
+append are bitwise those csa_compress builds from the same rows. A decode loop keeps the fp8 KV
+and indexer-key caches by append and runs index -> top-k -> attend after every token, across
+block closes and wraps of the window ring, against the oracle.
 """
 import numpy as np
 import pytest
@@ -131,14 +134,11 @@ def test_cache_append_matches_oracle(in_dtype, ent_dtype, raw_dtype, m, T, p0):
         _check_rows(ent_dtype, got_e[b, rows], None if sc_e is None else sc_e[b, rows], e)
         untouched = np.setdiff1d(np.arange(n_ent), rows)
         assert (got_e[b, untouched] == 0).all()
-        # Raw rows: positions p0 + 4 .. p0 + 4 + window - 1 (the later ones fall past the store).
-        toks = np.arange(p0[b], p0[b] + T)
-        rr = toks - (p0[b] + 4)
-        keep = (rr >= 0) & (rr < window)
-        want_r = x64[b, pre[b] + np.nonzero(keep)[0]]
-        _check_rows(raw_dtype, got_r[b, rr[keep]], None if sc_r is None else sc_r[b, rr[keep]],
-                    want_r)
-        assert keep.sum() == window or (got_r[b, rr[keep].max() + 1:] == 0).all()
+        # Raw ring: the last min(T, window) tokens at rows (p - pos0) mod window.
+        toks = np.arange(max(p0[b], p0[b] + T - window), p0[b] + T)
+        rr = np.mod(toks - (p0[b] + 4), window)
+        want_r = x64[b, pre[b] + (toks - p0[b])]
+        _check_rows(raw_dtype, got_r[b, rr], None if sc_r is None else sc_r[b, rr], want_r)
         # Staging ring: the open block's tokens, exact in fp32.
         last = p0[b] + T - 1
         open_start = last - last % m
@@ -146,3 +146,145 @@ def test_cache_append_matches_oracle(in_dtype, ent_dtype, raw_dtype, m, T, p0):
         for p in range(open_start, last + 1):
             s = p - start
             assert (st_x[p % m] == f32_round(x64[b, s])).all()
+
+
+@pytest.mark.parametrize("m,ent_dtype", [(4, lib.E4M3), (4, lib.BF16), (128, lib.E4M3),
+                                         (128, lib.BF16)])
+def test_append_bitwise_equals_compress(m, ent_dtype):
+    # Tokens appended one at a time from position 0 build the same entry rows, bit for bit, as
+    # csa_compress over the whole prefix (one shared pooling arithmetic and order).
+    B, nblk = 2, 5
+    T = m * nblk + m // 2
+    rng = np.random.default_rng(77 + m)
+    xb = to_bf16_bits(_normal(rng, (B, T, D), 1.0 / np.sqrt(D)))
+    gb = to_bf16_bits(_normal(rng, (B, T, D), 1.0))
+    bias = torch.from_numpy(_normal(rng, (m,), 1.0 / np.sqrt(m))).cuda()
+    x_dev = torch.from_numpy(xb.view(np.int16)).cuda()
+    g_dev = torch.from_numpy(gb.view(np.int16)).cuda()
+    ent_a = _store(ent_dtype, B, nblk)
+    ent_c = _store(ent_dtype, B, nblk)
+    stage_x = torch.zeros((B, m, D), dtype=torch.float32, device="cuda")
+    stage_g = torch.zeros_like(stage_x)
+    print(f"[append] bitwise vs compress m={m} dtype={ent_dtype}", flush=True)
+    for p in range(T):
+        pos = torch.full((B,), p, dtype=torch.int64, device="cuda")
+        lib.csa_cache_append(x_dev[:, p].contiguous(), g_dev[:, p].contiguous(), lib.BF16, bias,
+                             m, pos, D_C, D_R, stage_x, stage_g, ent_a, None)
+    lib.csa_compress(x_dev, g_dev, lib.BF16, bias, m, B, T, D_C, D_R, ent_c)
+    torch.cuda.synchronize()
+    assert torch.equal(ent_a.c, ent_c.c) and torch.equal(ent_a.r, ent_c.r)
+    if ent_dtype == lib.E4M3:
+        assert torch.equal(ent_a.scale, ent_c.scale)
+
+
+def _e4m3_key_store(B, rows, d):
+    c = torch.zeros((B, rows, d), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((B, rows), dtype=torch.float32, device="cuda")
+    return lib.Store(c=c, dtype=lib.E4M3, d_c=d, d_r=0, rows=rows, ld_c=d, scale=sc)
+
+
+def test_decode_loop_ring_window_and_index_keys():
+    # Per decode step: append the token's KV row (fp8 entry store + fp8 window ring of 16 rows)
+    # and its indexer key (second append: d_c = 64, no raw store, e4m3 key store), then
+    # index -> top-k -> attend for the new token. The loop starts at a block boundary minus one
+    # with the history appended the same way, so it crosses block closes and ring wraps. Every
+    # step is checked stage-wise (scores, exact top-k on the GPU's scores, attention on the GPU's
+    # caches) and the caches against the oracle's pooling and storage rules.
+    from long_context_compressed_07_amd.inputs import _e4m3_rows
+    from oracle_io import check_topk_valid
+    B, m, H, H_I, d_I, k, window, ring = 2, 4, 128, 8, 64, 6, 12, 16
+    P0, S = 4 * 9 - 1, 22                  # history tokens, decode steps
+    T = P0 + S
+    n_cap = T // m + 1
+    rng = np.random.default_rng(4242)
+    xb = to_bf16_bits(_normal(rng, (B, T, D), 1.0 / np.sqrt(D)))
+    gb = to_bf16_bits(_normal(rng, (B, T, D), 1.0))
+    kxb = to_bf16_bits(_normal(rng, (B, T, d_I), 1.0 / np.sqrt(d_I)))
+    kgb = to_bf16_bits(_normal(rng, (B, T, d_I), 1.0))
+    bias_np = _normal(rng, (m,), 1.0 / np.sqrt(m))
+    qb = to_bf16_bits(_normal(rng, (S, B, H, D), 1.0))
+    qi_c, qi_s = _e4m3_rows(rng, (S, B, H_I, d_I), 1.0 / np.sqrt(d_I))
+    wi = _normal(rng, (S, B, H_I), 1.0 / np.sqrt(H_I))
+    dev = "cuda"
+    x_dev = torch.from_numpy(xb.view(np.int16)).to(dev)
+    g_dev = torch.from_numpy(gb.view(np.int16)).to(dev)
+    kx_dev = torch.from_numpy(kxb.view(np.int16)).to(dev)
+    kg_dev = torch.from_numpy(kgb.view(np.int16)).to(dev)
+    bias = torch.from_numpy(bias_np).to(dev)
+    ent = _store(lib.E4M3, B, n_cap)
+    raw = _store(lib.E4M3, B, ring)
+    raw.pos0 = torch.zeros(B, dtype=torch.int64, device=dev)
+    keys = _e4m3_key_store(B, n_cap, d_I)
+    st_x = torch.zeros((B, m, D), dtype=torch.float32, device=dev)
+    st_g = torch.zeros_like(st_x)
+    sk_x = torch.zeros((B, m, d_I), dtype=torch.float32, device=dev)
+    sk_g = torch.zeros_like(sk_x)
+    seq = torch.arange(B, dtype=torch.int32, device=dev)
+    scores = torch.empty((B, n_cap), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, D_C), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    sm_scale = 1.0 / np.sqrt(D)
+    x64, g64 = bf16_decode(xb), bf16_decode(gb)
+    kx64, kg64 = bf16_decode(kxb), bf16_decode(kgb)
+
+    def append(p):
+        pos = torch.full((B,), p, dtype=torch.int64, device=dev)
+        lib.csa_cache_append(x_dev[:, p].contiguous(), g_dev[:, p].contiguous(), lib.BF16, bias,
+                             m, pos, D_C, D_R, st_x, st_g, ent, raw, raw.pos0)
+        lib.csa_cache_append(kx_dev[:, p].contiguous(), kg_dev[:, p].contiguous(), lib.BF16,
+                             bias, m, pos, d_I, 0, sk_x, sk_g, keys, None)
+
+    print("[append] decode loop: history", flush=True)
+    for p in range(P0):
+        append(p)
+    worst = 0.0
+    for s in range(S):
+        p = P0 + s
+        append(p)
+        pos = torch.full((B,), p, dtype=torch.int64, device=dev)
+        q_i = torch.from_numpy(qi_c[s]).to(dev)
+        q_i_s = torch.from_numpy(qi_s[s]).to(dev)
+        lib.csa_index(seq, pos, q_i, torch.from_numpy(wi[s]).to(dev), keys.c, scores, lib.E4M3,
+                      H_I, d_I, B, n_cap, m, q_i_scale=q_i_s, k_i_scale=keys.scale)
+        lib.csa_topk(seq, pos, scores, idx, n_cap, m, k)
+        q = torch.from_numpy(qb[s].view(np.int16)).to(dev)
+        lib.csa_attend(seq, pos, q, lib.BF16, H, ent, m, idx, k, raw, window, sm_scale, out, lse)
+        torch.cuda.synchronize()
+        got_e, sc_e = _read(ent)
+        got_r, sc_r = _read(raw)
+        kc = keys.c.cpu().numpy()
+        ks = keys.scale.cpu().numpy().astype(np.float64)
+        sc_gpu = scores.cpu().numpy()
+        idx_gpu = idx.cpu().numpy()
+        o_gpu = out.cpu().numpy()
+        nv = orc.n_visible(p, m, n_cap)
+        for b in range(B):
+            # caches against the oracle's pooling + storage rules
+            e = orc.compress(x64[b, :p + 1], g64[b, :p + 1], bias_np, m)
+            _check_rows(lib.E4M3, got_e[b, :nv], sc_e[b, :nv], e)
+            ek = orc.compress(kx64[b, :p + 1], kg64[b, :p + 1], bias_np, m)
+            kq_ref, ks_ref = orc.store_e4m3_rows(ek)
+            assert np.abs(ks[b, :nv] - ks_ref).max() <= 1e-5 * ks_ref.max()
+            wpos = np.arange(max(0, p - window + 1), p + 1)
+            _check_rows(lib.E4M3, got_r[b, wpos % ring], sc_r[b, wpos % ring], x64[b, wpos])
+            # index on the GPU's key cache, top-k on the GPU's scores, attention on its caches
+            kI = e4m3_decode(kc[b, :nv]) * ks[b, :nv, None]
+            qI = e4m3_decode(qi_c[s, b]) * qi_s[s, b][:, None].astype(np.float64)
+            s_ref = orc.index_scores(qI, wi[s, b].astype(np.float64), kI, nv)
+            if nv:
+                den = np.abs(s_ref[:nv]).max()
+                assert np.abs(sc_gpu[b, :nv] - s_ref[:nv]).max() <= 1e-5 * den
+            sel, _ = orc.topk(sc_gpu[b, :nv].astype(np.float64), nv, k)
+            assert (sel == idx_gpu[b]).all(), (s, b)
+            check_topk_valid(idx_gpu[b], s_ref, nv, k)
+            ent_store = (e4m3_decode(ent.c[b].cpu().numpy()) * sc_e[b][:, None],
+                         bf16_decode(ent.r[b].cpu().numpy().view(np.uint16)), None, 0)
+            raw_store = (e4m3_decode(raw.c[b].cpu().numpy()) * sc_r[b][:, None],
+                         bf16_decode(raw.r[b].cpu().numpy().view(np.uint16)), None, 0)
+            o_ref, _ = orc.csa_attend_one(bf16_decode(qb[s, b]), ent_store, idx_gpu[b], raw_store,
+                                          p, window, sm_scale)
+            err = np.abs(o_gpu[b] - o_ref).max() / np.abs(o_ref).max()
+            worst = max(worst, err)
+            assert err <= 2e-2, (s, b, err)
+    print(f"[append] decode loop: {S} steps, worst attention rel err {worst:.2e}", flush=True)

@@ -211,9 +211,8 @@ def test_bf16_two_role_kernel_other_head_counts():
 
 
 @pytest.mark.parametrize("sharp", [False, True])
-def test_csa_prefill_64_heads_key_splits(sharp):
-    # Few queries over many keys: 64-head workgroups split each query's keys (partials merged by
-    # the combine kernel).
+def test_csa_prefill_64_heads_few_queries(sharp):
+    # Few queries over many keys with 64-head workgroups (bf16 lists this long are not split).
     wl = SMALL["C2"].replace(T=8003, nq=6, k=1000, window=40)
     print(f"[parity] csa prefill 64 heads key splits sharp={sharp}", flush=True)
     host, step = _run(wl, sharp, 21)
@@ -240,9 +239,9 @@ def test_hca_prefill_128_heads_many_queries():
 
 
 def test_hca_few_queries_many_entries_split():
-    # Few queries over many entries: several workgroups per query along the key list, merged by
-    # the log-sum-exp combine kernel.
-    wl = SMALL["C3"].replace(m=16, T=16 * 2300 + 5, nq=3, H=128)
+    # Few queries over many entries: 17000 bf16 entries take two workgroups per query along the
+    # key list, merged by the log-sum-exp combine kernel.
+    wl = SMALL["C3"].replace(m=16, T=16 * 17000 + 5, nq=3, H=128)
     print("[parity] hca key splits", flush=True)
     for sharp in (False, True):
         host, step = _run(wl, sharp, 18)

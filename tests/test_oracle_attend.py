@@ -175,6 +175,77 @@ def test_hca_query_before_first_block_sees_nothing():
     assert (out == 0).all() and (lse == -np.inf).all()
 
 
-def test_window_outside_store_raises():
+def test_window_longer_than_ring_raises():
     with pytest.raises(ValueError):
-        o.window_rows(pos=100, window=8, pos0=95, n_rows=10)
+        o.window_rows(pos=100, window=11, pos0=0, n_rows=10)
+
+
+def test_window_ring_rows_worked_example():
+    # Ring of 5 rows, offset 2: position p in row (p - 2) mod 5. Window of 4 at position 9:
+    # positions 6, 7, 8, 9 -> rows 4, 0, 1, 2.
+    assert o.window_rows(pos=9, window=4, pos0=2, n_rows=5).tolist() == [4, 0, 1, 2]
+    # A store holding every position from pos0 on: no wrap.
+    assert o.window_rows(pos=9, window=4, pos0=3, n_rows=100).tolist() == [3, 4, 5, 6]
+
+
+def test_ring_store_equals_linear_store():
+    # A ring of R >= window rows, written token by token (row p mod R), holds the same window as
+    # the store of every position: CSA attention over either is the same.
+    T, d, H, R, w = 41, 6, 3, 7, 5
+    x = _r((T, d), 40)
+    ring = np.zeros((R, d))
+    for p in range(T):
+        ring[p % R] = x[p]
+    q = _r((H, d), 41)
+    e = _r((6, d), 42)
+    ent = _store(e[:, :4], e[:, 4:])
+    idx = np.array([0, 3, 5])
+    a = o.csa_attend_one(q, ent, idx, _store(x[:, :4], x[:, 4:]), T - 1, w, 0.7)
+    b = o.csa_attend_one(q, ent, idx, _store(ring[:, :4], ring[:, 4:]), T - 1, w, 0.7)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ---- token selection: the original tokens of the selected blocks ---------------------------
+# hongke120.com 2.2 item 3; yudonglee.me "DeepSeek-V4 详解" 2.2 Steps 3-4.
+
+def test_tokens_m1_equals_entry_attention():
+    # With m = 1 every block is one token and pooling is the identity (compress pin), so token
+    # selection over the raw rows equals entry selection over the m = 1 entries.
+    T, d, H = 30, 5, 3
+    x, g = _r((T, d), 60), _r((T, d), 61)
+    e = o.compress(x, g, np.array([0.3]), 1)
+    q = _r((H, d), 62)
+    idx = np.array([1, 4, -1, 9, 17])
+    raw = _store(x[:, :3], x[:, 3:])
+    a = o.csa_attend_tokens_one(q, raw, idx, 1, 25, 4, 0.6)
+    b = o.csa_attend_one(q, _store(e[:, :3], e[:, 3:]), idx, raw, 25, 4, 0.6)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-14)
+
+
+def test_tokens_brute_force_against_textbook():
+    # m = 4: blocks 2 and 5 give positions 8..11 and 20..23, then the window 26..29 (position 29
+    # is the query); textbook attention over exactly that multiset of rows.
+    T, d, H, m = 30, 6, 4, 4
+    x = _r((T, d), 63)
+    q = _r((H, d), 64)
+    out, lse = o.csa_attend_tokens_one(q, _store(x[:, :4], x[:, 4:]), np.array([5, -1, 2]), m,
+                                       29, 4, 0.45)
+    rows = [20, 21, 22, 23, 8, 9, 10, 11, 26, 27, 28, 29]
+    want_o, want_l = textbook(q, x[rows], x[rows][:, :4], 0.45)
+    np.testing.assert_allclose(out, want_o, atol=1e-13)
+    np.testing.assert_allclose(lse, want_l, atol=1e-13)
+
+
+def test_tokens_store_offset_and_missing_rows():
+    T, d, m = 24, 4, 4
+    x = _r((T, d), 65)
+    q = _r((2, d), 66)
+    full = o.csa_attend_tokens_one(q, _store(x[:, :2], x[:, 2:]), np.array([3, 4]), m, 23, 3, 1.0)
+    part = o.csa_attend_tokens_one(q, _store(x[8:, :2], x[8:, 2:], None, 8), np.array([3, 4]), m,
+                                   23, 3, 1.0)
+    np.testing.assert_array_equal(full[0], part[0])
+    with pytest.raises(ValueError):
+        o.csa_attend_tokens_one(q, _store(x[8:, :2], x[8:, 2:], None, 8), np.array([1]), m, 23, 3,
+                                1.0)

@@ -122,3 +122,38 @@ def test_page_counts():
     # The page's rounded statements agree with the exact counts.
     assert abs(g["csa_entries_at_1m"] - g["csa_entries_stated_approx"]) / 262144 < 0.05
     assert abs(n_hca - g["hca_entries_stated_approx"]) / n_hca < 0.05
+
+
+# ---- low-precision indexer: MXFP4 vectors, bf16 scores ---------------------------------------
+# deepseek.csdn.net "一文搞懂 DeepSeek", V4 的其他升级 (FP4 paragraph).
+
+def test_bf16_score_storage():
+    s = np.array([1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9, -np.inf, 3.0])
+    out = o.store_scores_bf16(s)
+    # 1 + 2^-9 is halfway between 1 and 1 + 2^-7: ties to even -> 1; 1 + 3 * 2^-9 -> 1 + 2^-7.
+    assert out[0] == 1.0 and out[1] == 1.0 + 2.0 ** -7
+    assert out[2] == -np.inf and out[3] == 3.0
+
+
+def test_mxfp4_index_worked_example():
+    # One head, w = 1: query block 0 = [1, 1, 0, ...] (scale 2^0), keys: [2, 0.5, ...] -> 2.5,
+    # [-1, 0, ...] -> ReLU 0, [6, 6, ...] with scale 2^-2 -> 3. bf16 keeps all three exactly.
+    from oracle.numerics import mxfp4_decode
+    q = np.zeros((1, 32), np.uint8)
+    q[0, 0] = 0x22                                   # codes 2, 2: 1.0, 1.0
+    qs = np.array([[127, 127]], np.uint8)
+    k = np.zeros((3, 32), np.uint8)
+    k[0, 0] = 0x14                                   # 2.0, 0.5
+    k[1, 0] = 0x0A                                   # -1.0, 0
+    k[2, 0] = 0x77                                   # 6, 6
+    ks = np.array([[127, 127], [127, 127], [125, 127]], np.uint8)
+    s = o.store_scores_bf16(o.index_scores(mxfp4_decode(q, qs), np.array([1.0]),
+                                           mxfp4_decode(k, ks), 3))
+    assert s.tolist() == [2.5, 0.0, 3.0]
+
+
+def test_recall():
+    assert o.recall(np.array([3, 5, 9, -1]), np.array([3, 5, 7, -1])) == 2 / 3
+    assert o.recall(np.array([1, 2]), np.array([-1, -1])) == 1.0
+    sel, _ = o.topk(np.arange(10.0), 10, 4)
+    assert o.recall(sel, sel) == 1.0

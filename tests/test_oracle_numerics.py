@@ -74,3 +74,60 @@ def test_e4m3_encode_roundtrip():
     vals = nu.e4m3_decode(codes)
     ok = np.isfinite(vals) & (codes != 0x80)     # -0 encodes as +0
     assert (nu.e4m3_encode(vals[ok]) == codes[ok]).all()
+
+
+# ---- MXFP4 (OCP Microscaling specification): E2M1 elements, E8M0 block scales ---------------
+
+def test_e2m1_values_are_the_specification_table():
+    # The specification lists the E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); bit 3 is
+    # the sign.
+    from oracle.numerics import E2M1_VALUES
+    assert E2M1_VALUES[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert (E2M1_VALUES[8:] == -E2M1_VALUES[:8]).all()
+
+
+def test_e8m0_decode_matches_torch():
+    from oracle.numerics import e8m0_decode
+    codes = np.arange(255, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    np.testing.assert_array_equal(e8m0_decode(codes), want)
+    assert np.isnan(e8m0_decode(np.array([255], np.uint8)))[0]
+
+
+def test_mxfp4_decode_worked_example():
+    # Byte 0x21: element 0 = code 1 (0.5), element 1 = code 2 (1.0). Byte 0xF7: element 0 = code 7
+    # (6), element 1 = code 15 (-6). Scale 128 doubles the first block; scale 126 halves the second.
+    from oracle.numerics import mxfp4_decode
+    packed = np.zeros((1, 32), np.uint8)
+    packed[0, 0] = 0x21
+    packed[0, 16] = 0xF7
+    v = mxfp4_decode(packed, np.array([[128, 126]], np.uint8))
+    assert v[0, :2].tolist() == [1.0, 2.0] and (v[0, 2:32] == 0).all()
+    assert v[0, 32:34].tolist() == [3.0, -3.0] and (v[0, 34:] == 0).all()
+
+
+def test_mxfp4_storage_cast():
+    # The inputs' MXFP4 cast: scale 2^(floor(log2 amax) - 2), nearest E2M1 with ties to the even
+    # fraction bit, saturation at 6. Block: 6 (amax, scale 1), 1.25 (tie 1 | 1.5 -> 1), 1.75 (tie
+    # 1.5 | 2 -> 2), 2.5 (tie 2 | 3 -> 2), 0.2 (-> 0), -5 (tie 4 | 6 -> 4).
+    from long_context_compressed_07_amd.inputs import to_mxfp4
+    from oracle.numerics import mxfp4_decode
+    x = np.zeros((1, 32), np.float32)
+    x[0, :6] = [6.0, 1.25, 1.75, 2.5, 0.2, -5.0]
+    p, sc = to_mxfp4(x)
+    assert sc.tolist() == [[127]]
+    assert mxfp4_decode(p, sc)[0, :6].tolist() == [6.0, 1.0, 2.0, 2.0, 0.0, -4.0]
+    # amax 7: scale 2^0 again, 7 saturates to 6
+    x[0, 0] = 7.0
+    p, sc = to_mxfp4(x)
+    assert mxfp4_decode(p, sc)[0, 0] == 6.0
+    # random rows: every element within half a step of its value below the block's saturation
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((50, 64)).astype(np.float32) * 0.1
+    p, sc = to_mxfp4(z)
+    y = mxfp4_decode(p, sc)
+    scale = np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, axis=1)
+    mag = np.abs(z) / scale
+    half_step = np.where(mag < 2, 0.25, np.where(mag < 4, 0.5, 1.0)) * scale
+    ok = (mag <= 6) & (np.abs(y - z) <= half_step + 1e-12)
+    assert (ok | (mag > 6)).all() and (np.abs(y[mag > 6]) == 6 * scale[mag > 6]).all()
