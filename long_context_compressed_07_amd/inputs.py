@@ -86,6 +86,18 @@ def to_mxfp4(x: np.ndarray):
     return packed, (e + 127).astype(np.uint8)
 
 
+def to_e4m3_rows(x: np.ndarray):
+    """float32 [..., d] -> (E4M3 codes uint8 [..., d], float32 row scales [...]): the storage cast of
+    fp8 rows with one scale per row, sigma = amax / 448 and codes = e4m3(x / sigma) (torch's cast;
+    an all-zero row stores sigma 0)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    sigma = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(sigma > 0, sigma, np.float32(1.0))
+    codes = torch.from_numpy(np.ascontiguousarray(x / safe[..., None])).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).numpy(), sigma
+
+
 def mxfp4_rows(rng: np.random.Generator, shape, std: float):
     """MXFP4 rows of Gaussian draws with the given std: (packed codes, scales)."""
     return to_mxfp4(_normal(rng, shape, std))
