@@ -206,6 +206,17 @@ csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scor
                     int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 size_t csa_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
 
+/* csa_topk_noalloc -- csa_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): same arguments, rule and
+ * results as csa_topk, without (ws, ws_bytes). Its scratch is a device array inside the library,
+ * 16 MiB per GPU, held by every GPU the library runs on until the process ends; the call
+ * allocates nothing. Calls whose csa_topk_workspace_bytes(nq, N, k) exceeds 16 MiB fail with
+ * CSA_EWORKSPACE (rows of up to 32768 entries need none). Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (several streams or host threads) race on it. Nothing in
+ * it needs to start at zero: a call writes every slot it reads. */
+csa_status csa_topk_noalloc(const csa_queries_t* Q, const float* scores, int64_t ld_scores,
+                            int64_t N, int32_t m, int32_t k, int32_t* idx, void* stream);
+
 /* csa_topk_bf16 -- csa_topk on bf16 scores (csa_index_mxfp4's output), same rule and workspace
  * ([csdn] V4 的其他升级: bf16 index scores make the selection faster). scores [nq][ld_scores] bf16
  * codes; ties (far more frequent at bf16's 8 significant bits) go to the lower index. */

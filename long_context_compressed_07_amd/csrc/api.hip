@@ -154,6 +154,28 @@ csa_status csa_topk(const csa_queries_t* Q, const float* scores, int64_t ld_scor
   return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
+csa_status csa_topk_noalloc(const csa_queries_t* Q, const float* scores, int64_t ld_scores,
+                            int64_t N, int32_t m, int32_t k, int32_t* idx, void* stream) {
+  if (csa_status st = check_queries(Q)) return st;
+  if (k < 1 || N < 0 || m < 1 || ld_scores < N) return fail(CSA_EINVAL, "bad sizes");
+  if (Q->nq > 0 && (scores == nullptr || idx == nullptr)) return fail(CSA_EINVAL, "null scores/idx");
+  if (!csa::topk_supported(N, k))
+    return fail(CSA_EUNSUPPORTED,
+                "rows longer than 32768 need k <= 2048 and ceil(N / 32768) * k <= 32768");
+  const size_t need = csa::topk_workspace(Q->nq, N, k);
+  if (need > csa::kTopkScratchBytes)
+    return fail(CSA_EWORKSPACE, ("the call needs " + std::to_string(need) +
+                                 " bytes of scratch; the no-allocation top-k holds " +
+                                 std::to_string(csa::kTopkScratchBytes)).c_str());
+  void* ws = nullptr;
+  if (need > 0) {
+    if (csa_status st = hip_status(csa::topk_scratch(&ws))) return st;
+  }
+  csa::TopkArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, scores, 0, ld_scores, N, m, k, idx, ws,
+                  need};
+  return hip_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
 csa_status csa_topk_bf16(const csa_queries_t* Q, const uint16_t* scores, int64_t ld_scores,
                          int64_t N, int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream) {

@@ -106,6 +106,10 @@ struct TopkArgs {
 };
 size_t topk_workspace(int nq, int64_t N, int k);
 bool topk_supported(int64_t N, int k);
+// The no-allocation top-k's scratch: a device array of kTopkScratchBytes per GPU; *ptr receives
+// the current device's address of it.
+constexpr size_t kTopkScratchBytes = (size_t)16 << 20;
+hipError_t topk_scratch(void** ptr);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // Instrumentation: event timing of the main attention kernel (see csa.h).

@@ -26,6 +26,8 @@
 // the result is exact. Every chunk before a row's last visible one holds kWideChunk >= k entries
 // and so yields exactly k candidates: a row's candidates are the first n slots of its [chunks][k]
 // block, in entry order.
+#include <mutex>
+
 #include "common.h"
 
 namespace csa {
@@ -591,6 +593,35 @@ hipError_t launch_topk_t(const TopkArgs& a, hipStream_t s) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.Q.nq == 0) return hipSuccess;
   return a.bf16 ? launch_topk_t<uint16_t>(a, s) : launch_topk_t<float>(a, s);
+}
+
+// ---- Scratch of the no-allocation top-k (csa_topk_noalloc) -------------------------------------
+// A file-scope device array that every call on a GPU shares: each GPU the library runs on holds
+// its own copy until the process ends. Host code never passes the array's name (a host-side
+// stand-in) to a kernel: it takes the device address from hipGetSymbolAddress, once per device,
+// with that device current, and passes that.
+namespace {
+__device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t topk_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace csa

@@ -26,7 +26,8 @@ EXPORTS = ("csa_compress", "csa_index", "csa_topk", "csa_topk_workspace_bytes", 
            "csa_attend_workspace_bytes", "hca_attend", "hca_attend_workspace_bytes",
            "csa_status_str", "csa_last_error", "csa_abi_version", "csa_kernel_timing_enable",
            "csa_kernel_timing_read", "csa_peak_mfma_bf16", "csa_peak_sink_floats",
-           "csa_cache_append", "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16")
+           "csa_cache_append", "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16",
+           "csa_topk_noalloc")
 
 
 class KV(ctypes.Structure):
@@ -65,6 +66,7 @@ def load(path: str = LIB_PATH):
     lib.csa_topk.argtypes = [P(Queries), vp, i64, i64, i32, i32, vp, vp, sz, vp]
     lib.csa_topk_workspace_bytes.argtypes = [i32, i64, i32]
     lib.csa_topk_bf16.argtypes = [P(Queries), vp, i64, i64, i32, i32, vp, vp, sz, vp]
+    lib.csa_topk_noalloc.argtypes = [P(Queries), vp, i64, i64, i32, i32, vp, vp]
     lib.csa_index_mxfp4.argtypes = [P(Queries), vp, vp, vp, i32, i32, vp, vp, i32, i64, i32, vp,
                                     i64, vp]
     lib.csa_attend.argtypes = [P(Queries), vp, i32, i32, P(KV), i32, vp, i32, P(KV), i32, f32,
@@ -83,7 +85,7 @@ def load(path: str = LIB_PATH):
     for fn in ("csa_compress", "csa_index", "csa_topk", "csa_attend", "hca_attend",
                "csa_abi_version", "csa_kernel_timing_enable", "csa_kernel_timing_read",
                "csa_peak_mfma_bf16", "csa_peak_sink_floats", "csa_cache_append",
-               "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16"):
+               "csa_attend_tokens", "csa_index_mxfp4", "csa_topk_bf16", "csa_topk_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int32
     for fn in ("csa_topk_workspace_bytes", "csa_attend_workspace_bytes",
                "hca_attend_workspace_bytes"):
@@ -235,6 +237,17 @@ def csa_topk_bf16(seq, pos, scores, idx, N: int, m: int, k: int,
     ld = N if ld_scores is None else ld_scores
     _check(lib.csa_topk_bf16(ctypes.byref(Q), _ptr(scores), ld, N, m, k, _ptr(idx), _ptr(ws),
                              0 if ws is None else ws.numel(), _stream(stream)), "csa_topk_bf16")
+
+
+def csa_topk_noalloc(seq, pos, scores, idx, N: int, m: int, k: int,
+                     ld_scores: Optional[int] = None, stream=None):
+    """Top-k with the library's own scratch, allocating nothing (csa_topk_noalloc in
+    include/csa.h)."""
+    lib = load()
+    Q = _queries(seq, pos)
+    ld = N if ld_scores is None else ld_scores
+    _check(lib.csa_topk_noalloc(ctypes.byref(Q), _ptr(scores), ld, N, m, k, _ptr(idx),
+                                _stream(stream)), "csa_topk_noalloc")
 
 
 def csa_attend_workspace_bytes(nq: int, H: int, d_c: int, max_keys: int) -> int:
