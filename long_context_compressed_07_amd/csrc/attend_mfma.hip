@@ -383,10 +383,8 @@ attend_mfma_kernel(AttendArgs a, MfmaPlan plan) {
 // logits left the fp16 range of P, the block recomputes the four heads with the fp32 reference
 // code instead.
 constexpr int kCombHeads = kGenThreads / kWave;
-constexpr int kCombBatch = 8;
 
 __global__ void __launch_bounds__(kGenThreads) combine_kernel(AttendArgs a, MfmaPlan plan) {
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   __shared__ float smem[generic_smem_bytes(kD) / sizeof(float)];
   const int per_q = a.H / kCombHeads;
   const int qi = blockIdx.x / per_q;
@@ -400,46 +398,7 @@ __global__ void __launch_bounds__(kGenThreads) combine_kernel(AttendArgs a, Mfma
     for (int h = h0; h < h0 + kCombHeads; ++h) attend_generic_one(a, qi, h, smem);
     return;
   }
-  const int head = h0 + t / kWave;
-  const int d0 = (t & (kWave - 1)) * 8;
-  const int64_t p0 = (int64_t)qi * plan.n_split * a.H + head;   // partial index of split 0
-  const int64_t ps = a.H;                                        // stride between splits
-  float mx = -INFINITY, lsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < plan.n_split; s0 += kCombBatch) {
-    float2 ml[kCombBatch];
-    h8 v[kCombBatch];
-#pragma unroll
-    for (int u = 0; u < kCombBatch; ++u) {
-      const bool in = s0 + u < plan.n_split;
-      const int64_t pidx = p0 + (int64_t)(in ? s0 + u : s0) * ps;
-      ml[u] = *reinterpret_cast<const float2*>(plan.ws_ml + pidx * 2);
-      v[u] = *reinterpret_cast<const h8*>(plan.ws_o + pidx * kDC + d0);
-      if (!in) ml[u].x = -INFINITY;
-    }
-    float nm = mx;
-#pragma unroll
-    for (int u = 0; u < kCombBatch; ++u) nm = fmaxf(nm, ml[u].x);
-    const float r = mx == -INFINITY ? 0.f : exp2f(mx - nm);
-    lsum *= r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= r;
-#pragma unroll
-    for (int u = 0; u < kCombBatch; ++u) {
-      const float wgt = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - nm) * ml[u].y;
-      lsum += wgt;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)v[u][j];
-    }
-    mx = nm;
-  }
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  float* dst = a.out + ((int64_t)qi * a.H + head) * kDC + d0;
-  *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (a.lse != nullptr && d0 == 0)
-    a.lse[(int64_t)qi * a.H + head] =
-        lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+  merge_partials8(a, plan, qi, h0 + t / kWave, (t & (kWave - 1)) * 8);
 }
 
 // Plans without key splits: recompute, with the fp32 reference code, every query one of whose
