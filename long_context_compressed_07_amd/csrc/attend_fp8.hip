@@ -167,8 +167,13 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int R = 128;
   constexpr int kBufB = kTK * kRowB;
   constexpr int kPSteps = kTK / 16;
-  __shared__ __attribute__((aligned(1024))) char kv[2][kBufB];     // fp16 tiles
-  __shared__ __attribute__((aligned(1024))) char stg[kNst][kStB];  // staged cache rows
+  // Two fp16 tiles, then the staging slots of cache rows; after the tile loop the whole region
+  // stages the outputs.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufB + kNst * kStB];
+  char (*const kv)[kBufB] = reinterpret_cast<char (*)[kBufB]>(smem);
+  char (*const stg)[kStB] = reinterpret_cast<char (*)[kStB]>(smem + 2 * kBufB);
+  static_assert(4 * 32 * kStageLd<_Float16> <= 2 * kBufB + kNst * kStB, "fp16 output staging");
+  static_assert(2 * 32 * kStageLd<float> <= 2 * kBufB + kNst * kStB, "fp32 output staging");
   __shared__ __attribute__((aligned(16))) char s_p[kPSteps * RG * 1024];
   __shared__ int s_code[kSlotsF8][kTK];
   __shared__ KeyAddr8 s_addr[kSlotsF8][kTK];
@@ -199,17 +204,45 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
   const RowBases8 rbases = row_bases8(a, kl.b);
 
-  // Q^T fragments of this lane's head in fp16 (rounded from bf16): dims 16 s + 8 hi + [0, 8).
-  v4i qb[kKSteps];
+  const bool sel_dma = kl.sel != nullptr;
+  const KeyCodes32 kc = key_codes32(kl, ke);
+
+  // Prologue. The codes of tiles 0 .. kAheadF8 (tile w in wave w) need the selection slots, a
+  // dependent load; it goes out before the query loads, so that the wait for it does not also
+  // wait for them, and the rows' DMA is issued while the queries are still in flight.
+  const int c_pro = lane < kTK ? key_code(a, kl, k0 + w * kTK + lane, ke) : -1;
+  if (w == 0 && sel_dma) {   // selection slots of tiles kAheadF8 + 1 and + 2
+    dma_sel<kTK>(kl, k0 + (kAheadF8 + 1) * kTK, ke, s_sel[(kAheadF8 + 1) % 3]);
+    dma_sel<kTK>(kl, k0 + (kAheadF8 + 2) * kTK, ke, s_sel[(kAheadF8 + 2) % 3]);
+  }
+  // Q^T fragments of this lane's head (dims 16 s + 8 hi + [0, 8)), loaded as bf16 now and
+  // rounded to fp16 once the rows' DMA is out.
+  uint4 qraw[kKSteps];
   {
     const uint16_t* qrow =
         static_cast<const uint16_t*>(a.q) + ((int64_t)qi * a.H + hbase + qrow_i) * kD + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * s);
-      qb[s] = __builtin_bit_cast(v4i, bf16x8_to_f16(v.x, v.y, v.z, v.w));
+    for (int s = 0; s < kKSteps; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s);
+  }
+  if (lane < kTK) {
+    s_code[w][lane] = c_pro;
+    s_addr[w][lane] = key_addr8(rbases, c_pro);
+  }
+  {
+    const bool h = __any(c_pro >= 0);
+    const bool f = __all(c_pro >= 0 || lane >= kTK);
+    if (lane == 0) {
+      s_has_key[w] = h;
+      s_full[w] = f;
     }
   }
+  lds_barrier();   // codes and row addresses of tiles 0 .. kAheadF8 (LDS only)
+#pragma unroll
+  for (int j = 0; j < kAheadF8; ++j) dma_stage(s_addr[j], stg[j]);
+  v4i qb[kKSteps];
+#pragma unroll
+  for (int s = 0; s < kKSteps; ++s)
+    qb[s] = __builtin_bit_cast(v4i, bf16x8_to_f16(qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w));
   floatx16 o[4][RG];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -217,36 +250,7 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
     for (int r = 0; r < RG; ++r) o[mt][r] = floatx16{};
   float m_ref = -INFINITY, l_run = 0.f;
   bool have_ref = false;
-  bool overflow = false;
   const float cscale = a.sm_scale * kLog2e;
-  const bool sel_dma = kl.sel != nullptr;
-  const KeyCodes32 kc = key_codes32(kl, ke);
-
-  // Prologue: codes of tiles 0 .. kAheadF8 (wave 0), selection slots of tile kAheadF8 + 1 and
-  // kAheadF8 + 2, tiles 0 .. kAheadF8 - 1 staged, tile 0 converted.
-  if (threadIdx.x < 64) {
-#pragma unroll
-    for (int j = 0; j <= kAheadF8; ++j) {
-      const int c = threadIdx.x < kTK ? key_code(a, kl, k0 + j * kTK + threadIdx.x, ke) : -1;
-      if (threadIdx.x < kTK) {
-        s_code[j][threadIdx.x] = c;
-        s_addr[j][threadIdx.x] = key_addr8(rbases, c);
-      }
-      const bool h = __any(c >= 0);
-      const bool f = __all(c >= 0 || threadIdx.x >= kTK);
-      if (threadIdx.x == 0) {
-        s_has_key[j] = h;
-        s_full[j] = f;
-      }
-    }
-    if (sel_dma) {
-      dma_sel<kTK>(kl, k0 + (kAheadF8 + 1) * kTK, ke, s_sel[(kAheadF8 + 1) % 3]);
-      dma_sel<kTK>(kl, k0 + (kAheadF8 + 2) * kTK, ke, s_sel[(kAheadF8 + 2) % 3]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kAheadF8; ++j) dma_stage(s_addr[j], stg[j]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   convert_stage(stg[0], kv[0]);
@@ -393,47 +397,50 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
     s_l[qrow_i] = l_run;
     s_ref[qrow_i] = m_ref;
   }
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < RG; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][r][i]);
-  if (__any(overflow)) atomicOr(&s_flag, 1);
-  __syncthreads();
-  if (threadIdx.x == 0) plan.flags[item] = s_flag;
+  __syncthreads();   // (m, l) of every head; the tile and staging buffers are idle
 
-  // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
-  // row group at a time, staged in the (now idle) tile buffers.
-  char* stage = &kv[0][0];
+  // Outputs (n_split == 1: o / l in fp32, two 32-head row groups per pass) or partials (o / l in
+  // fp16, all 128 heads in one pass, and (m, l)), staged through LDS and written as whole rows.
+  // A staged value that is not finite in its type (fp16 P overflowed, or a converted value did)
+  // flags the workgroup for the fp32 recompute.
+  bool bad = false;
+  if (plan.n_split == 1) {
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int hrow = 32 * r + (lane & 31);
-    const float l = s_l[hrow];
-    const float m = s_ref[hrow];
-    const int head = hbase + hrow;
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t row0 = plan.n_split == 1 ? (int64_t)qi * a.H + hbase + 32 * r
-                                           : ((int64_t)qi * plan.n_split + split) * a.H + hbase + 32 * r;
-    if (plan.n_split == 1) {
-      stage_rows<float>(o, r, inv, stage);
-      if (a.lse != nullptr && w == 0 && hi == 0)
-        a.lse[(int64_t)qi * a.H + head] =
-            l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
-      __syncthreads();
-      flush_rows<float>(stage, a.out + row0 * kDC);
-    } else {
-      stage_rows<_Float16>(o, r, inv, stage);
-      if (w == 0 && hi == 0) {
-        const int64_t pidx = row0 + (lane & 31);
-        plan.ws_ml[pidx * 2] = m;
-        plan.ws_ml[pidx * 2 + 1] = l;
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = 2 * half + rr;
+        const int hrow = 32 * r + (lane & 31);
+        const float l = s_l[hrow];
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        stage_rows_checked<float>(o, r, inv, smem + rr * 32 * kStageLd<float>, bad);
+        if (a.lse != nullptr && w == 0 && hi == 0)
+          a.lse[(int64_t)qi * a.H + hbase + hrow] =
+              l > 0.f ? (s_ref[hrow] + __log2f(l)) * 0.6931471805599453f : -INFINITY;
       }
       __syncthreads();
-      flush_rows<_Float16>(stage, plan.ws_o + row0 * kDC);
+      flush_rows<float, 64>(smem, a.out + ((int64_t)qi * a.H + hbase + 64 * half) * kDC);
+      __syncthreads();
+    }
+  } else {
+    const int64_t row0 = ((int64_t)qi * plan.n_split + split) * a.H + hbase;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int hrow = 32 * r + (lane & 31);
+      const float l = s_l[hrow];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      stage_rows_checked<_Float16>(o, r, inv, smem + r * 32 * kStageLd<_Float16>, bad);
+      if (w == 0 && hi == 0) {
+        plan.ws_ml[(row0 + hrow) * 2] = s_ref[hrow];
+        plan.ws_ml[(row0 + hrow) * 2 + 1] = l;
+      }
     }
     __syncthreads();
+    flush_rows<_Float16, 128>(smem, plan.ws_o + row0 * kDC);
   }
+  if (__any(bad)) atomicOr(&s_flag, 1);
+  __syncthreads();
+  if (threadIdx.x == 0) plan.flags[item] = s_flag;
 }
 
 }  // namespace

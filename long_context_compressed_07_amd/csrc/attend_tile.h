@@ -112,12 +112,39 @@ __device__ __forceinline__ void stage_rows(const floatx16 (&o)[4][RG], int r, fl
     }
 }
 
-// Writes the 32 staged rows: row h to dst + h * 512 (consecutive heads are consecutive rows).
-template <typename T>
+// stage_rows that also tells whether any staged value is not a finite value of T: each scaled
+// value is compared with T's largest finite magnitude (a NaN fails the comparison), so an
+// accumulator that overflowed, and a finite value that T cannot hold, both set `bad`.
+template <typename T, int RG>
+__device__ __forceinline__ void stage_rows_checked(const floatx16 (&o)[4][RG], int r, float inv,
+                                                   char* buf, bool& bad) {
+  constexpr float kMax = sizeof(T) == 2 ? 65504.f : 3.4028235e38f;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5;
+  char* row = buf + (lane & 31) * kStageLd<T> + (128 * w + 4 * hi) * (int)sizeof(T);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = o[mt][r][4 * j + u] * inv;
+        bad |= !(__builtin_fabsf(x[u]) <= kMax);
+      }
+      const t4 v = {(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
+      *reinterpret_cast<t4*>(row + (32 * mt + 8 * j) * (int)sizeof(T)) = v;
+    }
+}
+
+// Writes ROWS staged rows: row h to dst + h * 512 (consecutive heads are consecutive rows).
+template <typename T, int ROWS = 32>
 __device__ __forceinline__ void flush_rows(const char* buf, T* dst) {
   constexpr int kChunksRow = 512 * (int)sizeof(T) / 16;
+  static_assert(ROWS * kChunksRow % 256 == 0, "whole passes of 256 threads");
 #pragma unroll
-  for (int c = threadIdx.x; c < 32 * kChunksRow; c += 256) {
+  for (int i = 0; i < ROWS * kChunksRow / 256; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
     const int h = c / kChunksRow, k = c - h * kChunksRow;
     const uint4 v = *reinterpret_cast<const uint4*>(buf + h * kStageLd<T> + 16 * k);
     *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + (int64_t)h * 512) + 16 * k) = v;
