@@ -17,15 +17,17 @@
 // give every segment its output offset; selected positions are staged in LDS and written out with
 // coalesced stores.
 //
-// Rows of up to kChunk (8192) visible entries: one 256-thread workgroup per row. Rows of up to
+// Rows of up to kChunk (8192) visible entries: one 256-thread workgroup per row; rows of up to
 // kWideChunk (32768): one 1024-thread workgroup per row (the same code, 32 keys per thread).
-// Longer rows: stage 1 runs the same selection on chunks of kWideChunk entries (several
-// 1024-thread workgroups per row) and writes each chunk's local top-k (ascending); stage 2
-// selects the row's top-k among the concatenated candidates, with the 256-thread form when they
-// fit in it. The union of the chunks' top-k contains the row's top-k under the same tie rule, so
-// the result is exact. Every chunk before a row's last visible one holds kWideChunk >= k entries
-// and so yields exactly k candidates: a row's candidates are the first n slots of its [chunks][k]
-// block, in entry order.
+// Longer rows in a call with few rows (a decode step: one row per sequence) take the
+// sampled-threshold path below, which spreads each row over many workgroups. Other longer rows:
+// stage 1 runs the same selection on chunks of kWideChunk entries (several 1024-thread
+// workgroups per row) and writes each chunk's local top-k (ascending); stage 2 selects the row's
+// top-k among the concatenated candidates, with the 256-thread form when they fit in it. The
+// union of the chunks' top-k contains the row's top-k under the same tie rule, so the result is
+// exact. Every chunk before a row's last visible one holds kWideChunk >= k entries and so yields
+// exactly k candidates: a row's candidates are the first n slots of its [chunks][k] block, in
+// entry order.
 #include <mutex>
 
 #include "common.h"
@@ -119,13 +121,13 @@ __device__ __forceinline__ int block_scan(int a, int* s_tmp, int& total) {
 }
 
 // Largest key and smallest nonzero key of the block. s_tmp: 2 NT / 64 ints.
-template <int NT>
-__device__ __forceinline__ void block_range(const uint32_t (&kv)[kPer], int* s_tmp,
+template <int NT, int PER>
+__device__ __forceinline__ void block_range(const uint32_t (&kv)[PER], int* s_tmp,
                                             uint32_t& mx, uint32_t& mn) {
   constexpr int NW = NT / kWave;
   uint32_t a = 0, b = ~0u;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     a = max(a, kv[i]);
     b = min(b, kv[i] == 0u ? ~0u : kv[i]);
   }
@@ -204,15 +206,15 @@ __device__ __forceinline__ float key_score(uint32_t u) {
 // conflicts than the radix digits of the sign and exponent bits). Those keys are gathered in
 // position order and ranked against each other. Returns false, with hist zero again, when that
 // bin holds more than NT keys; otherwise the k-th largest key and *need_eq as kth_key.
-template <int NT>
-__device__ bool kth_key_by_value(const uint32_t (&kv)[kPer], int k, float f0, float scale,
+template <int NT, int PER>
+__device__ bool kth_key_by_value(const uint32_t (&kv)[PER], int k, float f0, float scale,
                                  int* hist, int* s_tmp, uint32_t* kth, int* need_eq) {
   auto bin = [&](uint32_t key) {
     const int b = (int)((key_score(key) - f0) * scale);   // >= 0: key_score(key) >= f0
     return b < kBins - 1 ? b : kBins - 1;
   };
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
+  for (int i = 0; i < PER; ++i)
     if (kv[i] != 0u) atomicAdd(&hist[bin(kv[i])], 1);
   lds_sync();
   int kk = k, count;
@@ -226,12 +228,12 @@ __device__ bool kth_key_by_value(const uint32_t (&kv)[kPer], int k, float f0, fl
   uint32_t* s_cand = reinterpret_cast<uint32_t*>(hist + kBins);
   int mine = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) mine += kv[i] != 0u && bin(kv[i]) == d;
+  for (int i = 0; i < PER; ++i) mine += kv[i] != 0u && bin(kv[i]) == d;
   int total;
   int off = block_scan<NT>(mine, s_tmp, total);
   if (mine > 0) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
+    for (int i = 0; i < PER; ++i)
       if (kv[i] != 0u && bin(kv[i]) == d) s_cand[off++] = kv[i];
   }
   // Padded with zero keys (below every real key) to a multiple of 16 for the 16-byte reads.
@@ -276,8 +278,8 @@ __device__ bool kth_key_by_value(const uint32_t (&kv)[kPer], int k, float f0, fl
 // where several workgroups share a CU's LDS (one workgroup per row, many rows: 568 -> 365 us for
 // 32768 rows of up to 8192 scores); the chunk and merge kernels of long rows run with about one
 // workgroup per CU, where the radix alone measured faster (12.2 vs 13.8 us per chunk launch).
-template <int NT, bool BY_VALUE>
-__device__ uint32_t kth_key(const uint32_t (&kv)[kPer], int k, int* hist, int* s_tmp,
+template <int NT, bool BY_VALUE, int PER>
+__device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* hist, int* s_tmp,
                             int* need_eq) {
   uint32_t mx, mn;
   block_range<NT>(kv, s_tmp, mx, mn);
@@ -292,7 +294,7 @@ __device__ uint32_t kth_key(const uint32_t (&kv)[kPer], int k, int* hist, int* s
     // NaN fails every comparison; an infinite score makes width or scale infinite.
     if (width > 0.f && width <= 3.4028235e38f && scale <= 3.4028235e38f) {
       uint32_t K;
-      if (kth_key_by_value<NT>(kv, k, f0, scale, hist, s_tmp, &K, need_eq)) return K;
+      if (kth_key_by_value<NT, PER>(kv, k, f0, scale, hist, s_tmp, &K, need_eq)) return K;
     }
   }
   const int p = 31 - __builtin_clz(mx ^ mn);   // highest bit in which real keys differ
@@ -310,7 +312,7 @@ __device__ uint32_t kth_key(const uint32_t (&kv)[kPer], int k, int* hist, int* s
     const uint32_t dmask = (2u << (hi - lo)) - 1u;
     int* h = hist + (level & 1) * kBins;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < PER; ++i) {
       if ((kv[i] & pmask) == prefix) atomicAdd(&h[(kv[i] >> lo) & dmask], 1);
     }
     lds_sync();
@@ -328,14 +330,14 @@ __device__ uint32_t kth_key(const uint32_t (&kv)[kPer], int k, int* hist, int* s
 
 // Calls put(o, j, key) for the top k in ascending position order o = 0 .. k-1 (j = PER t + i for
 // key kv[i] of thread t): keys > K and the first need_eq keys == K. Ends with an LDS barrier.
-template <int NT, typename Put>
-__device__ void compact(const uint32_t (&kv)[kPer], uint32_t K, int need_eq, int k, int* s_tmp,
+template <int NT, int PER, typename Put>
+__device__ void compact(const uint32_t (&kv)[PER], uint32_t K, int need_eq, int k, int* s_tmp,
                         Put put) {
   // Padding keys (0) are below every real key, and K is a real key (>= 1), so they never count.
-  const int j0 = threadIdx.x * kPer;
+  const int j0 = threadIdx.x * PER;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     gt += kv[i] > K;
     eq += kv[i] == K;
   }
@@ -346,7 +348,7 @@ __device__ void compact(const uint32_t (&kv)[kPer], uint32_t K, int need_eq, int
   int off = block_scan<NT>(gt + take_eq, s_tmp, total);
   int eq_left = take_eq;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     bool take = kv[i] > K;
     if (kv[i] == K && eq_left > 0) {
       take = true;
@@ -366,12 +368,13 @@ __device__ __forceinline__ float score_at(const uint16_t* row, int64_t j) {
 
 // Loads keys [PER t, PER t + PER) of a row of n scores (0 beyond n): 16-byte loads for whole,
 // aligned segments, element by element only for the segment holding the row's end.
-__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[kPer]) {
-  const int j0 = threadIdx.x * kPer;
+template <int PER>
+__device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[PER]) {
+  const int j0 = threadIdx.x * PER;
   const float* src = row + j0;
-  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const float4 v = reinterpret_cast<const float4*>(src)[q];
       kv[4 * q] = score_key(v.x);
       kv[4 * q + 1] = score_key(v.y);
@@ -381,17 +384,18 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv
   } else {
     const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
+    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
   }
 }
 
 // bf16 scores: 16-byte loads of 8 codes; each code is the high half of its fp32 value.
-__device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (&kv)[kPer]) {
-  const int j0 = threadIdx.x * kPer;
+template <int PER>
+__device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (&kv)[PER]) {
+  const int j0 = threadIdx.x * PER;
   const uint16_t* src = row + j0;
-  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < kPer / 8; ++q) {
+    for (int q = 0; q < PER / 8; ++q) {
       const uint4 v = reinterpret_cast<const uint4*>(src)[q];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -403,17 +407,18 @@ __device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (
   } else {
     const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? score_key(score_at(src, i)) : 0u;
+    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(score_at(src, i)) : 0u;
   }
 }
 
 // The same for keys already mapped (stage-2 candidates).
-__device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_t (&kv)[kPer]) {
-  const int j0 = threadIdx.x * kPer;
+template <int PER>
+__device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_t (&kv)[PER]) {
+  const int j0 = threadIdx.x * PER;
   const uint32_t* src = keys + j0;
-  if (j0 + kPer <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
 #pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const uint4 v = reinterpret_cast<const uint4*>(src)[q];
       kv[4 * q] = v.x;
       kv[4 * q + 1] = v.y;
@@ -423,7 +428,7 @@ __device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_
   } else {
     const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) kv[i] = i < m ? src[i] : 0u;
+    for (int i = 0; i < PER; ++i) kv[i] = i < m ? src[i] : 0u;
   }
 }
 
@@ -543,11 +548,263 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
   }
 }
 
+// ---- Sampled threshold: rows longer than kChunk when there are few of them ---------------------
+// One workgroup per row picks a threshold key T from evenly spaced samples (topk_sample_kernel);
+// workgroups of kFiltN entries then mark, one bit per entry, the row's keys above T and equal to
+// T (topk_filter_kernel); one workgroup per row selects the top k from the marked entries
+// (topk_select_kernel). With G keys above T and E equal to it: G >= k leaves the selection to
+// the G marked keys (at most kSelCap of them); G < k <= G + E makes T the k-th key, so the result
+// is every key above T plus the first k - G keys equal to it; a sample that misjudged the row
+// (G + E < k, or G > kSelCap) sends the row to an exact selection over all of its keys in the
+// select workgroup. Every case yields the unique top k, so which one ran never shows in the
+// result. These kernels run 1024 threads, few keys each: a decode call has too few rows to fill
+// the GPU, so each workgroup's latency, not the throughput, sets the time.
+constexpr int kSNT = 1024;                   // threads of the sampled path's workgroups
+constexpr int kSampPer = 2;                  // samples per thread
+constexpr int kSamp = kSNT * kSampPer;       // samples per row
+constexpr int kFiltPer = 8;                  // entries per thread of a filter workgroup
+constexpr int kFiltN = kSNT * kFiltPer;      // entries per filter workgroup
+constexpr int kSelCap = kSNT * kFiltPer;     // keys one select workgroup ranks
+
+// Samples of a row of n > 0 keys: positions floor(i n / s), i < s = min(n, kSamp). T is the r-th
+// largest sample: s evenly spaced samples hold about k s / n keys at or above the row's k-th key;
+// twice that plus 16 makes a shortfall unlikely unless the scores line up with the sample
+// positions, and then the exact fallback still gives the right result.
+__host__ __device__ __forceinline__ int sample_rank(int64_t n, int k) {
+  const int64_t s = n < kSamp ? n : kSamp;
+  const int64_t r = 2 * ((k * s + n - 1) / n) + 16;
+  return (int)(r < s ? r : s);
+}
+
+template <typename S>
+__global__ void __launch_bounds__(kSNT) topk_sample_kernel(TopkArgs a, uint32_t* thr) {
+  __shared__ int s_tmp[2 * kSNT / kWave + 2];
+  __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
+  const int qi = blockIdx.x;
+  const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
+  if (nv <= a.k) return;   // the select kernel writes such rows without a threshold
+  const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
+  const int64_t s = nv < kSamp ? nv : kSamp;
+  uint32_t kv[kSampPer];
+#pragma unroll
+  for (int u = 0; u < kSampPer; ++u) {
+    const int64_t i = (int64_t)threadIdx.x * kSampPer + u;
+    kv[u] = i < s ? score_key(score_at(row, i * nv / s)) : 0u;
+  }
+  clear_hist(s_hist, kSNT);
+  lds_sync();
+  int need_eq;
+  const uint32_t T = kth_key<kSNT, true>(kv, sample_rank(nv, a.k), s_hist, s_tmp, &need_eq);
+  if (threadIdx.x == 0) thr[qi] = T;
+}
+
+// Marks of the row's entries in blocks of 64 positions, in position order: {above T, equal to T}
+// as two 64-bit masks (uint4 {above lo, above hi, equal lo, equal hi}). Filter workgroup c covers
+// entries c kFiltN + 1024 u + t (u < kFiltPer): wave v's ballot for key u is the block of
+// positions c kFiltN + 1024 u + 64 v. Entries past the visible ones have key 0, below every real T.
+template <typename S>
+__global__ void __launch_bounds__(kSNT) topk_filter_kernel(TopkArgs a, int n_f, const uint32_t* thr,
+                                                           uint4* marks) {
+  const int qi = blockIdx.x / n_f;
+  const int c = blockIdx.x - qi * n_f;
+  const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
+  const int64_t base = (int64_t)c * kFiltN;
+  if (nv <= a.k || base >= nv) return;   // the select kernel reads no marks here
+  const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
+  uint32_t kv[kFiltPer];
+#pragma unroll
+  for (int u = 0; u < kFiltPer; ++u) {
+    const int64_t j = base + (int64_t)u * kSNT + threadIdx.x;
+    kv[u] = j < nv ? score_key(score_at(row, j)) : 0u;
+  }
+  const uint32_t T = thr[qi];
+  const int lane = threadIdx.x & (kWave - 1), v = threadIdx.x / kWave;
+  uint4* dst = marks + ((int64_t)qi * n_f + c) * (kFiltN / 64);
+#pragma unroll
+  for (int u = 0; u < kFiltPer; ++u) {
+    const uint64_t gt = __ballot(kv[u] > T);
+    const uint64_t eq = __ballot(kv[u] == T);
+    if (lane == 0)
+      dst[u * (kSNT / kWave) + v] =
+          make_uint4((uint32_t)gt, (uint32_t)(gt >> 32), (uint32_t)eq, (uint32_t)(eq >> 32));
+  }
+}
+
+// Exact top k of a whole row of n > k keys by one workgroup, kFiltN keys per pass: the same radix
+// select as kth_key (digits of the block's highest differing bit downwards) with the histograms
+// summed over passes, then an ordered compaction pass. The fallback of the sampled path.
+template <typename S>
+__device__ void select_row_passes(const S* row, int64_t n, int k, int32_t* out, int* hist,
+                                  int* s_tmp) {
+  constexpr int NT = kSNT;
+  uint32_t mx = 0, mn = ~0u;
+  for (int64_t b0 = 0; b0 < n; b0 += kFiltN) {
+    uint32_t kv[kFiltPer];
+    load_keys(row + b0, (int)(n - b0 < kFiltN ? n - b0 : kFiltN), kv);
+    uint32_t bx, bn;
+    block_range<NT>(kv, s_tmp, bx, bn);
+    mx = max(mx, bx);
+    mn = min(mn, bn);
+  }
+  uint32_t K = mx;
+  int kk = k;
+  if (mx != mn) {
+    const int p = 31 - __builtin_clz(mx ^ mn);
+    uint32_t pmask = p == 31 ? 0u : ~0u << (p + 1);
+    uint32_t prefix = mx & pmask;
+    int lo = p + 1;
+    while (lo > 0) {
+      const int hi = lo - 1;
+      lo = hi >= 10 ? hi - 10 : 0;
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+      clear_hist(hist, NT);
+      lds_sync();
+      for (int64_t b0 = 0; b0 < n; b0 += kFiltN) {
+        uint32_t kv[kFiltPer];
+        load_keys(row + b0, (int)(n - b0 < kFiltN ? n - b0 : kFiltN), kv);
+#pragma unroll
+        for (int i = 0; i < kFiltPer; ++i)
+          if ((kv[i] & pmask) == prefix) atomicAdd(&hist[(kv[i] >> lo) & dmask], 1);
+      }
+      lds_sync();
+      int count;
+      const uint32_t d = find_digit<NT>(hist, kk, s_tmp, count);
+      prefix |= d << lo;
+      pmask |= dmask << lo;
+    }
+    K = prefix;
+  }
+  // kk keys equal to K belong to the top k, the first ones in row order.
+  int written = 0, eq_left = kk;
+  for (int64_t b0 = 0; b0 < n && written < k; b0 += kFiltN) {
+    uint32_t kv[kFiltPer];
+    load_keys(row + b0, (int)(n - b0 < kFiltN ? n - b0 : kFiltN), kv);
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kFiltPer; ++i) {
+      gt += kv[i] > K;
+      eq += kv[i] == K;
+    }
+    int tot_gt, tot_eq;
+    block_scan<NT>(gt, s_tmp, tot_gt);
+    block_scan<NT>(eq, s_tmp, tot_eq);
+    compact<NT>(kv, K, eq_left, k - written, s_tmp,
+                [&](int o, int j, uint32_t) { out[written + o] = (int32_t)(b0 + j); });
+    const int taken = eq_left < tot_eq ? eq_left : tot_eq;
+    written += tot_gt + taken;
+    eq_left -= taken;
+  }
+}
+
+template <typename S>
+__global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, const uint4* marks) {
+  constexpr int NT = kSNT;
+  __shared__ int s_tmp[2 * NT / kWave + 2];
+  __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
+  __shared__ int s_pos[kSelCap];   // marked positions in row order
+  const int qi = blockIdx.x;
+  const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
+  int32_t* out = a.idx + (int64_t)qi * a.k;
+  if (nv <= a.k) {
+    for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
+  const uint4* mk = marks + (int64_t)qi * n_f * (kFiltN / 64);
+  // Thread t reads the mark blocks [t wpt, t wpt + wpt) of the row's nb blocks of 64 positions.
+  const int nb = (int)((nv + 63) / 64);
+  const int wpt = (nb + NT - 1) / NT;
+  const int b0 = threadIdx.x * wpt;
+  int cg = 0, ce = 0;
+  for (int i = 0; i < wpt; ++i) {
+    if (b0 + i < nb) {
+      const uint4 m = mk[b0 + i];
+      cg += __popc(m.x) + __popc(m.y);
+      ce += __popc(m.z) + __popc(m.w);
+    }
+  }
+  int G, E;
+  const int g_before = block_scan<NT>(cg, s_tmp, G);
+  const int e_before = block_scan<NT>(ce, s_tmp, E);
+  const int k = a.k;
+  if (G < k && k <= G + E) {
+    // T is the k-th key: every key above it, then the first k - G keys equal to it.
+    int take = k - G - e_before;
+    take = take < 0 ? 0 : (take > ce ? ce : take);
+    int tot;
+    int off = block_scan<NT>(cg + take, s_tmp, tot);
+    for (int i = 0; i < wpt && b0 + i < nb; ++i) {
+      const uint4 m = mk[b0 + i];
+      uint64_t e = ((uint64_t)m.w << 32) | m.z, keep = 0;
+      while (e != 0u && take > 0) {   // the lowest `take` bits of the equal marks
+        const uint64_t low = e & (0ull - e);
+        keep |= low;
+        e ^= low;
+        --take;
+      }
+      uint64_t bits = (((uint64_t)m.y << 32) | m.x) | keep;
+      while (bits != 0u) {
+        const int b = __builtin_ctzll(bits);
+        bits &= bits - 1u;
+        if (off < k) s_hist[off] = (b0 + i) * 64 + b;
+        ++off;
+      }
+    }
+    lds_sync();
+    for (int i = threadIdx.x; i < k; i += NT) out[i] = s_hist[i];
+    return;
+  }
+  if (G >= k && G <= kSelCap) {
+    // The marked keys above T, in row order, then the top k among them.
+    int off = g_before;
+    for (int i = 0; i < wpt && b0 + i < nb; ++i) {
+      const uint4 m = mk[b0 + i];
+      uint64_t bits = ((uint64_t)m.y << 32) | m.x;
+      while (bits != 0u) {
+        const int b = __builtin_ctzll(bits);
+        bits &= bits - 1u;
+        s_pos[off++] = (b0 + i) * 64 + b;
+      }
+    }
+    lds_sync();
+    uint32_t kv[kFiltPer];
+#pragma unroll
+    for (int u = 0; u < kFiltPer; ++u) {
+      const int j = threadIdx.x * kFiltPer + u;
+      kv[u] = j < G ? score_key(score_at(row, s_pos[j])) : 0u;
+    }
+    clear_hist(s_hist, NT);
+    lds_sync();
+    int need_eq;
+    const uint32_t K = kth_key<NT, true>(kv, k, s_hist, s_tmp, &need_eq);
+    compact<NT>(kv, K, need_eq, k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = s_pos[j]; });
+    for (int i = threadIdx.x; i < k; i += NT) out[i] = s_hist[i];
+    return;
+  }
+  select_row_passes(row, nv, k, out, s_hist, s_tmp);
+}
+
 int n_chunks_for(int64_t N) { return (int)((N + kWideChunk - 1) / kWideChunk); }
 
 }  // namespace
 
+// The sampled path serves rows longer than kWideChunk when they occupy few filter workgroups (a
+// latency-bound call) and k is small enough for the candidate list to fit one select workgroup
+// with a wide margin: about 2 k + 16 N / kSamp candidates are expected. Rows of up to kWideChunk
+// keep the single 1024-thread workgroup, which measured as fast as the three sampled-path
+// launches at 32768 entries (24 against 25 us for 64 rows) and faster below.
+bool use_sampled(int nq, int64_t N, int k) {
+  const int64_t n_f = (N + kFiltN - 1) / kFiltN;
+  const int64_t s = N < kSamp ? N : kSamp;
+  return N > kWideChunk && k <= kMaxK && (int64_t)nq * n_f <= 2048 &&
+         2 * (int64_t)k + 16 * ((N + s - 1) / s) <= kSelCap / 2;
+}
+
+size_t sampled_marks_offset(int nq) { return ((size_t)nq * sizeof(uint32_t) + 255) / 256 * 256; }
+
 size_t topk_workspace(int nq, int64_t N, int k) {
+  if (use_sampled(nq, N, k))
+    return sampled_marks_offset(nq) + (size_t)nq * ((N + kFiltN - 1) / kFiltN) * (kFiltN / 64) * sizeof(uint4);
   if (N <= kWideChunk) return 0;
   const int nc = n_chunks_for(N);
   return (size_t)nq * nc * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
@@ -563,6 +820,19 @@ template <typename S>
 hipError_t launch_topk_t(const TopkArgs& a, hipStream_t s) {
   if (a.N <= kChunk) {
     topk_row_kernel<256, S><<<a.Q.nq, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (use_sampled(a.Q.nq, a.N, a.k)) {
+    const int n_f = (int)((a.N + kFiltN - 1) / kFiltN);
+    uint32_t* thr = static_cast<uint32_t*>(a.ws);
+    uint4* marks = reinterpret_cast<uint4*>(static_cast<char*>(a.ws) + sampled_marks_offset(a.Q.nq));
+    topk_sample_kernel<S><<<a.Q.nq, kSNT, 0, s>>>(a, thr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    topk_filter_kernel<S><<<(unsigned)((int64_t)a.Q.nq * n_f), kSNT, 0, s>>>(a, n_f, thr, marks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    topk_select_kernel<S><<<a.Q.nq, kSNT, 0, s>>>(a, n_f, marks);
     return hipGetLastError();
   }
   if (a.N <= kWideChunk) {

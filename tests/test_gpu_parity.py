@@ -289,6 +289,64 @@ def test_topk_exact_with_ties_and_long_rows(N, k):
         assert (got[q] == want).all(), (q, nv)
 
 
+def _topk_check(sc, pos, N, k, m=4):
+    from oracle import csa_oracle as orc
+    nq = sc.shape[0]
+    seq = np.zeros(nq, dtype=np.int32)
+    scores = torch.tensor(sc, dtype=torch.float32, device="cuda")
+    idx = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+    print(f"[topk] nq={nq} N={N} k={k}", flush=True)
+    lib.csa_topk(torch.tensor(seq, device="cuda"), torch.tensor(pos, device="cuda"), scores,
+                 idx, N, m, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    s64 = scores.cpu().numpy().astype(np.float64)
+    for q in range(nq):
+        want, _ = orc.topk(s64[q], orc.n_visible(int(pos[q]), m, N), k)
+        assert (got[q] == want).all(), q
+
+
+@pytest.mark.parametrize("N,k", [(262144, 1024), (65536, 1024), (40000, 300)])
+def test_topk_sampled_threshold_misses_take_the_exact_fallback(N, k):
+    # Long rows of a call with few rows pick a threshold from evenly spaced samples (positions
+    # floor(i n / s), s = min(n, 2048)). Rows whose scores line up with those positions defeat
+    # it: high scores at exactly the sampled positions leave fewer than k keys at or above the
+    # threshold, low ones there leave far too many above it. Both must still give the exact top
+    # k, as must rows whose scores grow with the position and rows with k-th key ties.
+    rng = np.random.default_rng(N + 3 * k)
+    m = 4
+    nv = N
+    s = min(nv, 2048)
+    samp = (np.arange(s, dtype=np.int64) * nv) // s
+    rows = []
+    r = rng.random(N).astype(np.float32)
+    a = r.copy()
+    a[samp] = 100.0 + np.arange(s, dtype=np.float32)            # samples highest
+    rows.append(a)
+    b = 10.0 + r
+    b[samp] = -100.0 - np.arange(s, dtype=np.float32)           # samples lowest
+    rows.append(b)
+    rows.append(np.arange(N, dtype=np.float32) / N)               # grows with the position
+    c = np.round(rng.standard_normal(N) * 2).astype(np.float32)  # few distinct values
+    rows.append(c)
+    d = rng.standard_normal(N).astype(np.float32)
+    d[samp] = d.max() + 1.0                                       # samples tie at the top
+    rows.append(d)
+    sc = np.stack(rows)
+    pos = np.full(sc.shape[0], 4 * N - 1, dtype=np.int64)
+    _topk_check(sc, pos, N, k, m)
+
+
+def test_topk_many_long_rows():
+    # Enough rows of 20000 entries that each row takes one 1024-thread workgroup.
+    rng = np.random.default_rng(11)
+    nq, N, k = 800, 20000, 1024
+    sc = rng.standard_normal((nq, N)).astype(np.float32)
+    sc[::3] = np.round(sc[::3] * 4) / 4
+    pos = (4 * N - 1 - 97 * np.arange(nq)).astype(np.int64)
+    _topk_check(sc, pos, N, k)
+
+
 @pytest.mark.parametrize("N,k", [(8192, 1024), (30000, 1024), (3000, 257), (6000, 1)])
 def test_topk_exact_continuous_and_extreme_scores(N, k):
     # Continuous scores take the selection's equal-width score bins; one score far above the
