@@ -161,6 +161,9 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
   *reinterpret_cast<f16x8*>(kvb + kTK * 1024 + rr * 128 + 16 * (pr ^ swz(rr))) = rh;
 }
 
+// TOK: token selection (a.tok_m > 0). The entry form is compiled with the token fields known to
+// be zero, so its per-tile key arithmetic has no branches.
+template <bool TOK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int RG = 4;
@@ -198,7 +201,8 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   const int qrow_i = 32 * rg + (lane & 31);
   if (threadIdx.x == 0) s_flag = 0;
 
-  const KeyList kl = make_key_list(a, qi);
+  KeyList kl = make_key_list(a, qi);
+  if constexpr (!TOK) kl.tok_m = 0;
   const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
   const int64_t k0 = (int64_t)split * per_split;
   const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
@@ -447,7 +451,10 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
 
 hipError_t launch_attend_fp8(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
-  attend_fp8_kernel<<<grid, 256, 0, s>>>(a, p);
+  if (a.tok_m > 0)
+    attend_fp8_kernel<true><<<grid, 256, 0, s>>>(a, p);
+  else
+    attend_fp8_kernel<false><<<grid, 256, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

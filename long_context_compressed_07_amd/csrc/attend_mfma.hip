@@ -442,9 +442,11 @@ enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 // queries, and the merge takes the splits in a fixed order: a query's outputs are bitwise the same
 // whatever batch it is in and wherever in the batch it sits (deepseek.csdn.net "一文搞懂
 // DeepSeek", V4 的其他升级: deterministic, batch-invariant kernels). keys_per_split is the
-// kernel's granularity: fp8 (the decode cache) 256 keys, so that a 1152-key CSA list takes 4 splits
-// and an 8192-entry HCA list 32; bf16 (the prefill path, many queries per call) 8192, so that the
-// prefill workloads run unsplit; at most 64 splits.
+// kernel's granularity: fp8 (the decode cache) 288 keys, so that a 1152-key CSA list takes 4
+// splits and an 8192-entry HCA list 28 (the hybrid decode's 8 queries then fill 224 of the 256
+// CUs with their HCA layer and leave 32 for the 8 x 4 CSA workgroups that run beside it); bf16
+// (the prefill path, many queries per call) 8192, so that the prefill workloads run unsplit; at
+// most 64 splits.
 int splits_by_keys(int64_t max_keys, int64_t keys_per_split) {
   const int64_t ns = max_keys / keys_per_split;
   return (int)(ns < 1 ? 1 : (ns > 64 ? 64 : ns));
@@ -467,7 +469,7 @@ MfmaPlan make_plan(int H, int64_t max_keys, int kind) {
     p.f8_dma = 1;
     p.rg = 4;
     p.head_groups = groups32 / 4;
-    p.n_split = splits_by_keys(max_keys, 256);
+    p.n_split = splits_by_keys(max_keys, 288);
     return p;
   }
   // fp16-staging kernel: as many 32-head groups per staged tile as the head count allows.

@@ -142,6 +142,10 @@ __device__ __forceinline__ void load_q16_lds(int base, v4i (&q)[36]) {
       : "memory");
 }
 
+// TOK: token selection (a.tok_m > 0). The entry form is compiled with the token fields known to
+// be zero, so its per-tile key arithmetic has no branches and the compiler can place it among
+// the MFMAs.
+template <bool TOK>
 __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int TK = kPpTK;
   constexpr int R = kPpR;
@@ -167,7 +171,8 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
   const int hbase = hgrp * R;
   if (threadIdx.x == 0) s_flag = 0;
 
-  const KeyList kl = make_key_list(a, qi);
+  KeyList kl = make_key_list(a, qi);
+  if constexpr (!TOK) kl.tok_m = 0;
   const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
   const int64_t k0 = (int64_t)split * per_split;
   const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
@@ -542,7 +547,10 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
 
 hipError_t launch_attend_pp(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
-  attend_pp_kernel<<<grid, 512, 0, s>>>(a, p);
+  if (a.tok_m > 0)
+    attend_pp_kernel<true><<<grid, 512, 0, s>>>(a, p);
+  else
+    attend_pp_kernel<false><<<grid, 512, 0, s>>>(a, p);
   return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ class Step:
             need = lib.hca_attend_workspace_bytes(self.nq, wl.H, d_c, nh)
             self.ws["hca"] = torch.empty(max(need, 1), dtype=torch.uint8, device=self.dev)
             # The HCA layer reads nothing the CSA layer writes: it runs on a second stream (default
-            # priority, like every stream here) beside the CSA index, top-k and attention.
+            # priority, like every stream here) beside the CSA attention.
             self._side = torch.cuda.Stream(device=self.dev)
             self._fork = torch.cuda.Event()
             self._join = torch.cuda.Event()
@@ -139,17 +139,21 @@ class Step:
             self.compress()
             self.hca()
             return
+        if wl.compress_on_path:
+            self.compress()
+        self.index()
+        self.topk()
         if wl.kind == "hybrid_decode":
+            # The HCA layer needs nothing the CSA layer computes; it starts once the CSA index and
+            # top-k, which fill the GPU on their own, are done, so that its attention shares the
+            # CUs with the CSA attention (32 workgroups) instead of holding every CU while the
+            # index waits for them.
             main = torch.cuda.current_stream(self.dev)
             self._fork.record(main)
             self._side.wait_event(self._fork)
             with torch.cuda.stream(self._side):
                 self.hca()
             self._join.record(self._side)
-        if wl.compress_on_path:
-            self.compress()
-        self.index()
-        self.topk()
         self.attend()
         if wl.kind == "hybrid_decode":
             main.wait_event(self._join)
