@@ -69,14 +69,21 @@ __device__ __forceinline__ void merge_partials8(const AttendArgs& a, const AttnP
 
 
 // The work item of this workgroup. Workgroups go to the 8 XCDs in turn (workgroup b to XCD
-// b mod 8); this mapping gives each XCD a contiguous range of items, so that the key splits and
-// head groups of one query, and neighbouring queries, share that XCD's L2. The last
-// gridDim.x mod 8 workgroups keep their own index.
+// b mod 8); this mapping gives each XCD contiguous runs of items, so that the key splits and head
+// groups of one query, and neighbouring queries, share that XCD's L2. Grids of at least 8 x 2048
+// items are dealt out in runs of 512 (run r to XCD r mod 8), so that every XCD gets its share of
+// each region of the item range: under causality the first queries' key lists are short, and
+// one contiguous range per XCD would leave the XCD holding them idle at the end. Smaller grids
+// give each XCD one contiguous range. The last gridDim.x mod 8 workgroups keep their own index.
 __device__ __forceinline__ int xcd_item() {
+  constexpr int kRun = 512;
   const int b = blockIdx.x, n = gridDim.x;
   const int n8 = n & ~7;
   if (b >= n8) return b;
-  return (b & 7) * (n8 >> 3) + (b >> 3);
+  const int m = n8 >> 3;              // items per XCD
+  const int x = b & 7, j = b >> 3;    // XCD, and this workgroup's rank on it
+  if (m < 4 * kRun || m % kRun != 0) return x * m + j;
+  return ((j / kRun) * 8 + x) * kRun + j % kRun;
 }
 
 // Four values of a normalised partial output row (o / l in fp16; zeros when l == 0).

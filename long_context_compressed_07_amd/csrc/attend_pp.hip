@@ -158,6 +158,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
   __shared__ float s_l[2][R];           // per key half: softmax sums
   __shared__ float s_m[R];              // reference maxima
   __shared__ int s_flag;
+  __shared__ int s_last_sel;            // last selection slot that names an entry
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -169,18 +170,27 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
   const int hgrp = rem / plan.n_split;
   const int split = rem - hgrp * plan.n_split;
   const int hbase = hgrp * R;
-  if (threadIdx.x == 0) s_flag = 0;
+  if (threadIdx.x == 0) {
+    s_flag = 0;
+    s_last_sel = -1;
+  }
 
   KeyList kl = make_key_list(a, qi);
   if constexpr (!TOK) kl.tok_m = 0;
-  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
-  const int64_t k0 = (int64_t)split * per_split;
-  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
-  const RowBases rbases = row_bases(a, kl.b);
-  const bool sel_dma = kl.sel != nullptr;   // CSA: selection slots come from idx
-  const KeyCodes32 kc = key_codes32(kl, ke);
-  const int nt = ke > k0 ? (int)((ke - k0 + TK - 1) / TK) : 0;
-  const float cscale = a.sm_scale * kLog2e;
+  // Trailing selection slots that name no entry (-1, or a row past the entry store: a query that
+  // sees fewer than k entries) contribute nothing; the key list ends after the last slot that
+  // names one, so such queries skip those tiles. The slots are loaded (coalesced) before the
+  // queries' DMA and reduced after it, so waiting for them does not wait for the queries.
+  const bool trim = !TOK && kl.sel != nullptr;
+  constexpr int kTrimPer = 4;   // slots per thread held in registers; more are read in a loop
+  int sv[kTrimPer];
+  if (trim) {
+#pragma unroll
+    for (int u = 0; u < kTrimPer; ++u) {
+      const int j = (int)threadIdx.x + 512 * u;
+      sv[u] = j < kl.n_sel ? kl.sel[j] : -1;
+    }
+  }
 
   // Prologue, in parallel: every wave copies its share of the queries by DMA, while the PV
   // waves compute the codes of tiles 0-2, copy the selection slots of tiles 3 and 4 and issue the
@@ -198,6 +208,35 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       __builtin_amdgcn_global_load_lds(src, (lds_char*)(&kv[2][0] + 1024 * F), 16, 0, 0);
     }
   }
+
+  if (trim) {
+    int last = -1;
+#pragma unroll
+    for (int u = 0; u < kTrimPer; ++u) {
+      const int j = (int)threadIdx.x + 512 * u;
+      last = sv[u] >= 0 && sv[u] < kl.ent_rows ? j : last;
+    }
+    for (int j = (int)threadIdx.x + 512 * kTrimPer; j < kl.n_sel; j += 512) {
+      const int v = kl.sel[j];
+      last = v >= 0 && v < kl.ent_rows ? j : last;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+    lds_barrier();   // s_last_sel initialised
+    if (lane == 0) atomicMax(&s_last_sel, last);
+    lds_barrier();
+    kl.n_sel = s_last_sel + 1;
+    kl.total = kl.n_sel + kl.n_win;
+  }
+  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
+  const int64_t k0 = (int64_t)split * per_split;
+  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
+  const RowBases rbases = row_bases(a, kl.b);
+  const bool sel_dma = kl.sel != nullptr;   // CSA: selection slots come from idx
+  const KeyCodes32 kc = key_codes32(kl, ke);
+  const int nt = ke > k0 ? (int)((ke - k0 + TK - 1) / TK) : 0;
+  const float cscale = a.sm_scale * kLog2e;
+
   if (w < 4) {
     // ================================ QK waves ================================
     const int rg = w & 1, kh = w >> 1;

@@ -565,6 +565,7 @@ constexpr int kSamp = kSNT * kSampPer;       // samples per row
 constexpr int kFiltPer = 8;                  // entries per thread of a filter workgroup
 constexpr int kFiltN = kSNT * kFiltPer;      // entries per filter workgroup
 constexpr int kSelCap = kSNT * kFiltPer;     // keys one select workgroup ranks
+constexpr int kMaxWpt = 8;                   // mark blocks (64 entries) per select thread
 
 // Samples of a row of n > 0 keys: positions floor(i n / s), i < s = min(n, kSamp). T is the r-th
 // largest sample: s evenly spaced samples hold about k s / n keys at or above the row's k-th key;
@@ -711,17 +712,18 @@ __global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, 
   }
   const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
   const uint4* mk = marks + (int64_t)qi * n_f * (kFiltN / 64);
-  // Thread t reads the mark blocks [t wpt, t wpt + wpt) of the row's nb blocks of 64 positions.
+  // Thread t holds the mark blocks [t wpt, t wpt + wpt) of the row's nb blocks of 64 positions
+  // (wpt <= kMaxWpt: use_sampled bounds the row length), loaded once.
   const int nb = (int)((nv + 63) / 64);
   const int wpt = (nb + NT - 1) / NT;
   const int b0 = threadIdx.x * wpt;
+  uint4 mr[kMaxWpt];
   int cg = 0, ce = 0;
-  for (int i = 0; i < wpt; ++i) {
-    if (b0 + i < nb) {
-      const uint4 m = mk[b0 + i];
-      cg += __popc(m.x) + __popc(m.y);
-      ce += __popc(m.z) + __popc(m.w);
-    }
+#pragma unroll
+  for (int i = 0; i < kMaxWpt; ++i) {
+    mr[i] = i < wpt && b0 + i < nb ? mk[b0 + i] : make_uint4(0u, 0u, 0u, 0u);
+    cg += __popc(mr[i].x) + __popc(mr[i].y);
+    ce += __popc(mr[i].z) + __popc(mr[i].w);
   }
   int G, E;
   const int g_before = block_scan<NT>(cg, s_tmp, G);
@@ -733,8 +735,9 @@ __global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, 
     take = take < 0 ? 0 : (take > ce ? ce : take);
     int tot;
     int off = block_scan<NT>(cg + take, s_tmp, tot);
-    for (int i = 0; i < wpt && b0 + i < nb; ++i) {
-      const uint4 m = mk[b0 + i];
+#pragma unroll
+    for (int i = 0; i < kMaxWpt; ++i) {
+      const uint4 m = mr[i];
       uint64_t e = ((uint64_t)m.w << 32) | m.z, keep = 0;
       while (e != 0u && take > 0) {   // the lowest `take` bits of the equal marks
         const uint64_t low = e & (0ull - e);
@@ -757,8 +760,9 @@ __global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, 
   if (G >= k && G <= kSelCap) {
     // The marked keys above T, in row order, then the top k among them.
     int off = g_before;
-    for (int i = 0; i < wpt && b0 + i < nb; ++i) {
-      const uint4 m = mk[b0 + i];
+#pragma unroll
+    for (int i = 0; i < kMaxWpt; ++i) {
+      const uint4 m = mr[i];
       uint64_t bits = ((uint64_t)m.y << 32) | m.x;
       while (bits != 0u) {
         const int b = __builtin_ctzll(bits);
@@ -796,7 +800,8 @@ int n_chunks_for(int64_t N) { return (int)((N + kWideChunk - 1) / kWideChunk); }
 bool use_sampled(int nq, int64_t N, int k) {
   const int64_t n_f = (N + kFiltN - 1) / kFiltN;
   const int64_t s = N < kSamp ? N : kSamp;
-  return N > kWideChunk && k <= kMaxK && (int64_t)nq * n_f <= 2048 &&
+  return N > kWideChunk && N <= (int64_t)kSNT * 64 * kMaxWpt && k <= kMaxK &&
+         (int64_t)nq * n_f <= 2048 &&
          2 * (int64_t)k + 16 * ((N + s - 1) / s) <= kSelCap / 2;
 }
 
