@@ -498,18 +498,12 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       }
       lds_barrier();
     }
-    bool overflow = false;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) overflow |= !__builtin_isfinite(o[mt][rg][i]);
-    if (__any(overflow)) atomicOr(&s_flag, 1);
-    lds_barrier();                    // epilogue barrier 1: sums, maxima and flag complete
-    if (threadIdx.x == 256) plan.flags[item] = s_flag;
+    lds_barrier();                    // epilogue barrier 1: sums and maxima complete
     // Outputs (n_split == 1: o / l in fp32) or partials (o / l in fp16, and (m, l)), one 32-head
-    // row group at a time, staged in the (idle) tile buffers by the PV waves, written as rows.
+    // row group at a time, staged in the (idle) tile buffers by the PV waves, written as rows. A
+    // staged value that is not finite in its type (fp16 P overflowed) flags the workgroup for the
+    // fp32 recompute; the flag is complete after the last barrier.
+    bool bad = false;
     char* stage = &kv[0][0];
     const int pt = threadIdx.x - 256;   // 0 .. 255 over the PV waves
 #pragma unroll
@@ -527,10 +521,16 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              x[u] = o[mt][rg][4 * j + u] * inv;
+              bad |= !(__builtin_fabsf(x[u]) <= 3.4028235e38f);
+            }
             *reinterpret_cast<float4*>(row + (32 * mt + 8 * j) * 4) =
-                make_float4(o[mt][rg][4 * j] * inv, o[mt][rg][4 * j + 1] * inv,
-                            o[mt][rg][4 * j + 2] * inv, o[mt][rg][4 * j + 3] * inv);
+                make_float4(x[0], x[1], x[2], x[3]);
+          }
         if (a.lse != nullptr && p == 0 && hi == 0)
           a.lse[(int64_t)qi * a.H + head] =
               l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
@@ -540,16 +540,23 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              x[u] = o[mt][rg][4 * j + u] * inv;
+              bad |= !(__builtin_fabsf(x[u]) <= 65504.f);
+            }
             *reinterpret_cast<h4*>(row + (32 * mt + 8 * j) * 2) =
-                h4{(_Float16)(o[mt][rg][4 * j] * inv), (_Float16)(o[mt][rg][4 * j + 1] * inv),
-                   (_Float16)(o[mt][rg][4 * j + 2] * inv), (_Float16)(o[mt][rg][4 * j + 3] * inv)};
+                h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+          }
         if (p == 0 && hi == 0) {
           const int64_t pidx = row0 + (lane & 31);
           plan.ws_ml[pidx * 2] = m;
           plan.ws_ml[pidx * 2 + 1] = l;
         }
       }
+      if (rg == 1 && __any(bad)) atomicOr(&s_flag, 1);
       lds_barrier();                  // rows staged (the QK waves take part in every barrier)
       if (plan.n_split == 1) {
         // 16-byte chunk k of head row h: thread pt takes k = pt & 127 of rows pt / 128 + 2 u.
@@ -579,6 +586,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       }
       lds_barrier();                  // rows written, staging area free
     }
+    if (threadIdx.x == 256) plan.flags[item] = s_flag;
   }
 }
 
