@@ -4,8 +4,12 @@
 // Step 3 (only the top-k compressed rows by indexer score enter attention). Ties go to the lower
 // index and the output lists indices in ascending order (this library's reading).
 //
-// Algorithm (deterministic: the result depends only on the keys' order). Scores map to order-preserving 32-bit keys. Each
-// thread holds a contiguous segment of PER keys in registers. Single-stage rows first look for the
+// Algorithm (deterministic: the result depends only on the keys' order). Scores map to
+// order-preserving 32-bit keys, held in registers, PER per thread: wave v of a workgroup holds
+// 64 PER consecutive positions as groups of 256, lane l keys 4 l .. 4 l + 3 of each group
+// (key_pos), so that every load instruction of a wave reads one contiguous span. The selection is
+// bound by vector ALU work per key (few workgroups per CU, one key per lane and instruction), so
+// each step keeps that work small. Single-stage rows first look for the
 // k-th largest key K in equal-width score bins (kth_key_by_value: one histogram, then a direct
 // ranking of the few keys in K's bin). Otherwise, and when that bin is crowded, K is found by a
 // radix select: the block's largest and smallest keys fix the bits every key shares; then, from
@@ -13,9 +17,10 @@
 // bits) of the keys that match the digits found so far, and a block scan over the histogram
 // locates the digit of the k-th key and its rank among the keys of that digit. Starting at the
 // highest differing bit spreads clustered keys over the histogram, which keeps LDS atomic
-// conflicts low. Compaction keeps every key > K and the lowest-position keys == K: two block scans
-// give every segment its output offset; selected positions are staged in LDS and written out with
-// coalesced stores.
+// conflicts low. Compaction keeps every key > K and the lowest-position keys == K: per-wave
+// counts from ballots, one exchange of them between the waves, then each selected key's output
+// offset from lane-mask counts (mbcnt) in position order; selected positions are staged in LDS and
+// written out with coalesced stores.
 //
 // Rows of up to kChunk (8192) visible entries: one 256-thread workgroup per row; rows of up to
 // kWideChunk (32768): one 1024-thread workgroup per row (the same code, 32 keys per thread).
@@ -98,6 +103,22 @@ __device__ __forceinline__ uint32_t wave_incl_min(uint32_t x) {
 }
 
 __device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+
+// Position of key i of this thread within its workgroup's span of NT PER positions: wave v holds
+// [64 PER v, 64 PER (v + 1)) as PER / 4 groups of 256 positions, lane l positions 4 l .. 4 l + 3
+// of each group. Position order is (wave, group, lane, key within the lane's four).
+template <int PER>
+__device__ __forceinline__ int key_pos(int i) {
+  static_assert(PER % 4 == 0, "groups of four keys per lane");
+  return (int)(threadIdx.x / kWave) * (kWave * PER) + 256 * (i >> 2) +
+         4 * (int)(threadIdx.x & (kWave - 1)) + (i & 3);
+}
+
+// Number of set bits of the wave mask m in lanes below this one, plus acc.
+__device__ __forceinline__ int mbcnt(uint64_t m, int acc) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)acc));
+}
 
 // Exclusive prefix sum (in thread order) of a per-thread count over the block, and the total.
 // s_tmp: NT / 64 ints.
@@ -213,9 +234,22 @@ __device__ bool kth_key_by_value(const uint32_t (&kv)[PER], int k, float f0, flo
     const int b = (int)((key_score(key) - f0) * scale);   // >= 0: key_score(key) >= f0
     return b < kBins - 1 ? b : kBins - 1;
   };
+  // Each key's bin, kept from the histogram pass for the gather below: two 16-bit fields per
+  // word, 0xffff for padding keys.
+  uint32_t bp[(PER + 1) / 2];
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (kv[i] != 0u) atomicAdd(&hist[bin(kv[i])], 1);
+  for (int i = 0; i < PER; ++i) {
+    uint32_t b = 0xffffu;
+    if (kv[i] != 0u) {
+      b = (uint32_t)bin(kv[i]);
+      atomicAdd(&hist[b], 1);
+    }
+    if (i & 1)
+      bp[i >> 1] |= b << 16;
+    else
+      bp[i >> 1] = b;
+  }
+  auto bin_of = [&](int i) { return (bp[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
   lds_sync();
   int kk = k, count;
   const int d = (int)find_digit<NT>(hist, kk, s_tmp, count);
@@ -224,17 +258,17 @@ __device__ bool kth_key_by_value(const uint32_t (&kv)[PER], int k, float f0, flo
     lds_sync();
     return false;
   }
-  // The keys of bin d, in position order, into the second histogram's space.
+  // The keys of bin d (in any order: only their values matter), into the second histogram's space.
   uint32_t* s_cand = reinterpret_cast<uint32_t*>(hist + kBins);
   int mine = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) mine += kv[i] != 0u && bin(kv[i]) == d;
+  for (int i = 0; i < PER; ++i) mine += bin_of(i) == (uint32_t)d;
   int total;
   int off = block_scan<NT>(mine, s_tmp, total);
   if (mine > 0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (kv[i] != 0u && bin(kv[i]) == d) s_cand[off++] = kv[i];
+      if (bin_of(i) == (uint32_t)d) s_cand[off++] = kv[i];
   }
   // Padded with zero keys (below every real key) to a multiple of 16 for the 16-byte reads.
   const int t = threadIdx.x;
@@ -328,34 +362,79 @@ __device__ uint32_t kth_key(const uint32_t (&kv)[PER], int k, int* hist, int* s_
   return prefix;
 }
 
-// Calls put(o, j, key) for the top k in ascending position order o = 0 .. k-1 (j = PER t + i for
-// key kv[i] of thread t): keys > K and the first need_eq keys == K. Ends with an LDS barrier.
+// Calls put(o, j, key) for the top k in ascending position order o = 0 .. k-1 (j = key_pos(i) for
+// key kv[i]): keys > K and the first need_eq keys == K. The block's numbers of keys > K and == K
+// go to *tot_gt and *tot_eq when given. Ends with an LDS barrier. s_tmp: 2 NT / 64 ints.
 template <int NT, int PER, typename Put>
 __device__ void compact(const uint32_t (&kv)[PER], uint32_t K, int need_eq, int k, int* s_tmp,
-                        Put put) {
+                        Put put, int* tot_gt = nullptr, int* tot_eq = nullptr) {
   // Padding keys (0) are below every real key, and K is a real key (>= 1), so they never count.
-  const int j0 = threadIdx.x * PER;
-  int gt = 0, eq = 0;
+  constexpr int NW = NT / kWave;
+  const int wv = threadIdx.x / kWave;
+  int gl = 0, el = 0;   // this lane's keys > K and == K
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    gt += kv[i] > K;
-    eq += kv[i] == K;
+    gl += kv[i] > K;
+    el += kv[i] == K;
   }
-  int total;
-  const int eq_before = block_scan<NT>(eq, s_tmp, total);
-  int take_eq = need_eq - eq_before;
-  take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
-  int off = block_scan<NT>(gt + take_eq, s_tmp, total);
-  int eq_left = take_eq;
+  // The wave's counts, both in one sum (at most 64 PER < 2^16 each).
+  const int both = wave_incl_sum(gl | (el << 16));
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) {
+    s_tmp[wv] = both & 0xffff;
+    s_tmp[NW + wv] = both >> 16;
+  }
+  lds_sync();
+  int g_before = 0, e_before = 0, tg = 0, te = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    bool take = kv[i] > K;
-    if (kv[i] == K && eq_left > 0) {
-      take = true;
-      --eq_left;
+  for (int w = 0; w < NW; ++w) {
+    const int g = s_tmp[w], e = s_tmp[NW + w];
+    g_before += w < wv ? g : 0;
+    e_before += w < wv ? e : 0;
+    tg += g;
+    te += e;
+  }
+  lds_sync();   // s_tmp is free again
+  if (tot_gt != nullptr) *tot_gt = tg;
+  if (tot_eq != nullptr) *tot_eq = te;
+  const int ne = need_eq < 0 ? 0 : need_eq;
+  // Selected keys before this wave, and keys == K before the current group.
+  int off = g_before + (e_before < ne ? e_before : ne);
+  int eseen = e_before;
+  const bool take_all_eq = te <= ne;   // uniform: every key == K belongs to the top k
+  const int p0 = key_pos<PER>(0);
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    bool sel[4];
+    if (take_all_eq) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sel[c] = kv[4 * q + c] >= K;
+    } else {
+      bool e[4];
+      uint64_t me[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        e[c] = kv[4 * q + c] == K;
+        me[c] = __ballot(e[c]);
+      }
+      // Rank of each key == K among the row's keys == K, in position order.
+      int r = mbcnt(me[3], mbcnt(me[2], mbcnt(me[1], mbcnt(me[0], eseen))));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sel[c] = kv[4 * q + c] > K || (e[c] && r < ne);
+        r += e[c];
+      }
+      eseen += __popcll(me[0]) + __popcll(me[1]) + __popcll(me[2]) + __popcll(me[3]);
     }
-    if (take && (unsigned)off < (unsigned)k) put(off, j0 + i, kv[i]);
-    off += take;
+    uint64_t ms[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ms[c] = __ballot(sel[c]);
+    int o = mbcnt(ms[3], mbcnt(ms[2], mbcnt(ms[1], mbcnt(ms[0], off))));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (sel[c] && (unsigned)o < (unsigned)k) put(o, p0 + 256 * q + c, kv[4 * q + c]);
+      o += sel[c];
+    }
+    off += __popcll(ms[0]) + __popcll(ms[1]) + __popcll(ms[2]) + __popcll(ms[3]);
   }
   lds_sync();
 }
@@ -366,77 +445,98 @@ __device__ __forceinline__ float score_at(const uint16_t* row, int64_t j) {
   return __uint_as_float((uint32_t)row[j] << 16);
 }
 
-// Loads keys [PER t, PER t + PER) of a row of n scores (0 beyond n): 16-byte loads for whole,
-// aligned segments, element by element only for the segment holding the row's end.
+// Loads this thread's keys (positions key_pos(i)) of a row of n scores, 0 beyond n: one 16-byte
+// load per group of four that lies inside a 16-byte aligned row, element by element otherwise.
 template <int PER>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[PER]) {
-  const int j0 = threadIdx.x * PER;
-  const float* src = row + j0;
-  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  const int p0 = key_pos<PER>(0);
+  if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(src)[q];
-      kv[4 * q] = score_key(v.x);
-      kv[4 * q + 1] = score_key(v.y);
-      kv[4 * q + 2] = score_key(v.z);
-      kv[4 * q + 3] = score_key(v.w);
-    }
-  } else {
-    const int m = n - j0;
+      const int p = p0 + 256 * q;
+      if (p + 4 <= n) {
+        const float4 v = *reinterpret_cast<const float4*>(row + p);
+        kv[4 * q] = score_key(v.x);
+        kv[4 * q + 1] = score_key(v.y);
+        kv[4 * q + 2] = score_key(v.z);
+        kv[4 * q + 3] = score_key(v.w);
+      } else {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(src[i]) : 0u;
-  }
-}
-
-// bf16 scores: 16-byte loads of 8 codes; each code is the high half of its fp32 value.
-template <int PER>
-__device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (&kv)[PER]) {
-  const int j0 = threadIdx.x * PER;
-  const uint16_t* src = row + j0;
-  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-#pragma unroll
-    for (int q = 0; q < PER / 8; ++q) {
-      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        kv[8 * q + 2 * h] = score_key(__uint_as_float(w[h] << 16));
-        kv[8 * q + 2 * h + 1] = score_key(__uint_as_float(w[h] & 0xffff0000u));
+        for (int c = 0; c < 4; ++c) kv[4 * q + c] = p + c < n ? score_key(row[p + c]) : 0u;
       }
     }
   } else {
-    const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kv[i] = i < m ? score_key(score_at(src, i)) : 0u;
+    for (int i = 0; i < PER; ++i) {
+      const int p = p0 + 256 * (i >> 2) + (i & 3);
+      kv[i] = p < n ? score_key(row[p]) : 0u;
+    }
+  }
+}
+
+// bf16 scores: one 8-byte load of four codes per group (the same conditions, 8-byte aligned
+// rows); each code is the high half of its fp32 value.
+template <int PER>
+__device__ __forceinline__ void load_keys(const uint16_t* row, int n, uint32_t (&kv)[PER]) {
+  const int p0 = key_pos<PER>(0);
+  if ((reinterpret_cast<uintptr_t>(row) & 7) == 0) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const int p = p0 + 256 * q;
+      if (p + 4 <= n) {
+        const uint2 v = *reinterpret_cast<const uint2*>(row + p);
+        kv[4 * q] = score_key(__uint_as_float(v.x << 16));
+        kv[4 * q + 1] = score_key(__uint_as_float(v.x & 0xffff0000u));
+        kv[4 * q + 2] = score_key(__uint_as_float(v.y << 16));
+        kv[4 * q + 3] = score_key(__uint_as_float(v.y & 0xffff0000u));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kv[4 * q + c] = p + c < n ? score_key(score_at(row, p + c)) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = p0 + 256 * (i >> 2) + (i & 3);
+      kv[i] = p < n ? score_key(score_at(row, p)) : 0u;
+    }
   }
 }
 
 // The same for keys already mapped (stage-2 candidates).
 template <int PER>
 __device__ __forceinline__ void load_mapped(const uint32_t* keys, int n, uint32_t (&kv)[PER]) {
-  const int j0 = threadIdx.x * PER;
-  const uint32_t* src = keys + j0;
-  if (j0 + PER <= n && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+  const int p0 = key_pos<PER>(0);
+  if ((reinterpret_cast<uintptr_t>(keys) & 15) == 0) {
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
-      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
-      kv[4 * q] = v.x;
-      kv[4 * q + 1] = v.y;
-      kv[4 * q + 2] = v.z;
-      kv[4 * q + 3] = v.w;
+      const int p = p0 + 256 * q;
+      if (p + 4 <= n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + p);
+        kv[4 * q] = v.x;
+        kv[4 * q + 1] = v.y;
+        kv[4 * q + 2] = v.z;
+        kv[4 * q + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kv[4 * q + c] = p + c < n ? keys[p + c] : 0u;
+      }
     }
   } else {
-    const int m = n - j0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kv[i] = i < m ? src[i] : 0u;
+    for (int i = 0; i < PER; ++i) {
+      const int p = p0 + 256 * (i >> 2) + (i & 3);
+      kv[i] = p < n ? keys[p] : 0u;
+    }
   }
 }
 
-// Single stage: one workgroup per query row (n_vis <= NT * kPer). For 256 threads, six waves per
-// SIMD (at most 80 VGPRs, no spills): 370 -> 336 us for 32768 rows of up to 8192 scores against
-// five.
+// Single stage: one workgroup per query row (n_vis <= NT * kPer). For 256 threads, five waves per
+// SIMD (at most 96 VGPRs: room for the keys' bins beside the keys): 307 us for 32768 rows of up
+// to 8192 scores, against 321 us at six waves without the bins kept.
 template <int NT, typename S>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 6 : 4, NT == 256 ? 6 : 4)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 5 : 4, NT == 256 ? 5 : 4)))
 topk_row_kernel(TopkArgs a) {
   __shared__ int s_tmp[2 * NT / kWave + 2];
   __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
@@ -680,17 +780,10 @@ __device__ void select_row_passes(const S* row, int64_t n, int k, int32_t* out, 
   for (int64_t b0 = 0; b0 < n && written < k; b0 += kFiltN) {
     uint32_t kv[kFiltPer];
     load_keys(row + b0, (int)(n - b0 < kFiltN ? n - b0 : kFiltN), kv);
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < kFiltPer; ++i) {
-      gt += kv[i] > K;
-      eq += kv[i] == K;
-    }
     int tot_gt, tot_eq;
-    block_scan<NT>(gt, s_tmp, tot_gt);
-    block_scan<NT>(eq, s_tmp, tot_eq);
     compact<NT>(kv, K, eq_left, k - written, s_tmp,
-                [&](int o, int j, uint32_t) { out[written + o] = (int32_t)(b0 + j); });
+                [&](int o, int j, uint32_t) { out[written + o] = (int32_t)(b0 + j); }, &tot_gt,
+                &tot_eq);
     const int taken = eq_left < tot_eq ? eq_left : tot_eq;
     written += tot_gt + taken;
     eq_left -= taken;
@@ -774,7 +867,7 @@ __global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, 
     uint32_t kv[kFiltPer];
 #pragma unroll
     for (int u = 0; u < kFiltPer; ++u) {
-      const int j = threadIdx.x * kFiltPer + u;
+      const int j = key_pos<kFiltPer>(u);
       kv[u] = j < G ? score_key(score_at(row, s_pos[j])) : 0u;
     }
     clear_hist(s_hist, NT);

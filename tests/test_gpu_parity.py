@@ -263,10 +263,12 @@ def test_attend_mfma_matches_generic_kernel(monkeypatch):
 
 
 @pytest.mark.parametrize("N,k", [(40000, 1024), (40000, 2048), (20000, 1), (9000, 700),
-                                 (8192, 1024), (5000, 96), (8000, 2600), (262144, 128)])
+                                 (8192, 1024), (5000, 96), (8000, 2600), (262144, 128),
+                                 (8191, 1000), (30001, 1024), (45001, 2048), (70001, 512)])
 def test_topk_exact_with_ties_and_long_rows(N, k):
     # Top-k on identical fp32 scores is integer work: bit-exact against the oracle, including
-    # heavy ties (coarse score values, -0.0 vs +0.0) and rows longer than one chunk.
+    # heavy ties (coarse score values, -0.0 vs +0.0) and rows longer than one chunk. Odd N makes
+    # every row after the first start off a 16-byte boundary (the element-wise loads).
     from oracle import csa_oracle as orc
     rng = np.random.default_rng(N + k)
     nq, m = 6, 4
