@@ -209,11 +209,11 @@ csa_status csa_index_mxfp4(const csa_queries_t* Q, const uint8_t* q_i, const uin
 }
 
 size_t csa_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t max_keys) {
-  return csa::attend_workspace(nq, H, d_c, max_keys);
+  return csa::attend_workspace(nq, H, d_c, max_keys, false);
 }
 
 size_t hca_attend_workspace_bytes(int32_t nq, int32_t H, int32_t d_c, int64_t N) {
-  return csa::attend_workspace(nq, H, d_c, N);
+  return csa::attend_workspace(nq, H, d_c, N, true);
 }
 
 namespace {
@@ -246,7 +246,7 @@ csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
     if (raw->rows <= 0 && Q->nq > 0)
       return fail(CSA_EINVAL, "a window needs a raw store with rows > 0");
   }
-  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, (int64_t)k + window);
+  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, (int64_t)k + window, false);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
   csa::AttendArgs a{};
   a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};
@@ -278,7 +278,7 @@ csa_status csa_attend_tokens(const csa_queries_t* Q, const void* q, int32_t q_dt
   if (raw->rows <= 0 && Q->nq > 0 && (k > 0 || window > 0))
     return fail(CSA_EINVAL, "token selection needs a raw store with rows > 0");
   if ((int64_t)k * m + window > (int64_t)1 << 30) return fail(CSA_EINVAL, "k * m + window too large");
-  const size_t need = csa::attend_workspace(Q->nq, H, raw->d_c, (int64_t)k * m + window);
+  const size_t need = csa::attend_workspace(Q->nq, H, raw->d_c, (int64_t)k * m + window, false);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
   csa::AttendArgs a{};
   a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};
@@ -305,7 +305,7 @@ csa_status hca_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, in
                       const csa_kv_t* entries, int32_t m_prime, float sm_scale, float* out,
                       float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (csa_status st = check_attend_common(Q, q, q_dtype, H, entries, m_prime, out)) return st;
-  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, entries->rows);
+  const size_t need = csa::attend_workspace(Q->nq, H, entries->d_c, entries->rows, true);
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return fail(CSA_EWORKSPACE, "workspace too small");
   csa::AttendArgs a{};
   a.Q = csa::Queries{Q->seq, Q->pos, Q->nq};

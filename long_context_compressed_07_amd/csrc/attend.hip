@@ -10,12 +10,12 @@ namespace csa {
 
 hipError_t launch_attend_generic(const AttendArgs& a, hipStream_t s);
 bool attend_mfma_supported(const AttendArgs& a);
-size_t attend_mfma_workspace(int nq, int H, int64_t max_keys);
+size_t attend_mfma_workspace(int nq, int H, int64_t max_keys, bool dense);
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s);
 
-size_t attend_workspace(int nq, int H, int d_c, int64_t max_keys) {
+size_t attend_workspace(int nq, int H, int d_c, int64_t max_keys, bool dense) {
   if (d_c != 512 || H % 32 != 0) return 0;
-  return attend_mfma_workspace(nq, H, max_keys);
+  return attend_mfma_workspace(nq, H, max_keys, dense);
 }
 
 static bool force_generic() {

@@ -438,21 +438,23 @@ __global__ void __launch_bounds__(kGenThreads) fixup_kernel(AttendArgs a, MfmaPl
 enum PlanKind { kPlanStaging = 0, kPlanBf16 = 1, kPlanF8 = 2 };
 
 // Split rule. The number of key splits per query depends only on the call's longest key list
-// (max_keys: k + window for CSA, the entry rows for HCA) and on the kernel, never on the number of
-// queries, and the merge takes the splits in a fixed order: a query's outputs are bitwise the same
+// (max_keys: k + window for CSA, the entry rows for HCA), the call (CSA or HCA) and the kernel,
+// never on the number of queries, and the merge takes the splits in a fixed order: a query's outputs are bitwise the same
 // whatever batch it is in and wherever in the batch it sits (deepseek.csdn.net "一文搞懂
 // DeepSeek", V4 的其他升级: deterministic, batch-invariant kernels). keys_per_split is the
-// kernel's granularity: fp8 (the decode cache) 288 keys, so that a 1152-key CSA list takes 4
-// splits and an 8192-entry HCA list 28 (the hybrid decode's 8 queries then fill 224 of the 256
-// CUs with their HCA layer and leave 32 for the 8 x 4 CSA workgroups that run beside it); bf16
-// (the prefill path, many queries per call) 8192, so that the prefill workloads run unsplit; at
-// most 64 splits.
+// kernel's granularity. fp8 (the decode cache): 288 keys for csa_attend, so that a 1152-key list
+// takes 4 splits (64 sequences: one workgroup per CU; 3, 5, 6 and 8 splits measured 2-25% slower
+// per decode step), and 512 keys for hca_attend, whose dense lists are long: 16 splits for 8192
+// entries, so that the hybrid decode's HCA layer (8 queries, 128 workgroups) leaves CUs for the
+// CSA layer it runs beside (28 splits took every CU: 150 against 128 us per hybrid step; 13-20
+// splits measured alike). bf16 (the prefill path, many queries per call): 8192, so that the
+// prefill workloads run unsplit. At most 64 splits.
 int splits_by_keys(int64_t max_keys, int64_t keys_per_split) {
   const int64_t ns = max_keys / keys_per_split;
   return (int)(ns < 1 ? 1 : (ns > 64 ? 64 : ns));
 }
 
-MfmaPlan make_plan(int H, int64_t max_keys, int kind) {
+MfmaPlan make_plan(int H, int64_t max_keys, int kind, bool dense) {
   MfmaPlan p{};
   const int groups32 = H / 32;
   if (kind == kPlanBf16 && groups32 % 2 == 0) {
@@ -469,7 +471,7 @@ MfmaPlan make_plan(int H, int64_t max_keys, int kind) {
     p.f8_dma = 1;
     p.rg = 4;
     p.head_groups = groups32 / 4;
-    p.n_split = splits_by_keys(max_keys, 288);
+    p.n_split = splits_by_keys(max_keys, dense ? 512 : 288);
     return p;
   }
   // fp16-staging kernel: as many 32-head groups per staged tile as the head count allows.
@@ -510,11 +512,11 @@ static size_t plan_partial_bytes(const MfmaPlan& p, int nq, int H) {
 static size_t plan_flag_bytes(const MfmaPlan& p, int nq) {
   return (size_t)nq * p.head_groups * p.n_split * sizeof(int);
 }
-size_t attend_mfma_workspace(int nq, int H, int64_t max_keys) {
+size_t attend_mfma_workspace(int nq, int H, int64_t max_keys, bool dense) {
   // The dtypes are not part of the workspace query: cover every plan kind.
   size_t part = 0, flags = 0;
   for (int kind = 0; kind < 3; ++kind) {
-    const MfmaPlan p = make_plan(H, max_keys, kind);
+    const MfmaPlan p = make_plan(H, max_keys, kind, dense);
     part = std::max(part, plan_partial_bytes(p, nq, H));
     flags = std::max(flags, plan_flag_bytes(p, nq));
   }
@@ -589,7 +591,7 @@ void timing_stop(int slot, int i, hipStream_t s) {
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, int64_t max_keys, hipStream_t s) {
-  MfmaPlan p = make_plan(a.H, max_keys, plan_kind(a));
+  MfmaPlan p = make_plan(a.H, max_keys, plan_kind(a), a.dense);
   if (p.n_split > 1) {
     p.ws_o = static_cast<_Float16*>(a.ws);
     p.ws_ml = reinterpret_cast<float*>(p.ws_o + (size_t)a.Q.nq * p.n_split * a.H * kDC);

@@ -139,7 +139,7 @@ struct AttendArgs {
   void* ws;
   size_t ws_bytes;
 };
-size_t attend_workspace(int nq, int H, int d_c, int64_t max_keys);
+size_t attend_workspace(int nq, int H, int d_c, int64_t max_keys, bool dense);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 }  // namespace csa
