@@ -12,9 +12,9 @@
 // visible entries (j < n_vis of each query) are computed and written.
 //
 // index_fp8_stream_kernel (decode, e4m3 with per-row scales): each wave step reads 16 entries
-// (1 KiB, one 16-byte load per lane, fully coalesced), widens the codes to fp16 and runs two
-// 16x16x32 MFMAs with the query's heads as rows; ReLU(s_q s_k q.k) = s_q s_k ReLU(q.k) lets the
-// scales fold into the head weights and the row scale.
+// (1 KiB, one 16-byte load per lane, fully coalesced, non-temporal), widens the codes to fp16 and
+// runs two 16x16x32 MFMAs with the query's heads as rows; ReLU(s_q s_k q.k) = s_q s_k ReLU(q.k)
+// lets the scales fold into the head weights and the row scale.
 #include "common.h"
 
 namespace csa {
@@ -175,15 +175,15 @@ index_bf16_mfma_kernel(IndexArgs a) {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-// 8 e4m3 codes (two dwords) -> 8 fp16 values, exactly (every e4m3 value is an fp16 value).
+// 8 e4m3 codes (two dwords) -> 8 fp16 values, exactly (every e4m3 value is an fp16 value): the
+// packed fp8 -> fp16 conversion with a unit scale, two values per instruction.
 __device__ __forceinline__ half8 e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
-  typedef float float2v __attribute__((ext_vector_type(2)));
-  const float2v p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-  const float2v p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-  const float2v p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-  const float2v p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-  return half8{(_Float16)p0.x, (_Float16)p0.y, (_Float16)p1.x, (_Float16)p1.y,
-               (_Float16)p2.x, (_Float16)p2.y, (_Float16)p3.x, (_Float16)p3.y};
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // Workgroup (query qi, chunk c) covers entries [c * per_wg, (c + 1) * per_wg) (per_wg a multiple
@@ -219,19 +219,23 @@ __global__ void __launch_bounds__(256) index_fp8_stream_kernel(IndexArgs a, int6
   const uint8_t* kb = static_cast<const uint8_t*>(a.k_i) + b * a.N * 64;
   const float* ks = a.k_i_scale + b * a.N;
   float* out = a.scores + (int64_t)qi * a.ld_scores;
-  // Batches of 8 steps per wave (128 entries; 512 per workgroup): all 8 row loads and scale loads
-  // are issued before any is used. Rows past the end are clamped to the last entry (loaded, not
-  // stored), so the loads need no branches.
-  for (int64_t base = j0 + 128 * w; base < j1; base += 512) {
-    uint4 v[8];
-    float sc[8];
+  // Batches of 8 steps per wave (128 entries; 512 per workgroup and batch): all 8 row loads and
+  // scale loads of a batch are issued together, and the next batch's before this one is used.
+  // Rows past the end are clamped to the last entry (loaded, not stored), so the loads need no
+  // branches. The keys are read once: non-temporal loads, so that they do not displace the
+  // scores and queries from the caches (measured 33 -> 27 us for 64 rows of 32768 entries, with
+  // the batches in flight two at a time and 2048 entries per workgroup).
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  auto load = [&](int64_t base, u32x4 (&v)[8], float (&sc)[8]) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       int64_t ent = base + 16 * u + col;
       ent = ent < j1 ? ent : j1 - 1;
-      v[u] = *reinterpret_cast<const uint4*>(kb + ent * 64 + 16 * g);
-      sc[u] = ks[ent];
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + ent * 64 + 16 * g));
+      sc[u] = __builtin_nontemporal_load(ks + ent);
     }
+  };
+  auto compute = [&](int64_t base, const u32x4 (&v)[8], const float (&sc)[8]) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -245,6 +249,23 @@ __global__ void __launch_bounds__(256) index_fp8_stream_kernel(IndexArgs a, int6
       const int64_t ent = base + 16 * u + col;
       if (g == 0 && ent < j1) out[ent] = p * sc[u];
     }
+  };
+  int64_t base = j0 + 128 * w;
+  if (base >= j1) return;   // no barrier follows: waves finish independently
+  u32x4 v0[8], v1[8];
+  float s0[8], s1[8];
+  load(base, v0, s0);
+  while (true) {   // two batches per trip, alternating between the two register sets
+    const int64_t nb = base + 512;
+    if (nb < j1) load(nb, v1, s1);
+    compute(base, v0, s0);
+    if (nb >= j1) break;
+    base = nb;
+    const int64_t nb2 = base + 512;
+    if (nb2 < j1) load(nb2, v0, s0);
+    compute(base, v1, s1);
+    if (nb2 >= j1) break;
+    base = nb2;
   }
 }
 
@@ -261,9 +282,11 @@ bool index_fast(const IndexArgs& a, hipStream_t s, hipError_t* err) {
     return true;
   }
   if (a.dtype == CSA_E4M3) {
-    // Enough workgroups to keep every CU streaming: >= 2048 in total, >= 1024 entries each.
+    // Enough workgroups to keep every CU streaming: >= 2048 in total where the rows allow, >= 2048
+    // entries each (four batches per wave: 1024 and 4096 measured 29 us against 27 us for 64 rows
+    // of 32768 entries).
     int64_t per_wg = (a.N * a.Q.nq + 2047) / 2048;
-    per_wg = per_wg < 1024 ? 1024 : per_wg;
+    per_wg = per_wg < 2048 ? 2048 : per_wg;
     per_wg = (per_wg + 511) / 512 * 512;
     const int64_t nx = (a.N + per_wg - 1) / per_wg;
     if (nx == 0) { *err = hipSuccess; return true; }
