@@ -16,13 +16,16 @@
 namespace csa {
 namespace {
 
+// Vector loads of token rows; the pooling reads each row once, so the loads are non-temporal.
 template <typename TIn>
 struct Vec;
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
   __device__ static void load(const void* base, int64_t off, float* out) {
-    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off));
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   }
 };
@@ -30,7 +33,9 @@ template <>
 struct Vec<uint16_t> {
   static constexpr int N = 8;
   __device__ static void load(const void* base, int64_t off, float* out) {
-    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -54,6 +54,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexFp4Args a, int64_
   const uint8_t* ks = a.k_i_scale + b * a.N * 2;
   uint16_t* out = a.scores + (int64_t)qi * a.ld_scores;
   // Keys past the range are clamped to its last one (loaded, not stored): no branches on loads.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   for (int64_t base = j0 + 32 * kFp4Batch * w; base < j1; base += kFp4PerIter) {
     uint4 v[kFp4Batch];
     int sc[kFp4Batch];
@@ -61,8 +62,10 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexFp4Args a, int64_
     for (int u = 0; u < kFp4Batch; ++u) {
       int64_t ent = base + 32 * u + col;
       ent = ent < j1 ? ent : j1 - 1;
-      v[u] = *reinterpret_cast<const uint4*>(kb + ent * 32 + 16 * half);
-      sc[u] = ks[ent * 2 + half];
+      // Keys are read once: non-temporal loads.
+      const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + ent * 32 + 16 * half));
+      v[u] = make_uint4(kv.x, kv.y, kv.z, kv.w);
+      sc[u] = __builtin_nontemporal_load(ks + ent * 2 + half);
     }
 #pragma unroll
     for (int u = 0; u < kFp4Batch; ++u) {

@@ -447,6 +447,9 @@ __device__ __forceinline__ float score_at(const uint16_t* row, int64_t j) {
 
 // Loads this thread's keys (positions key_pos(i)) of a row of n scores, 0 beyond n: one 16-byte
 // load per group of four that lies inside a 16-byte aligned row, element by element otherwise.
+// The row is read once per selection: non-temporal loads (about 2% faster than ordinary loads
+// for the 32K prefill's rows: 311 -> 306 us, the two timed in alternation).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int PER>
 __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv)[PER]) {
   const int p0 = key_pos<PER>(0);
@@ -455,7 +458,7 @@ __device__ __forceinline__ void load_keys(const float* row, int n, uint32_t (&kv
     for (int q = 0; q < PER / 4; ++q) {
       const int p = p0 + 256 * q;
       if (p + 4 <= n) {
-        const float4 v = *reinterpret_cast<const float4*>(row + p);
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + p));
         kv[4 * q] = score_key(v.x);
         kv[4 * q + 1] = score_key(v.y);
         kv[4 * q + 2] = score_key(v.z);
