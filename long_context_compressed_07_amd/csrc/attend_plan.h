@@ -60,8 +60,11 @@ __device__ __forceinline__ void merge_partials8(const AttendArgs& a, const AttnP
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   float* dst = a.out + ((int64_t)qi * a.H + head) * kDc + d0;
-  *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  typedef float f32x4 __attribute__((ext_vector_type(4)));   // final outputs: non-temporal
+  __builtin_nontemporal_store(f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv},
+                              reinterpret_cast<f32x4*>(dst));
+  __builtin_nontemporal_store(f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv},
+                              reinterpret_cast<f32x4*>(dst + 4));
   if (a.lse != nullptr && d0 == 0)
     a.lse[(int64_t)qi * a.H + head] =
         lsum > 0.f ? (mx + __log2f(lsum)) * 0.6931471805599453f : -INFINITY;

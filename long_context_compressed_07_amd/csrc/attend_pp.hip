@@ -192,7 +192,8 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     }
   }
 
-  // Prologue, in parallel: every wave copies its share of the queries by DMA, while the PV
+  // Prologue, in parallel: every wave copies its share of the queries by DMA (non-temporal: read
+  // once, so that they do not displace key rows from the caches), while the PV
   // waves compute the codes of tiles 0-2, copy the selection slots of tiles 3 and 4 and issue the
   // DMA of tiles 0 and 1. The queries of the 64 heads go to tile buffers 2 and 3 (idle until the
   // first tile's block) in the QK waves' fragment order: fragment f of row group rg at
@@ -205,7 +206,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       const int F = 9 * w + i;
       const int rgF = F / 36, f = F - 36 * rgF;
       const char* src = qblk + ((32 * rgF + 16 * (f & 1) + c) * kD + 32 * (f >> 1) + 8 * g) * 2;
-      __builtin_amdgcn_global_load_lds(src, (lds_char*)(&kv[2][0] + 1024 * F), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_char*)(&kv[2][0] + 1024 * F), 16, 0, kNonTemporal);
     }
   }
 
@@ -568,9 +569,8 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
         for (int u = 0; u < kU; ++u)
           v[u] = *reinterpret_cast<const uint4*>(stage + (h0 + 2 * u) * kStageLd<float> + 16 * k);
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.out + (row0 + h0 + 2 * u) * kDC) +
-                                    16 * k) = v[u];
+        for (int u = 0; u < kU; ++u)   // final outputs: non-temporal stores
+          store_nt(reinterpret_cast<char*>(a.out + (row0 + h0 + 2 * u) * kDC) + 16 * k, v[u]);
       } else {
         constexpr int kCh = 512 * 2 / 16;
         constexpr int kU = 32 * kCh / 256;

@@ -137,6 +137,16 @@ __device__ __forceinline__ void stage_rows_checked(const floatx16 (&o)[4][RG], i
     }
 }
 
+// Cache policy of a DMA (global_load_lds) whose rows are read once: non-temporal.
+constexpr int kNonTemporal = 2;
+
+// 16-byte store of data written once (final outputs): non-temporal, so that it does not displace
+// the key rows that later workgroups read from the caches.
+__device__ __forceinline__ void store_nt(char* dst, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
+
 // Writes ROWS staged rows: row h to dst + h * 512 (consecutive heads are consecutive rows).
 template <typename T, int ROWS = 32>
 __device__ __forceinline__ void flush_rows(const char* buf, T* dst) {
@@ -147,7 +157,11 @@ __device__ __forceinline__ void flush_rows(const char* buf, T* dst) {
     const int c = (int)threadIdx.x + 256 * i;
     const int h = c / kChunksRow, k = c - h * kChunksRow;
     const uint4 v = *reinterpret_cast<const uint4*>(buf + h * kStageLd<T> + 16 * k);
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + (int64_t)h * 512) + 16 * k) = v;
+    char* d = reinterpret_cast<char*>(dst + (int64_t)h * 512) + 16 * k;
+    if constexpr (sizeof(T) == 4)
+      store_nt(d, v);   // fp32: final outputs, written once
+    else
+      *reinterpret_cast<uint4*>(d) = v;   // fp16 partials: read back by the merge
   }
 }
 
