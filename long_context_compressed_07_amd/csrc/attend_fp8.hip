@@ -330,12 +330,18 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
     const float nm = have_ref ? -m_ref : 0.f;
     {
       f16x8 ph[2];
+      float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], cscale, nm));
-        l_run += p;
-        ph[i >> 3][i & 7] = (_Float16)p;
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], cscale, nm));
+        ph[i >> 3][i & 7] = (_Float16)pv[i];
       }
+      // The tile's 16 values summed as a tree (depth 4, not a chain of 16 dependent adds).
+#pragma unroll
+      for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+        for (int i = 0; i < w2; ++i) pv[i] += pv[i + w2];
+      l_run += pv[0];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         *reinterpret_cast<f16x8*>(pbuf + ((s * RG + rg) * 64 + lane) * 16) = ph[s];
