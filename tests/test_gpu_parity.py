@@ -188,6 +188,17 @@ def test_deterministic(cfg):
                            y.view(torch.uint8) if y.dtype != torch.uint8 else y)
 
 
+@pytest.mark.parametrize("H,k,window", [(32, 300, 50), (96, 1000, 128), (64, 2, 1)])
+def test_fp8_decode_other_head_counts(H, k, window):
+    # fp8 decode with head counts that are not a multiple of 128 (the fp16-staging kernel's
+    # head-group and key-split layouts), key lists that end inside a tile (k + window not a
+    # multiple of 32) and very short lists.
+    wl = SMALL["C4"].replace(H=H, k=k, window=window)
+    print(f"[parity] fp8 decode H={H} k={k} window={window}", flush=True)
+    host, step = _run(wl, True, 30 + H)
+    parity.check_csa(wl, host, step)
+
+
 @pytest.mark.parametrize("sharp", [False, True])
 def test_csa_prefill_128_heads(sharp):
     # 128 heads per query: two 64-head workgroups of the two-role kernel.
