@@ -653,22 +653,24 @@ __global__ void __launch_bounds__(NT) topk_merge_kernel(TopkArgs a, int n_chunks
 
 // ---- Sampled threshold: rows longer than kChunk when there are few of them ---------------------
 // One workgroup per row picks a threshold key T from evenly spaced samples (topk_sample_kernel);
-// workgroups of kFiltN entries then mark, one bit per entry, the row's keys above T and equal to
-// T (topk_filter_kernel); one workgroup per row selects the top k from the marked entries
-// (topk_select_kernel). With G keys above T and E equal to it: G >= k leaves the selection to
-// the G marked keys (at most kSelCap of them); G < k <= G + E makes T the k-th key, so the result
-// is every key above T plus the first k - G keys equal to it; a sample that misjudged the row
-// (G + E < k, or G > kSelCap) sends the row to an exact selection over all of its keys in the
-// select workgroup. Every case yields the unique top k, so which one ran never shows in the
-// result. These kernels run 1024 threads, few keys each: a decode call has too few rows to fill
-// the GPU, so each workgroup's latency, not the throughput, sets the time.
+// workgroups of kFiltN entries then write the row's keys at or above T, with their positions, as
+// one candidate list per workgroup in position order (topk_filter_kernel); one workgroup per row
+// gathers the lists (in workgroup order, so the candidates stay in position order) and selects the
+// top k among them (topk_select_kernel). With C keys at or above T: C >= k means the row's k-th
+// key is at or above T, so every key of the top k is a candidate and the top k of the candidates
+// (ties to the lower position) is the row's; a sample that misjudged the row (C < k), or too many
+// candidates (a list past kCandCap, or C past kSelCap), sends the row to an exact selection over
+// all of its keys in the select workgroup. Every case yields the unique top k, so which one ran
+// never shows in the result. These kernels run 1024 threads, few keys each: a decode call has too
+// few rows to fill the GPU, so each workgroup's latency, not the throughput, sets the time.
 constexpr int kSNT = 1024;                   // threads of the sampled path's workgroups
 constexpr int kSampPer = 2;                  // samples per thread
 constexpr int kSamp = kSNT * kSampPer;       // samples per row
 constexpr int kFiltPer = 8;                  // entries per thread of a filter workgroup
 constexpr int kFiltN = kSNT * kFiltPer;      // entries per filter workgroup
 constexpr int kSelCap = kSNT * kFiltPer;     // keys one select workgroup ranks
-constexpr int kMaxWpt = 8;                   // mark blocks (64 entries) per select thread
+constexpr int kCandCap = 512;                // candidates one filter workgroup may list
+constexpr int kMaxFilt = 64;                 // filter workgroups per row
 
 // Samples of a row of n > 0 keys: positions floor(i n / s), i < s = min(n, kSamp). T is the r-th
 // largest sample: s evenly spaced samples hold about k s / n keys at or above the row's k-th key;
@@ -702,18 +704,25 @@ __global__ void __launch_bounds__(kSNT) topk_sample_kernel(TopkArgs a, uint32_t*
   if (threadIdx.x == 0) thr[qi] = T;
 }
 
-// Marks of the row's entries in blocks of 64 positions, in position order: {above T, equal to T}
-// as two 64-bit masks (uint4 {above lo, above hi, equal lo, equal hi}). Filter workgroup c covers
-// entries c kFiltN + 1024 u + t (u < kFiltPer): wave v's ballot for key u is the block of
-// positions c kFiltN + 1024 u + 64 v. Entries past the visible ones have key 0, below every real T.
+// Candidates of filter workgroup c of row qi, entries c kFiltN + 1024 u + t (u < kFiltPer): the
+// keys >= T and their positions, in position order ((u, wave, lane) order), as the list
+// cand[qi][c][0 .. count) with count in counts[qi][c] (a count past kCandCap: the list overflowed,
+// only its first kCandCap entries are written). Entries past the visible ones have key 0, below
+// every real T.
 template <typename S>
 __global__ void __launch_bounds__(kSNT) topk_filter_kernel(TopkArgs a, int n_f, const uint32_t* thr,
-                                                           uint4* marks) {
+                                                           int* counts, uint2* cand) {
+  constexpr int NW = kSNT / kWave;
+  __shared__ int s_off[kFiltPer * NW];
   const int qi = blockIdx.x / n_f;
   const int c = blockIdx.x - qi * n_f;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
   const int64_t base = (int64_t)c * kFiltN;
-  if (nv <= a.k || base >= nv) return;   // the select kernel reads no marks here
+  int* cnt = counts + (int64_t)qi * n_f + c;
+  if (nv <= a.k || base >= nv) {   // no candidates here (rows of at most k entries: none read)
+    if (threadIdx.x == 0) *cnt = 0;
+    return;
+  }
   const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
   uint32_t kv[kFiltPer];
 #pragma unroll
@@ -723,14 +732,28 @@ __global__ void __launch_bounds__(kSNT) topk_filter_kernel(TopkArgs a, int n_f, 
   }
   const uint32_t T = thr[qi];
   const int lane = threadIdx.x & (kWave - 1), v = threadIdx.x / kWave;
-  uint4* dst = marks + ((int64_t)qi * n_f + c) * (kFiltN / 64);
+  uint64_t m[kFiltPer];
 #pragma unroll
   for (int u = 0; u < kFiltPer; ++u) {
-    const uint64_t gt = __ballot(kv[u] > T);
-    const uint64_t eq = __ballot(kv[u] == T);
-    if (lane == 0)
-      dst[u * (kSNT / kWave) + v] =
-          make_uint4((uint32_t)gt, (uint32_t)(gt >> 32), (uint32_t)eq, (uint32_t)(eq >> 32));
+    m[u] = __ballot(kv[u] >= T);
+    if (lane == 0) s_off[u * NW + v] = __popcll(m[u]);
+  }
+  lds_sync();
+  // Exclusive prefix of the (u, wave) counts in position order, by wave 0 (two per lane).
+  if (v == 0) {
+    const int a0 = s_off[2 * lane], a1 = s_off[2 * lane + 1];
+    const int inc = wave_incl_sum(a0 + a1);
+    s_off[2 * lane] = inc - a0 - a1;
+    s_off[2 * lane + 1] = inc - a1;
+    if (lane == kWave - 1) *cnt = inc;
+  }
+  lds_sync();
+  uint2* dst = cand + ((int64_t)qi * n_f + c) * kCandCap;
+#pragma unroll
+  for (int u = 0; u < kFiltPer; ++u) {
+    const int o = mbcnt(m[u], s_off[u * NW + v]);
+    if (kv[u] >= T && o < kCandCap)
+      dst[o] = make_uint2(kv[u], (uint32_t)(base + (int64_t)u * kSNT + threadIdx.x));
   }
 }
 
@@ -794,11 +817,15 @@ __device__ void select_row_passes(const S* row, int64_t n, int k, int32_t* out, 
 }
 
 template <typename S>
-__global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, const uint4* marks) {
+__global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, const int* counts,
+                                                           const uint2* cand) {
   constexpr int NT = kSNT;
   __shared__ int s_tmp[2 * NT / kWave + 2];
   __shared__ __attribute__((aligned(16))) int s_hist[2 * kBins];
-  __shared__ int s_pos[kSelCap];   // marked positions in row order
+  __shared__ uint32_t s_key[kSelCap];   // candidates in position order
+  __shared__ int s_pos[kSelCap];
+  __shared__ int s_start[kMaxFilt + 1];
+  __shared__ int s_bad;
   const int qi = blockIdx.x;
   const int64_t nv = n_visible(a.Q.pos[qi], a.m, a.N);
   int32_t* out = a.idx + (int64_t)qi * a.k;
@@ -807,81 +834,62 @@ __global__ void __launch_bounds__(kSNT) topk_select_kernel(TopkArgs a, int n_f, 
     return;
   }
   const S* row = static_cast<const S*>(a.scores) + (int64_t)qi * a.ld_scores;
-  const uint4* mk = marks + (int64_t)qi * n_f * (kFiltN / 64);
-  // Thread t holds the mark blocks [t wpt, t wpt + wpt) of the row's nb blocks of 64 positions
-  // (wpt <= kMaxWpt: use_sampled bounds the row length), loaded once.
-  const int nb = (int)((nv + 63) / 64);
-  const int wpt = (nb + NT - 1) / NT;
-  const int b0 = threadIdx.x * wpt;
-  uint4 mr[kMaxWpt];
-  int cg = 0, ce = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxWpt; ++i) {
-    mr[i] = i < wpt && b0 + i < nb ? mk[b0 + i] : make_uint4(0u, 0u, 0u, 0u);
-    cg += __popc(mr[i].x) + __popc(mr[i].y);
-    ce += __popc(mr[i].z) + __popc(mr[i].w);
-  }
-  int G, E;
-  const int g_before = block_scan<NT>(cg, s_tmp, G);
-  const int e_before = block_scan<NT>(ce, s_tmp, E);
   const int k = a.k;
-  if (G < k && k <= G + E) {
-    // T is the k-th key: every key above it, then the first k - G keys equal to it.
-    int take = k - G - e_before;
-    take = take < 0 ? 0 : (take > ce ? ce : take);
-    int tot;
-    int off = block_scan<NT>(cg + take, s_tmp, tot);
-#pragma unroll
-    for (int i = 0; i < kMaxWpt; ++i) {
-      const uint4 m = mr[i];
-      uint64_t e = ((uint64_t)m.w << 32) | m.z, keep = 0;
-      while (e != 0u && take > 0) {   // the lowest `take` bits of the equal marks
-        const uint64_t low = e & (0ull - e);
-        keep |= low;
-        e ^= low;
-        --take;
-      }
-      uint64_t bits = (((uint64_t)m.y << 32) | m.x) | keep;
-      while (bits != 0u) {
-        const int b = __builtin_ctzll(bits);
-        bits &= bits - 1u;
-        if (off < k) s_hist[off] = (b0 + i) * 64 + b;
-        ++off;
-      }
+  // Where each filter workgroup's list goes (wave 0: one list per lane, n_f <= 64).
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int cn = lane < n_f ? counts[(int64_t)qi * n_f + lane] : 0;
+    const int inc = wave_incl_sum(cn);
+    s_start[lane] = inc - cn;
+    if (lane == kWave - 1) {
+      s_start[kMaxFilt] = inc;
+      s_bad = inc < k || inc > kSelCap;
     }
-    lds_sync();
-    for (int i = threadIdx.x; i < k; i += NT) out[i] = s_hist[i];
+    if (cn > kCandCap) s_bad = 1;   // any lane: an overflowed list
+  }
+  lds_sync();
+  const int C = s_start[kMaxFilt];
+  if (s_bad) {
+    select_row_passes(row, nv, k, out, s_hist, s_tmp);
     return;
   }
-  if (G >= k && G <= kSelCap) {
-    // The marked keys above T, in row order, then the top k among them.
-    int off = g_before;
+  // Gather the lists: list c by the kSNT / kMaxFilt threads 16 c .. 16 c + 15, all loads issued
+  // before any store.
+  {
+    constexpr int kTpl = NT / kMaxFilt;                  // threads per list
+    constexpr int kPerT = kCandCap / kTpl;               // candidates per thread at most
+    const int c = threadIdx.x / kTpl, r = threadIdx.x % kTpl;
+    const int st = c < n_f ? s_start[c] : 0;
+    const int cn = c < n_f ? s_start[c + 1] - st : 0;
+    const uint2* src = cand + ((int64_t)qi * n_f + (c < n_f ? c : 0)) * kCandCap;
+    uint2 v[kPerT];
 #pragma unroll
-    for (int i = 0; i < kMaxWpt; ++i) {
-      const uint4 m = mr[i];
-      uint64_t bits = ((uint64_t)m.y << 32) | m.x;
-      while (bits != 0u) {
-        const int b = __builtin_ctzll(bits);
-        bits &= bits - 1u;
-        s_pos[off++] = (b0 + i) * 64 + b;
+    for (int i = 0; i < kPerT; ++i) {
+      const int j = r + kTpl * i;
+      v[i] = j < cn ? src[j] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int j = r + kTpl * i;
+      if (j < cn) {
+        s_key[st + j] = v[i].x;
+        s_pos[st + j] = (int)v[i].y;
       }
     }
-    lds_sync();
-    uint32_t kv[kFiltPer];
-#pragma unroll
-    for (int u = 0; u < kFiltPer; ++u) {
-      const int j = key_pos<kFiltPer>(u);
-      kv[u] = j < G ? score_key(score_at(row, s_pos[j])) : 0u;
-    }
-    clear_hist(s_hist, NT);
-    lds_sync();
-    int need_eq;
-    const uint32_t K = kth_key<NT, true>(kv, k, s_hist, s_tmp, &need_eq);
-    compact<NT>(kv, K, need_eq, k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = s_pos[j]; });
-    for (int i = threadIdx.x; i < k; i += NT) out[i] = s_hist[i];
-    return;
   }
-  select_row_passes(row, nv, k, out, s_hist, s_tmp);
+  lds_sync();
+  uint32_t kv[kFiltPer];
+#pragma unroll
+  for (int u = 0; u < kFiltPer; ++u) {
+    const int j = key_pos<kFiltPer>(u);
+    kv[u] = j < C ? s_key[j] : 0u;
+  }
+  clear_hist(s_hist, NT);
+  lds_sync();
+  int need_eq;
+  const uint32_t K = kth_key<NT, true>(kv, k, s_hist, s_tmp, &need_eq);
+  compact<NT>(kv, K, need_eq, k, s_tmp, [&](int o, int j, uint32_t) { s_hist[o] = s_pos[j]; });
+  for (int i = threadIdx.x; i < k; i += NT) out[i] = s_hist[i];
 }
 
 int n_chunks_for(int64_t N) { return (int)((N + kWideChunk - 1) / kWideChunk); }
@@ -896,16 +904,22 @@ int n_chunks_for(int64_t N) { return (int)((N + kWideChunk - 1) / kWideChunk); }
 bool use_sampled(int nq, int64_t N, int k) {
   const int64_t n_f = (N + kFiltN - 1) / kFiltN;
   const int64_t s = N < kSamp ? N : kSamp;
-  return N > kWideChunk && N <= (int64_t)kSNT * 64 * kMaxWpt && k <= kMaxK &&
-         (int64_t)nq * n_f <= 2048 &&
+  return N > kWideChunk && n_f <= kMaxFilt && k <= kMaxK && (int64_t)nq * n_f <= 2048 &&
          2 * (int64_t)k + 16 * ((N + s - 1) / s) <= kSelCap / 2;
 }
 
-size_t sampled_marks_offset(int nq) { return ((size_t)nq * sizeof(uint32_t) + 255) / 256 * 256; }
+// Sampled-path workspace: thresholds [nq], list counts [nq][n_f], lists [nq][n_f][kCandCap].
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+size_t sampled_counts_offset(int nq) { return align256((size_t)nq * sizeof(uint32_t)); }
+size_t sampled_lists_offset(int nq, int n_f) {
+  return sampled_counts_offset(nq) + align256((size_t)nq * n_f * sizeof(int));
+}
 
 size_t topk_workspace(int nq, int64_t N, int k) {
-  if (use_sampled(nq, N, k))
-    return sampled_marks_offset(nq) + (size_t)nq * ((N + kFiltN - 1) / kFiltN) * (kFiltN / 64) * sizeof(uint4);
+  if (use_sampled(nq, N, k)) {
+    const int n_f = (int)((N + kFiltN - 1) / kFiltN);
+    return sampled_lists_offset(nq, n_f) + (size_t)nq * n_f * kCandCap * sizeof(uint2);
+  }
   if (N <= kWideChunk) return 0;
   const int nc = n_chunks_for(N);
   return (size_t)nq * nc * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
@@ -925,15 +939,18 @@ hipError_t launch_topk_t(const TopkArgs& a, hipStream_t s) {
   }
   if (use_sampled(a.Q.nq, a.N, a.k)) {
     const int n_f = (int)((a.N + kFiltN - 1) / kFiltN);
-    uint32_t* thr = static_cast<uint32_t*>(a.ws);
-    uint4* marks = reinterpret_cast<uint4*>(static_cast<char*>(a.ws) + sampled_marks_offset(a.Q.nq));
+    char* ws = static_cast<char*>(a.ws);
+    uint32_t* thr = reinterpret_cast<uint32_t*>(ws);
+    int* counts = reinterpret_cast<int*>(ws + sampled_counts_offset(a.Q.nq));
+    uint2* lists = reinterpret_cast<uint2*>(ws + sampled_lists_offset(a.Q.nq, n_f));
     topk_sample_kernel<S><<<a.Q.nq, kSNT, 0, s>>>(a, thr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    topk_filter_kernel<S><<<(unsigned)((int64_t)a.Q.nq * n_f), kSNT, 0, s>>>(a, n_f, thr, marks);
+    topk_filter_kernel<S><<<(unsigned)((int64_t)a.Q.nq * n_f), kSNT, 0, s>>>(a, n_f, thr, counts,
+                                                                            lists);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    topk_select_kernel<S><<<a.Q.nq, kSNT, 0, s>>>(a, n_f, marks);
+    topk_select_kernel<S><<<a.Q.nq, kSNT, 0, s>>>(a, n_f, counts, lists);
     return hipGetLastError();
   }
   if (a.N <= kWideChunk) {
