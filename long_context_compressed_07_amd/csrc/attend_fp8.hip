@@ -201,23 +201,21 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   const int qrow_i = 32 * rg + (lane & 31);
   if (threadIdx.x == 0) s_flag = 0;
 
-  KeyList kl = make_key_list(a, qi);
-  if constexpr (!TOK) kl.tok_m = 0;
-  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
-  const int64_t k0 = (int64_t)split * per_split;
-  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
-  const RowBases8 rbases = row_bases8(a, kl.b);
-
-  const bool sel_dma = kl.sel != nullptr;
-  const KeyCodes32 kc = key_codes32(kl, ke);
-
-  // Prologue. The codes of tiles 0 .. kAheadF8 (tile w in wave w) need the selection slots, a
-  // dependent load; it goes out before the query loads, so that the wait for it does not also
-  // wait for them, and the rows' DMA is issued while the queries are still in flight.
-  const int c_pro = lane < kTK ? key_code(a, kl, k0 + w * kTK + lane, ke) : -1;
-  if (w == 0 && sel_dma) {   // selection slots of tiles kAheadF8 + 1 and + 2
-    dma_sel<kTK>(kl, k0 + (kAheadF8 + 1) * kTK, ke, s_sel[(kAheadF8 + 1) % 3]);
-    dma_sel<kTK>(kl, k0 + (kAheadF8 + 2) * kTK, ke, s_sel[(kAheadF8 + 2) % 3]);
+  // Prologue loads that wait for nothing. The selection slot of this lane's key in tiles
+  // 0 .. kAheadF8 (tile w in wave w) is loaded at the key range a query with a full window
+  // has, before the query's position is known (it is a dependent load); a query whose range
+  // turns out different (an early position, in a key split past the first) loads it again below.
+  // The queries' loads follow: issued before anything waits, and not waited for by the codes.
+  const int64_t n_sel0 = TOK ? (int64_t)a.k * a.tok_m : (int64_t)a.k;
+  int64_t k0_spec = 0;
+  int raw_spec = 0;
+  if (!a.dense) {
+    const bool win = a.window > 0 && a.raw.c != nullptr && a.raw.rows > 0;
+    const int64_t tot = n_sel0 + (win ? a.window : 0);
+    k0_spec = (int64_t)split * ((tot + plan.n_split - 1) / plan.n_split);
+    const int64_t kk = k0_spec + w * kTK + lane;
+    if (lane < kTK && kk < n_sel0)
+      raw_spec = a.idx[(int64_t)qi * a.k + (TOK ? kk / a.tok_m : kk)];
   }
   // Q^T fragments of this lane's head (dims 16 s + 8 hi + [0, 8)), loaded as bf16 now and
   // rounded to fp16 once the rows' DMA is out.
@@ -228,9 +226,34 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s);
   }
+
+  KeyList kl = make_key_list(a, qi);
+  if constexpr (!TOK) kl.tok_m = 0;
+  const int64_t per_split = (kl.total + plan.n_split - 1) / plan.n_split;
+  const int64_t k0 = (int64_t)split * per_split;
+  const int64_t ke = k0 + per_split < kl.total ? k0 + per_split : kl.total;
+  const RowBases8 rbases = row_bases8(a, kl.b);
+
+  const bool sel_dma = kl.sel != nullptr;
+  const KeyCodes32 kc = key_codes32(kl, ke);
+
+  // Codes of tiles 0 .. kAheadF8, so that the rows' DMA is issued while the queries are still in
+  // flight. No LDS DMA goes out between the loads above and this use of the selection slot: the
+  // compiler would then wait for every load outstanding, the queries included.
+  int raw0 = raw_spec;
+  if (sel_dma && k0 != k0_spec) {
+    const int64_t kk = k0 + w * kTK + lane;
+    raw0 = (lane < kTK && kk < kl.n_sel && kk < ke) ? kl.sel[sel_index(kl, kk)] : 0;
+    asm volatile("" ::"v"(raw0));   // waited for here, so that only the early loads stay pending
+  }
+  const int c_pro = lane < kTK ? key_code32(kc, (int)(k0 + w * kTK + lane), raw0) : -1;
   if (lane < kTK) {
     s_code[w][lane] = c_pro;
     s_addr[w][lane] = key_addr8(rbases, c_pro);
+  }
+  if (w == 0 && sel_dma) {   // selection slots of tiles kAheadF8 + 1 and + 2
+    dma_sel<kTK>(kl, k0 + (kAheadF8 + 1) * kTK, ke, s_sel[(kAheadF8 + 1) % 3]);
+    dma_sel<kTK>(kl, k0 + (kAheadF8 + 2) * kTK, ke, s_sel[(kAheadF8 + 2) % 3]);
   }
   {
     const bool h = __any(c_pro >= 0);

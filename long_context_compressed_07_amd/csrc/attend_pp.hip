@@ -191,13 +191,31 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       sv[u] = j < kl.n_sel ? kl.sel[j] : -1;
     }
   }
+  // The PV waves' selection slots of tiles 0-2 (the first workgroup of a query, whose key range
+  // starts at 0 whatever the trim finds), also loaded ahead of the queries' DMA: loads return in
+  // order, so loaded after it they would wait for the whole 72 KB of queries before the codes and
+  // the first rows' DMA could go out. Slots past the trimmed range are loaded but never used.
+  const bool early_sel = trim && split == 0 && w >= 4;
+  int raw_pre[3] = {0, 0, 0};
+  if (early_sel) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int kk = j * TK + (lane & (TK - 1));
+      raw_pre[j] = kk < kl.n_sel ? kl.sel[kk] : 0;
+    }
+  }
+  asm volatile("" ::: "memory");   // keep those loads ahead of the DMA below
 
-  // Prologue, in parallel: every wave copies its share of the queries by DMA (non-temporal: read
+  // Prologue, in parallel: every wave copies its share of the queries (non-temporal loads: read
   // once, so that they do not displace key rows from the caches), while the PV
   // waves compute the codes of tiles 0-2, copy the selection slots of tiles 3 and 4 and issue the
   // DMA of tiles 0 and 1. The queries of the 64 heads go to tile buffers 2 and 3 (idle until the
   // first tile's block) in the QK waves' fragment order: fragment f of row group rg at
   // (36 rg + f) KB, lane l's 16 bytes at 16 l; each of the 8 waves copies 9 of the 72 fragments.
+  // The copy is made of ordinary loads into registers, written to LDS once they land: the
+  // compiler counts those loads exactly when it waits for the selection slots above, whereas any
+  // LDS DMA issued after a load makes its wait for that load a wait for everything outstanding.
+  v4i qld[9];
   {
     const int c = lane & 15, g = lane >> 4;
     const char* qblk = static_cast<const char*>(a.q) + ((int64_t)qi * a.H + hbase) * kD * 2;
@@ -206,9 +224,14 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       const int F = 9 * w + i;
       const int rgF = F / 36, f = F - 36 * rgF;
       const char* src = qblk + ((32 * rgF + 16 * (f & 1) + c) * kD + 32 * (f >> 1) + 8 * g) * 2;
-      __builtin_amdgcn_global_load_lds(src, (lds_char*)(&kv[2][0] + 1024 * F), 16, 0, kNonTemporal);
+      qld[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
     }
   }
+  auto store_queries = [&]() {
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      *reinterpret_cast<v4i*>(&kv[2][0] + 1024 * (9 * w + i) + 16 * lane) = qld[i];
+  };
 
   if (trim) {
     int last = -1;
@@ -243,7 +266,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     const int rg = w & 1, kh = w >> 1;
     const int c = lane & 15, g = lane >> 4;
     v4i qb[36];
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the queries
+    store_queries();                  // this wave's share of the queries
     __syncthreads();                  // all queries and the prologue's tiles in LDS
     {
       const char* qf = &kv[2][0] + 36 * 1024 * rg + 16 * lane;
@@ -376,13 +399,24 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     {
       const int kl32 = lane & (TK - 1);
       int raw[3];
+      if (early_sel) {   // as below: a key past the (trimmed) selection reads a zero
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int kk = (int)k0 + j * TK + kl32;
-        const int32_t* src = (sel_dma && kk < kc.ke && kk < kc.n_sel)
-                                 ? kl.sel + sel_index(kl, kk)
-                                 : reinterpret_cast<const int32_t*>(kZeroRow);
-        raw[j] = *src;
+        for (int j = 0; j < 3; ++j) {
+          const int kk = (int)k0 + j * TK + kl32;
+          raw[j] = kk < kc.ke && kk < kc.n_sel ? raw_pre[j] : 0;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int kk = (int)k0 + j * TK + kl32;
+          const int32_t* src = (sel_dma && kk < kc.ke && kk < kc.n_sel)
+                                   ? kl.sel + sel_index(kl, kk)
+                                   : reinterpret_cast<const int32_t*>(kZeroRow);
+          raw[j] = *src;
+        }
+        // Waited for here, inside this branch, so that after it only the early loads are
+        // pending and the wait for them need not include the queries' loads.
+        asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]));
       }
       KeyAddr ad[2];
 #pragma unroll
@@ -399,6 +433,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
       }
       dma_tile_regs(ad[0], kv[0], w - 4);
       dma_tile_regs(ad[1], kv[1], w - 4);
+      store_queries();
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
