@@ -162,8 +162,10 @@ __device__ __forceinline__ void convert_stage(const char* st, char* kvb) {
 }
 
 // TOK: token selection (a.tok_m > 0). The entry form is compiled with the token fields known to
-// be zero, so its per-tile key arithmetic has no branches.
-template <bool TOK>
+// be zero, so its per-tile key arithmetic has no branches. DENSE: hca_attend, whose keys are the
+// visible entries in order (key kk is entry row kk): the rows' addresses and the tile masks follow
+// from the key index, so the loop has no per-tile key codes and reads no row addresses from LDS.
+template <bool TOK, bool DENSE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int RG = 4;
@@ -307,11 +309,26 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
       dma.sel = (sel_dma && lane < kTK && kk < ke && kk < kl.n_sel)
                     ? reinterpret_cast<const char*>(kl.sel + sel_index(kl, kk))
                     : reinterpret_cast<const char*>(kZeroRow);
-      const KeyAddr8* ad = s_addr[(it + kAheadF8) % kSlotsF8];
+      if constexpr (DENSE) {
+        // Entry rows of tile it + kAheadF8. A key past the list reads the list's last row instead
+        // (finite values; its logit is masked to -inf, so it adds 0 to every sum).
+        const int tb = (int)(t0 + kAheadF8 * kTK), last = (int)ke - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma.lat[i] = ad[(w + 4 * i) + 16 * (lane >> 5)].lat + 16 * (lane & 31);
-      dma.rope = ad[8 * w + (lane >> 3)].rope + 16 * (lane & 7);
-      dma.scl = lane < kTK ? ad[lane].scl : reinterpret_cast<const char*>(kZeroRow);
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(tb + (w + 4 * i) + 16 * (lane >> 5), last);
+          dma.lat[i] = rbases.c0 + (uint64_t)(uint32_t)row * rbases.ldc0 + 16 * (lane & 31);
+        }
+        const int rrow = min(tb + 8 * w + (lane >> 3), last);
+        dma.rope = rbases.r0 + (uint64_t)(uint32_t)rrow * rbases.ldr0 + 16 * (lane & 7);
+        dma.scl = rbases.s0 + 4 * (uint64_t)(uint32_t)min(tb + (lane & (kTK - 1)), last);
+      } else {
+        const KeyAddr8* ad = s_addr[(it + kAheadF8) % kSlotsF8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dma.lat[i] = ad[(w + 4 * i) + 16 * (lane >> 5)].lat + 16 * (lane & 31);
+        dma.rope = ad[8 * w + (lane >> 3)].rope + 16 * (lane & 7);
+        dma.scl = lane < kTK ? ad[lane].scl : reinterpret_cast<const char*>(kZeroRow);
+      }
       dma.m0_sel = __builtin_amdgcn_readfirstlane(
           lds_addr(reinterpret_cast<const char*>(s_sel[(it + kAheadF8 + 3) % 3])));
       dma.m0_lat = __builtin_amdgcn_readfirstlane(lds_addr(sdst) + kStPair * w);
@@ -336,14 +353,16 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
       acc = qk_chain_f16(qb, lb, rb, dma);
     }
 
-    if (!s_full[slot]) {
+    if (DENSE ? t0 + kTK > ke : !s_full[slot]) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = 8 * (i >> 2) + 4 * hi + (i & 3);
-        acc[i] = codes[key] >= 0 ? acc[i] : -INFINITY;
+        const bool ok = DENSE ? t0 + key < ke : codes[key] >= 0;
+        acc[i] = ok ? acc[i] : -INFINITY;
       }
     }
-    if (!have_ref && s_has_key[slot]) {   // uniform: every head sees the same keys
+    // (A dense tile always holds a key: t0 < ke.)
+    if (!have_ref && (DENSE || s_has_key[slot])) {   // uniform: every head sees the same keys
       float tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[i] * cscale);
@@ -397,8 +416,8 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
 
     // Selection slots for the codes below were copied two tiles ago; at most the DMA instructions
     // issued since (two tiles' worth) may still be outstanding.
-    __builtin_amdgcn_s_waitcnt(kVmcntDma<2 * (kDmaOpsF8 + 1)>);
-    if (threadIdx.x < 64) {
+    if (!DENSE) __builtin_amdgcn_s_waitcnt(kVmcntDma<2 * (kDmaOpsF8 + 1)>);
+    if (!DENSE && threadIdx.x < 64) {
       const int kk2 = (int)t0 + (kAheadF8 + 1) * kTK + (int)threadIdx.x;
       const int raw2 = sel_dma ? s_sel[(it + kAheadF8 + 1) % 3][threadIdx.x] : 0;
       const int c2 = threadIdx.x < kTK ? key_code32(kc, kk2, raw2) : -1;
@@ -481,9 +500,11 @@ attend_fp8_kernel(AttendArgs a, AttnPlan plan) {
 hipError_t launch_attend_fp8(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   if (a.tok_m > 0)
-    attend_fp8_kernel<true><<<grid, 256, 0, s>>>(a, p);
+    attend_fp8_kernel<true, false><<<grid, 256, 0, s>>>(a, p);
+  else if (a.dense)
+    attend_fp8_kernel<false, true><<<grid, 256, 0, s>>>(a, p);
   else
-    attend_fp8_kernel<false><<<grid, 256, 0, s>>>(a, p);
+    attend_fp8_kernel<false, false><<<grid, 256, 0, s>>>(a, p);
   return hipGetLastError();
 }
 
