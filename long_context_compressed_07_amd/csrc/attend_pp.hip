@@ -145,7 +145,10 @@ __device__ __forceinline__ void load_q16_lds(int base, v4i (&q)[36]) {
 // TOK: token selection (a.tok_m > 0). The entry form is compiled with the token fields known to
 // be zero, so its per-tile key arithmetic has no branches and the compiler can place it among
 // the MFMAs.
-template <bool TOK>
+// DENSE: hca_attend, whose keys are the visible entries in order (key kk is entry row kk): the
+// QK waves take the rows' addresses and the tile masks from the key index, and the PV waves compute
+// no key codes after the prologue.
+template <bool TOK, bool DENSE>
 __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan plan) {
   constexpr int TK = kPpTK;
   constexpr int R = kPpR;
@@ -294,26 +297,39 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
         dma.sel = (sel_dma && lane < TK && kk < ke && kk < kl.n_sel)
                       ? reinterpret_cast<const char*>(kl.sel + sel_index(kl, kk))
                       : reinterpret_cast<const char*>(kZeroRow);
-        const KeyAddr* ad = s_addr[(i + 2) % kPpBuf];
-        const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
         dma.off[0] = 16 * (lane ^ swz(w));
         dma.off[1] = 16 * (lane ^ swz(w + 4));
-#pragma unroll
-        for (int j = 0; j < TK / 4; ++j) {
-          const uint64_t base =
-              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uintptr_t)mine, j)) |
-              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uintptr_t)mine >> 32), j)
-               << 32);
-          dma.lat[j] = reinterpret_cast<const char*>(base);
-        }
         const int rr = 8 * w + (lane >> 3);
-        dma.rope[0] = ad[rr].rope + 16 * ((lane & 7) ^ swz(rr));
+        if constexpr (DENSE) {
+          // Entry rows of tile i + 2. A key past the list reads the list's last row instead
+          // (finite values; its logit is masked to -inf, so it adds 0 to every sum).
+          const int tb = (int)(t0 + 2 * TK), last = (int)ke - 1;
+          const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform: scalar addresses
+#pragma unroll
+          for (int j = 0; j < TK / 4; ++j)
+            dma.lat[j] = rbases.c0 + (uint64_t)(uint32_t)min(tb + 4 * j + wu, last) * rbases.ldc0;
+          dma.rope[0] = rbases.r0 + (uint64_t)(uint32_t)min(tb + rr, last) * rbases.ldr0 +
+                        16 * ((lane & 7) ^ swz(rr));
+        } else {
+          const KeyAddr* ad = s_addr[(i + 2) % kPpBuf];
+          const char* mine = lane < TK / 4 ? ad[4 * lane + w].lat : nullptr;
+#pragma unroll
+          for (int j = 0; j < TK / 4; ++j) {
+            const uint64_t base =
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uintptr_t)mine, j)) |
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                     (int)(uint32_t)((uintptr_t)mine >> 32), j)
+                 << 32);
+            dma.lat[j] = reinterpret_cast<const char*>(base);
+          }
+          dma.rope[0] = ad[rr].rope + 16 * ((lane & 7) ^ swz(rr));
+        }
         dma.m0_rows = __builtin_amdgcn_readfirstlane(lds_addr(nbuf) + 1024 * w);
         dma.m0_sel = __builtin_amdgcn_readfirstlane(
             lds_addr(reinterpret_cast<const char*>(s_sel[(i + 5) % 3])));
       }
       // Whether the tile holds a key / only keys (uniform), from its 32 codes.
-      const int code_l = s_code[slot][lane & (TK - 1)];
+      const int code_l = DENSE ? (t0 + (lane & (TK - 1)) < ke ? 0 : -1) : s_code[slot][lane & (TK - 1)];
       floatx4 acc[2];
       const int cb = lds_addr(cbuf);
       qk16_chain(qb, cb + lat_off + oe, cb + lat_off + oo, cb + rope_off + oe, cb + rope_off + oo,
@@ -324,7 +340,7 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
         const int* codes = s_code[slot];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool ok = codes[16 * kh + 4 * g + j] >= 0;
+          const bool ok = DENSE ? t0 + 16 * kh + 4 * g + j < ke : codes[16 * kh + 4 * g + j] >= 0;
           acc[0][j] = ok ? acc[0][j] : -INFINITY;
           acc[1][j] = ok ? acc[1][j] : -INFINITY;
         }
@@ -511,17 +527,17 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
     for (int j = 0; j < 8; ++j) vh[j] = f16x8{};
     for (int i = 0; i <= nt; ++i) {
       if (i < nt && !have_ref) {   // the QK waves' reference barrier, at the first tile with a key
-        if (__any(s_code[i % kPpBuf][kl32] >= 0)) {
+        if (DENSE || __any(s_code[i % kPpBuf][kl32] >= 0)) {
           lds_barrier();
           have_ref = true;
         }
       }
-      const int raw = s_sel[(i + 3) % 3][kl32];   // issued first: waited for by count
+      const int raw = DENSE ? 0 : s_sel[(i + 3) % 3][kl32];   // issued first: waited for by count
       v4i pf[4];
       read_p(s_p[(i + 1) & 1], pf);
       v2i vr[16];
       read_v(kv[i % kPpBuf], vr);
-      codes(i, raw);
+      if (!DENSE) codes(i, raw);
       const bool first = i == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) pf[j] = first ? v4i{} : pf[j];
@@ -630,9 +646,11 @@ __global__ void __launch_bounds__(512) attend_pp_kernel(AttendArgs a, AttnPlan p
 hipError_t launch_attend_pp(const AttendArgs& a, const AttnPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.Q.nq * p.head_groups * p.n_split);
   if (a.tok_m > 0)
-    attend_pp_kernel<true><<<grid, 512, 0, s>>>(a, p);
+    attend_pp_kernel<true, false><<<grid, 512, 0, s>>>(a, p);
+  else if (a.dense)
+    attend_pp_kernel<false, true><<<grid, 512, 0, s>>>(a, p);
   else
-    attend_pp_kernel<false><<<grid, 512, 0, s>>>(a, p);
+    attend_pp_kernel<false, false><<<grid, 512, 0, s>>>(a, p);
   return hipGetLastError();
 }
 
