@@ -22,8 +22,8 @@
 //     row addresses of tile i + 3 (the same values), in between.
 // One barrier closes each iteration. Each SIMD holds one wave of each role, so while one runs its
 // softmax, conversions or LDS traffic the other keeps the matrix unit busy. The prologue copies
-// the 64 heads' queries once by DMA (into the two buffers idle until the first tile) and the QK
-// waves read their fragments from there.
+// the 64 heads' queries once (loads written into the two buffers idle until the first tile) and
+// the QK waves read their fragments from there.
 //
 // Numerics: bf16 products exact in fp32, V converted to fp16 (exact in fp16's normal range), P
 // fp16, fixed reference maximum from the first tile that holds a key, and a non-finite output
