@@ -114,7 +114,9 @@ typedef struct {
  *   out    entry store with out->rows == T/m: out->dtype_c CSA_F32, CSA_BF16 (RNE) or CSA_E4M3
  *          (one fp32 scale per row, scale = amax(|e_c|)/448, codes RNE-satfinite of e_c/scale;
  *          an all-zero row stores scale 0). The r part is stored bf16 (fp32 when out is F32).
- *   Constraints: m >= 1, T >= 0, d % 4 == 0 (fp32) or d % 8 == 0 (bf16).
+ *   Constraints: m >= 1, T >= 0, d % 4 == 0 (fp32) or d % 8 == 0 (bf16). Projection mode also
+ *   needs d % 64 == 0, an even d_c, d_model % 4 == 0, m in {1, 2, 4}, a non-E4M3 out and 16-byte
+ *   aligned hidden, w_x, w_g (CSA_EUNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const float* bias,
                         int32_t m, int32_t B, int64_t T, int32_t d_c, int32_t d_r,
@@ -239,6 +241,8 @@ csa_status csa_topk_bf16(const csa_queries_t* Q, const uint16_t* scores, int64_t
  *          the last raw->rows positions written to it. Selected slots holding a row at or past
  *          entries->rows are skipped like -1 slots.
  *   out    [nq][H][d_c] fp32; lse [nq][H] fp32 (may be NULL).
+ *   Shapes: d_c <= 1024, d_c + d_r even and <= 4096 (else CSA_EUNSUPPORTED; the same for
+ *   csa_attend_tokens and hca_attend).
  *   Workspace: csa_attend_workspace_bytes(nq, H, d_c, k + window).
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_attend(const csa_queries_t* Q, const void* q, int32_t q_dtype, int32_t H,

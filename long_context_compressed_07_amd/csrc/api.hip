@@ -99,8 +99,10 @@ csa_status csa_compress(const void* x, const void* g, int32_t in_dtype, const fl
     if (x != nullptr || g != nullptr) return fail(CSA_EINVAL, "projection mode takes no x/g");
     if (!hidden || !w_x || !w_g || !raw_x_out) return fail(CSA_EINVAL, "projection mode needs hidden, w_x, w_g, raw_x_out");
     if (in_dtype != CSA_F32 || d_model <= 0) return fail(CSA_EINVAL, "projection mode is fp32 with d_model > 0");
-    if (d % 64 != 0 || d_model % 4 != 0 || (m != 1 && m != 2 && m != 4) || out->dtype_c == CSA_E4M3)
-      return fail(CSA_EUNSUPPORTED, "projection mode needs d % 64 == 0, d_model % 4 == 0, m in {1,2,4}, non-fp8 out");
+    if (d % 64 != 0 || d_c % 2 != 0 || d_model % 4 != 0 || (m != 1 && m != 2 && m != 4) ||
+        out->dtype_c == CSA_E4M3)
+      return fail(CSA_EUNSUPPORTED,
+                  "projection mode needs d % 64 == 0, even d_c, d_model % 4 == 0, m in {1,2,4}, non-fp8 out");
     if (!aligned16(hidden) || !aligned16(w_x) || !aligned16(w_g))
       return fail(CSA_EUNSUPPORTED, "projection operands must be 16-byte aligned");
   } else {
@@ -225,8 +227,9 @@ csa_status check_attend_common(const csa_queries_t* Q, const void* q, int32_t q_
   if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return fail(CSA_EINVAL, "q_dtype must be F32 or BF16");
   if (H <= 0 || m < 1) return fail(CSA_EINVAL, "bad H or m");
   if (Q->nq > 0 && (q == nullptr || out == nullptr)) return fail(CSA_EINVAL, "null q or out");
-  if (entries->d_c > 1024 || (entries->d_c + entries->d_r) % 2 != 0)
-    return fail(CSA_EUNSUPPORTED, "d_c must be <= 1024 and d_c + d_r even");
+  if (entries->d_c > 1024 || (entries->d_c + entries->d_r) % 2 != 0 ||
+      entries->d_c + entries->d_r > 4096)
+    return fail(CSA_EUNSUPPORTED, "d_c must be <= 1024, d_c + d_r even and <= 4096");
   return CSA_OK;
 }
 

@@ -104,4 +104,177 @@ __host__ __device__ constexpr size_t generic_smem_bytes(int d) {
   return sizeof(float) * (d + kGenThreads + 8) + sizeof(int64_t) * kGenThreads + sizeof(int) * kGenThreads;
 }
 
+// The same arithmetic as attend_generic_one (same sums in the same order, so the same results),
+// with each chunk's key rows first copied into LDS by the whole block: row elements are read once,
+// by consecutive threads, instead of one row per thread in the logits and one dependent load per
+// key in the output sums. A chunk holds `chunk` keys (at most kGenThreads); rows are stored with a
+// stride of d + 1 floats so that the threads of the logit loop, one key each, read different banks.
+__host__ __device__ constexpr int staged_row_stride(int d) { return d + 1; }
+
+// Floats ahead of the 8-byte row indices: the query (d rounded up to even), probabilities and
+// row scales of the chunk, the reduction slots.
+__host__ __device__ constexpr int staged_floats(int d) { return ((d + 1) & ~1) + 2 * kGenThreads + 8; }
+
+__host__ __device__ constexpr size_t staged_fixed_bytes(int d) {
+  return sizeof(float) * staged_floats(d) + 2 * sizeof(uint64_t) * kGenThreads;
+}
+
+// Keys per chunk that fit `budget` bytes of LDS (at least 1, at most kGenThreads).
+__host__ __device__ constexpr int staged_chunk(int d, size_t budget) {
+  const size_t row = sizeof(float) * (size_t)staged_row_stride(d);
+  const size_t fixed = staged_fixed_bytes(d);
+  const size_t n = budget > fixed ? (budget - fixed) / row : 0;
+  return n < 1 ? 1 : (n > (size_t)kGenThreads ? kGenThreads : (int)n);
+}
+
+__host__ __device__ constexpr size_t staged_smem_bytes(int d, int chunk) {
+  return staged_fixed_bytes(d) + sizeof(float) * (size_t)staged_row_stride(d) * chunk;
+}
+
+// A load through a global-memory pointer: the store pointers come from the argument struct, so
+// the compiler cannot tell them from LDS and would emit flat loads, which also count as LDS
+// operations and make every wait for an LDS read a wait for the row loads as well.
+template <typename T>
+__device__ __forceinline__ T gload(const void* base, int64_t off) {
+  typedef __attribute__((address_space(1))) const T GT;
+  return ((GT*)base)[off];
+}
+
+// The chunk's cnt rows into sk (row j at j * ld), element by element in row order, from the rows'
+// addresses in s_cptr / s_rptr (0: no row; the row's c part, then its r part, of dtype DT): 32
+// loads per thread are issued before their LDS stores, so the copy is not a chain of load
+// latencies.
+template <int DT>
+__device__ void stage_rows(int d_c, int cnt, int d, int ld, const uint64_t* s_cptr,
+                           const uint64_t* s_rptr, float* sk) {
+  constexpr int kBatch = 32;
+  const int n = cnt * d;
+  for (int i0 = 0; i0 < n; i0 += kBatch * kGenThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kGenThreads + (int)threadIdx.x;
+      v[u] = 0.f;
+      if (i < n) {
+        const int j = i / d, e = i - j * d;
+        const uint64_t cp = s_cptr[j];
+        if (cp != 0) {
+          if (e < d_c) {
+            const void* c = (const void*)(uintptr_t)cp;
+            if constexpr (DT == CSA_F32) v[u] = gload<float>(c, e);
+            else if constexpr (DT == CSA_BF16) v[u] = bf16_to_f32(gload<uint16_t>(c, e));
+            else v[u] = e4m3_to_f32(gload<uint8_t>(c, e));
+          } else {
+            const void* r = (const void*)(uintptr_t)s_rptr[j];
+            if constexpr (DT == CSA_F32) v[u] = gload<float>(r, e - d_c);
+            else v[u] = bf16_to_f32(gload<uint16_t>(r, e - d_c));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kGenThreads + (int)threadIdx.x;
+      if (i < n) {
+        const int j = i / d;
+        sk[j * ld + (i - j * d)] = v[u];
+      }
+    }
+  }
+}
+
+static __device__ void attend_generic_staged(const AttendArgs& a, int qi, int h, float* smem,
+                                             int chunk) {
+  const int d_c = a.ent.d_c, d_r = a.ent.d_r, d = d_c + d_r;
+  const int ld = staged_row_stride(d);
+  float* sq = smem;                                // [d]
+  float* sp = sq + ((d + 1) & ~1);                 // [kGenThreads] probabilities of the chunk
+  float* s_scale = sp + kGenThreads;               // [kGenThreads] row scale of each key
+  float* s_red = s_scale + kGenThreads;            // [8]
+  // [kGenThreads] address of each key's c row (0: no row) and r row
+  uint64_t* s_cptr = reinterpret_cast<uint64_t*>(smem + staged_floats(d));
+  uint64_t* s_rptr = s_cptr + kGenThreads;
+  float* sk = reinterpret_cast<float*>(s_rptr + kGenThreads);     // [chunk][ld]
+  const KeyList kl = make_key_list(a, qi);
+  const int csz = a.ent.dtype == CSA_F32 ? 4 : (a.ent.dtype == CSA_BF16 ? 2 : 1);
+  const int rsz = a.ent.dtype == CSA_F32 ? 4 : 2;
+  for (int e = threadIdx.x; e < d; e += kGenThreads)
+    sq[e] = load_vec(a.q, a.q_dtype, ((int64_t)qi * a.H + h) * d + e);
+  constexpr int kMaxPer = 4;             // output dims per thread: d_c <= 1024
+  float o[kMaxPer] = {0.f, 0.f, 0.f, 0.f};
+  float run_max = -INFINITY, run_sum = 0.f;
+  for (int64_t c0 = 0; c0 < kl.total; c0 += chunk) {
+    const int cnt = (int)(kl.total - c0 < chunk ? kl.total - c0 : chunk);
+    if ((int)threadIdx.x < cnt) {
+      int src = 0;
+      const int64_t row = key_row(a, kl, c0 + threadIdx.x, src);
+      uint64_t cp = 0, rp = 0;
+      float sc = 0.f;
+      if (row >= 0) {
+        const Store& st = src ? a.raw : a.ent;
+        const int64_t gr = kl.b * st.rows + row;
+        cp = (uint64_t)(uintptr_t)st.c + (uint64_t)(gr * st.ld_c * csz);
+        rp = st.r != nullptr ? (uint64_t)(uintptr_t)st.r + (uint64_t)(gr * st.ld_r * rsz) : 0;
+        sc = row_scale(st, kl.b, row);
+      }
+      s_cptr[threadIdx.x] = cp;
+      s_rptr[threadIdx.x] = rp;
+      s_scale[threadIdx.x] = sc;
+    }
+    __syncthreads();
+    // The chunk's rows (entries and raw rows share the dtype).
+    if (a.ent.dtype == CSA_F32)
+      stage_rows<CSA_F32>(d_c, cnt, d, ld, s_cptr, s_rptr, sk);
+    else if (a.ent.dtype == CSA_BF16)
+      stage_rows<CSA_BF16>(d_c, cnt, d, ld, s_cptr, s_rptr, sk);
+    else
+      stage_rows<CSA_E4M3>(d_c, cnt, d, ld, s_cptr, s_rptr, sk);
+    __syncthreads();
+    float logit = -INFINITY;
+    const bool my_key = (int)threadIdx.x < cnt && s_cptr[threadIdx.x] != 0;
+    if (my_key) {
+      const float* kr = sk + threadIdx.x * ld;
+      float dc = 0.f, dr = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < d_c; ++e) dc = fmaf(sq[e], kr[e], dc);
+#pragma unroll 8
+      for (int e = 0; e < d_r; ++e) dr = fmaf(sq[d_c + e], kr[d_c + e], dr);
+      logit = a.sm_scale * fmaf(dc, s_scale[threadIdx.x], dr);
+    }
+    const float cmax = block_reduce(logit, s_red, true);
+    const float new_max = fmaxf(run_max, cmax);
+    float p = 0.f;
+    if (my_key && new_max > -INFINITY) p = expf(logit - new_max);
+    sp[threadIdx.x] = p;
+    const float csum = block_reduce(p, s_red, false);
+    const float corr = run_max > -INFINITY ? expf(run_max - new_max) : 0.f;
+    run_sum = run_sum * corr + csum;
+#pragma unroll
+    for (int r = 0; r < kMaxPer; ++r) o[r] *= corr;
+    run_max = new_max;
+#pragma unroll 4
+    for (int j = 0; j < cnt; ++j) {
+      const float pj = sp[j];
+      if (pj == 0.f) continue;
+      const float w = pj * s_scale[j];
+      const float* vr = sk + j * ld;
+#pragma unroll
+      for (int r = 0; r < kMaxPer; ++r) {
+        const int e = threadIdx.x + r * kGenThreads;
+        if (e < d_c) o[r] = fmaf(w, vr[e], o[r]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t ob = ((int64_t)qi * a.H + h) * d_c;
+  const float inv = run_sum > 0.f ? 1.0f / run_sum : 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxPer; ++r) {
+    const int e = threadIdx.x + r * kGenThreads;
+    if (e < d_c) a.out[ob + e] = o[r] * inv;
+  }
+  if (a.lse != nullptr && threadIdx.x == 0)
+    a.lse[(int64_t)qi * a.H + h] = run_sum > 0.f ? run_max + logf(run_sum) : -INFINITY;
+}
+
 }  // namespace csa

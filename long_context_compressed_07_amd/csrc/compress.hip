@@ -142,76 +142,89 @@ __global__ void __launch_bounds__(256) pool_kernel(CompressArgs a, int cpr, int 
   if (active) store_entry<VEC>(a.out, b, j, ch, acc, sigma);
 }
 
-// fp32 projection + pooling. Tile: 64 tokens x 64 channels of both x and g; thread (ty, tx) owns
-// tokens [4ty, 4ty+4) and channels [4tx, 4tx+4), so every block of m in {1, 2, 4} tokens is
-// thread-local.
+// fp32 projection + pooling. Tile: 64 tokens x 32 channels of both x and g; thread (ty, tx) owns
+// tokens [4ty, 4ty+4) and channels [2tx, 2tx+2), so every block of m in {1, 2, 4} tokens is
+// thread-local. Each output is one fma chain over the model dims in order. 32-channel tiles give
+// the 4096-token, 128-channel projection 256 workgroups (one per CU) and 16 outputs per thread.
 __global__ void __launch_bounds__(256) project_pool_kernel(CompressArgs a) {
-  constexpr int TK = 16;
+  constexpr int TK = 32;
+  constexpr int TC = 32;
   __shared__ float sh[64][TK + 1];
-  __shared__ float swx[TK][64];
-  __shared__ float swg[TK][64];
+  __shared__ float swx[TK][TC];
+  __shared__ float swg[TK][TC];
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
   const int64_t b = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const int c0 = blockIdx.y * 64;
+  const int c0 = blockIdx.y * TC;
   const int d = a.d_c + a.d_r;
   const int dm = a.d_model;
-  float ax[4][4] = {}, ag[4][4] = {};
+  // Slice k0 .. k0 + TK of the model dims: hidden 64 tokens x 32 (two float4 per thread), w_x
+  // (waves 0-1) or w_g (waves 2-3) 32 rows x 32 channels (two float4 per thread). The next
+  // slice's loads are issued before the current slice's products, so their latency overlaps them.
+  const int tok = tid >> 2, kq = (tid & 3) * 4;
+  const int wt = tid & 127, wr = wt >> 3, wc = (wt & 7) * 4;
+  const float* W = tid < 128 ? a.w_x : a.w_g;
+  float4 hv[2], wv[2];
+  auto load_slice = [&](int k0) {
+    const int64_t t = t0 + tok;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = k0 + kq + 16 * u;
+      hv[u] = t < a.T && k < dm ? *reinterpret_cast<const float4*>(a.hidden + (b * a.T + t) * dm + k)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int kr = k0 + wr + 16 * u;
+      wv[u] = kr < dm ? *reinterpret_cast<const float4*>(W + (int64_t)kr * d + c0 + wc)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float ax[4][2] = {}, ag[4][2] = {};
+  load_slice(0);
   for (int k0 = 0; k0 < dm; k0 += TK) {
-    {
-      const int tok = tid >> 2, kq = (tid & 3) * 4;
-      const int64_t t = t0 + tok;
-      float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < a.T && k0 + kq < dm)
-        hv = *reinterpret_cast<const float4*>(a.hidden + (b * a.T + t) * dm + k0 + kq);
-      sh[tok][kq] = hv.x; sh[tok][kq + 1] = hv.y; sh[tok][kq + 2] = hv.z; sh[tok][kq + 3] = hv.w;
-      const int wr = tid >> 4, wc = (tid & 15) * 4;
-      float4 wx = make_float4(0.f, 0.f, 0.f, 0.f), wg = wx;
-      if (k0 + wr < dm) {
-        wx = *reinterpret_cast<const float4*>(a.w_x + (int64_t)(k0 + wr) * d + c0 + wc);
-        wg = *reinterpret_cast<const float4*>(a.w_g + (int64_t)(k0 + wr) * d + c0 + wc);
-      }
-      *reinterpret_cast<float4*>(&swx[wr][wc]) = wx;
-      *reinterpret_cast<float4*>(&swg[wr][wc]) = wg;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = kq + 16 * u;
+      sh[tok][kk] = hv[u].x; sh[tok][kk + 1] = hv[u].y; sh[tok][kk + 2] = hv[u].z; sh[tok][kk + 3] = hv[u].w;
+      *reinterpret_cast<float4*>(tid < 128 ? &swx[wr + 16 * u][wc] : &swg[wr + 16 * u][wc]) = wv[u];
     }
     __syncthreads();
+    if (k0 + TK < dm) load_slice(k0 + TK);
 #pragma unroll
     for (int kk = 0; kk < TK; ++kk) {
       float h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) h[r] = sh[ty * 4 + r][kk];
-      const float4 wx = *reinterpret_cast<const float4*>(&swx[kk][tx * 4]);
-      const float4 wg = *reinterpret_cast<const float4*>(&swg[kk][tx * 4]);
-      const float wxv[4] = {wx.x, wx.y, wx.z, wx.w};
-      const float wgv[4] = {wg.x, wg.y, wg.z, wg.w};
+      const float2 wx = *reinterpret_cast<const float2*>(&swx[kk][tx * 2]);
+      const float2 wg = *reinterpret_cast<const float2*>(&swg[kk][tx * 2]);
+      const float wxv[2] = {wx.x, wx.y};
+      const float wgv[2] = {wg.x, wg.y};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
           ax[r][c] = fmaf(h[r], wxv[c], ax[r][c]);
           ag[r][c] = fmaf(h[r], wgv[c], ag[r][c]);
         }
     }
     __syncthreads();
   }
-  const int ch = c0 + tx * 4;
+  const int ch = c0 + tx * 2;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t t = t0 + ty * 4 + r;
     if (t < a.T) {
       float* p = a.raw_x_out + (b * a.T + t) * d + ch;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) p[c] = ax[r][c];
+      for (int c = 0; c < 2; ++c) p[c] = ax[r][c];
     }
   }
   const int m = a.m;
   for (int blk = 0; blk < 4 / m; ++blk) {
     const int64_t tb = t0 + ty * 4 + blk * m;  // first token of the block
     if (tb + m > a.T) break;
-    float e[4];
+    float e[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
       float ai[4], xi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -223,7 +236,7 @@ __global__ void __launch_bounds__(256) project_pool_kernel(CompressArgs a) {
       pool_fold(pa, ai, xi, m);
       e[c] = pool_value(pa);
     }
-    store_entry<4>(a.out, b, tb / m, ch, e, 0.f);
+    store_entry<2>(a.out, b, tb / m, ch, e, 0.f);
   }
 }
 
@@ -234,7 +247,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const int64_t nb = a.T / a.m;
   if (a.hidden != nullptr) {
     if (a.T == 0) return hipSuccess;
-    dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)(d / 64), (unsigned)a.B);
+    dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)(d / 32), (unsigned)a.B);
     project_pool_kernel<<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
