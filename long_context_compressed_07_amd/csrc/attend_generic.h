@@ -104,8 +104,10 @@ __host__ __device__ constexpr size_t generic_smem_bytes(int d) {
   return sizeof(float) * (d + kGenThreads + 8) + sizeof(int64_t) * kGenThreads + sizeof(int) * kGenThreads;
 }
 
-// The same arithmetic as attend_generic_one (same sums in the same order, so the same results),
-// with each chunk's key rows first copied into LDS by the whole block: row elements are read once,
+// The arithmetic of attend_generic_one (an online softmax over chunks of keys; within a chunk the
+// same sums in the same order), with chunks of `chunk` keys whose rows are first copied into LDS
+// by the whole block (the chunk boundaries, where the running sums are rescaled, differ, so results
+// agree to rounding): row elements are read once,
 // by consecutive threads, instead of one row per thread in the logits and one dependent load per
 // key in the output sums. A chunk holds `chunk` keys (at most kGenThreads); rows are stored with a
 // stride of d + 1 floats so that the threads of the logit loop, one key each, read different banks.
