@@ -80,6 +80,19 @@ index_bf16_mfma_kernel(IndexArgs a) {
     }
   }
   __syncthreads();
+  // This lane's four queries (8 w + 4 rt + 2 hi + u): head weights and visible entries in
+  // registers, so the block loop's barriers do not make it read them again from LDS.
+  float wreg[2][2][8];
+  int nvreg[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ql = 8 * w + 4 * rt + 2 * hi + u;
+      nvreg[rt][u] = s_nv[ql];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wreg[rt][u][e] = s_w[ql * 8 + e];
+    }
   // One pass: stage sequence b's key blocks and write the scores of the queries in `cur`.
   auto pass = [&](int64_t b, uint32_t cur, int nmax) {
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_i) + b * a.N * 64;
@@ -117,21 +130,24 @@ index_bf16_mfma_kernel(IndexArgs a) {
           bfr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(s_k + (32 * ct + (lane & 31)) * kRowK +
                                                              16 * s + 8 * hi));
         const int ent = e0 + 32 * ct + (lane & 31);
+        // The two row tiles' chains interleaved (independent MFMAs back to back).
+        floatx16 accs[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            accs[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][s], bfr[s], accs[rt], 0, 0, 0);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          floatx16 acc = floatx16{};
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][s], bfr[s], acc, 0, 0, 0);
+          const floatx16& acc = accs[rt];
           // acc[8 u + e] = head e of query 8 w + 4 rt + 2 hi + u (u = 0, 1), entry `ent`.
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int ql = 8 * w + 4 * rt + 2 * hi + u;
-            const float* wq = s_w + ql * 8;
             float p = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p = fmaf(wq[e], fmaxf(acc[8 * u + e], 0.f), p);
-            if (((cur >> ql) & 1u) && ent < s_nv[ql])
+            for (int e = 0; e < 8; ++e) p = fmaf(wreg[rt][u][e], fmaxf(acc[8 * u + e], 0.f), p);
+            if (((cur >> ql) & 1u) && ent < nvreg[rt][u])
               a.scores[(int64_t)(q0 + ql) * a.ld_scores + ent] = p;
           }
         }
