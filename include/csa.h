@@ -167,7 +167,8 @@ csa_status csa_cache_append(const void* x_new, const void* g_new, int32_t in_dty
  *   k_i    [B][N][d_I] in ki_dtype (same dtype as q_i); k_i_scale [B][N] fp32 iff E4M3.
  *          For fp8: qI = q_i_scale * q_i and kI = k_i_scale * k_i.
  *   scores [nq][ld_scores] fp32, ld_scores >= N. Columns j >= n_vis(pos[i]) are not written.
- *   Constraints: d_I == 64 for E4M3/BF16 fast paths; any d_I % 4 == 0 otherwise.
+ *   Constraints: d_I == 64 for E4M3/BF16 fast paths; any d_I % 4 == 0 otherwise, with
+ *   H_I * (d_I + 1) * 4 <= 32 KiB (CSA_EUNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_index(const csa_queries_t* Q, const void* q_i, const float* q_i_scale,
                      int32_t qi_dtype, const float* w, int32_t H_I, int32_t d_I, const void* k_i,

@@ -131,7 +131,7 @@ csa_status csa_index(const csa_queries_t* Q, const void* q_i, const float* q_i_s
   if (N > 0 && k_i == nullptr) return fail(CSA_EINVAL, "null k_i");
   if (qi_dtype == CSA_E4M3 && (q_i_scale == nullptr || k_i_scale == nullptr))
     return fail(CSA_EINVAL, "fp8 indexer needs q_i_scale and k_i_scale");
-  if ((size_t)H_I * (d_I + 1) * sizeof(float) > 64 * 1024) return fail(CSA_EUNSUPPORTED, "H_I * d_I too large");
+  if ((size_t)H_I * (d_I + 1) * sizeof(float) > 32 * 1024) return fail(CSA_EUNSUPPORTED, "H_I * d_I too large");
   csa::IndexArgs a{csa::Queries{Q->seq, Q->pos, Q->nq}, q_i, q_i_scale, qi_dtype, w, H_I, d_I,
                    k_i, k_i_scale, B, N, m, scores, ld_scores};
   return hip_status(csa::launch_index(a, static_cast<hipStream_t>(stream)));

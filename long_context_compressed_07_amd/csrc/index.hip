@@ -5,17 +5,58 @@
 // lightning indexer, FP8 accelerated). The ReLU-weighted head sum is this library's reading.
 //
 // index_generic_kernel: one thread per (query, entry), any dtype and d_I; the query's heads are
-// dequantised once into LDS. It is the reference kernel and the fallback for shapes without a
-// specialised path.
+// dequantised once into LDS and the workgroup's key rows are copied into LDS first (coalesced
+// loads, a batch of 16 in flight per thread; rows d_I + 1 floats apart so that the threads, one
+// entry each, read different banks). It is the reference kernel and the fallback for shapes
+// without a specialised path. Each entry's sums run in the same order as a row-by-row loop.
 #include "common.h"
 
 namespace csa {
 namespace {
 
-__global__ void __launch_bounds__(256) index_generic_kernel(IndexArgs a, int tiles) {
+// A load through a global-memory pointer (the argument struct's pointers would otherwise be
+// treated as generic and loaded with flat instructions).
+template <typename T>
+__device__ __forceinline__ T gload(const void* base, int64_t off) {
+  typedef __attribute__((address_space(1))) const T GT;
+  return ((GT*)base)[off];
+}
+
+template <int DT>
+__device__ __forceinline__ float key_elem(const void* k, int64_t off) {
+  if constexpr (DT == CSA_F32) return gload<float>(k, off);
+  if constexpr (DT == CSA_BF16) return bf16_to_f32(gload<uint16_t>(k, off));
+  return e4m3_to_f32(gload<uint8_t>(k, off));
+}
+
+// Entries [j0, j0 + cnt) of sequence b's keys into sk (entry j at j * (d_I + 1)).
+template <int DT>
+__device__ void stage_keys(const IndexArgs& a, int64_t b, int64_t j0, int cnt, float* sk) {
+  constexpr int kBatch = 16;
+  const int d = a.d_I, n = cnt * d;
+  const int64_t base = (b * a.N + j0) * d;
+  for (int i0 = 0; i0 < n; i0 += kBatch * 256) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      v[u] = i < n ? key_elem<DT>(a.k_i, base + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      if (i < n) {
+        const int j = i / d;
+        sk[j * (d + 1) + (i - j * d)] = v[u];
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) index_generic_kernel(IndexArgs a, int tiles, int ept) {
   extern __shared__ float smem[];
   const int qi = blockIdx.x / tiles;
-  const int64_t j0 = (int64_t)(blockIdx.x - qi * tiles) * 256;
+  const int64_t j0 = (int64_t)(blockIdx.x - qi * tiles) * ept;
   const int64_t pos = a.Q.pos[qi];
   const int64_t b = a.Q.seq[qi];
   const int64_t nv = n_visible(pos, a.m, a.N);
@@ -23,24 +64,34 @@ __global__ void __launch_bounds__(256) index_generic_kernel(IndexArgs a, int til
   const int hd = a.H_I * a.d_I;
   float* sq = smem;
   float* sw = smem + hd;
+  float* sk = sw + a.H_I;
   for (int e = threadIdx.x; e < hd; e += blockDim.x) {
     float v = load_vec(a.q_i, a.dtype, (int64_t)qi * hd + e);
     if (a.dtype == CSA_E4M3) v *= a.q_i_scale[(int64_t)qi * a.H_I + e / a.d_I];
     sq[e] = v;
   }
   for (int h = threadIdx.x; h < a.H_I; h += blockDim.x) sw[h] = a.w[(int64_t)qi * a.H_I + h];
+  const int cnt = (int)(nv - j0 < ept ? nv - j0 : ept);
+  if (a.dtype == CSA_F32)
+    stage_keys<CSA_F32>(a, b, j0, cnt, sk);
+  else if (a.dtype == CSA_BF16)
+    stage_keys<CSA_BF16>(a, b, j0, cnt, sk);
+  else
+    stage_keys<CSA_E4M3>(a, b, j0, cnt, sk);
   __syncthreads();
-  const int64_t j = j0 + threadIdx.x;
-  if (j >= nv) return;
-  const int64_t krow = (b * a.N + j) * a.d_I;
-  const float ks = a.dtype == CSA_E4M3 ? a.k_i_scale[b * a.N + j] : 1.0f;
-  float s = 0.f;
-  for (int h = 0; h < a.H_I; ++h) {
-    float dot = 0.f;
-    for (int e = 0; e < a.d_I; ++e) dot = fmaf(sq[h * a.d_I + e], load_vec(a.k_i, a.dtype, krow + e), dot);
-    s = fmaf(sw[h], fmaxf(dot * ks, 0.f), s);
+  for (int jj = threadIdx.x; jj < cnt; jj += blockDim.x) {
+    const int64_t j = j0 + jj;
+    const float ks = a.dtype == CSA_E4M3 ? a.k_i_scale[b * a.N + j] : 1.0f;
+    const float* kr = sk + jj * (a.d_I + 1);
+    float s = 0.f;
+    for (int h = 0; h < a.H_I; ++h) {
+      float dot = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < a.d_I; ++e) dot = fmaf(sq[h * a.d_I + e], kr[e], dot);
+      s = fmaf(sw[h], fmaxf(dot * ks, 0.f), s);
+    }
+    a.scores[(int64_t)qi * a.ld_scores + j] = s;
   }
-  a.scores[(int64_t)qi * a.ld_scores + j] = s;
 }
 
 }  // namespace
@@ -51,9 +102,15 @@ hipError_t launch_index(const IndexArgs& a, hipStream_t s) {
   if (a.Q.nq == 0 || a.N == 0) return hipSuccess;
   hipError_t err;
   if (index_fast(a, s, &err)) return err;
-  const int tiles = (int)((a.N + 255) / 256);
-  const size_t shm = sizeof(float) * ((size_t)a.H_I * a.d_I + a.H_I);
-  index_generic_kernel<<<(unsigned)((int64_t)tiles * a.Q.nq), 256, shm, s>>>(a, tiles);
+  // Entries per workgroup: as many key rows as fit 64 KB of LDS beside the query (at most 256;
+  // the query takes at most 32 KB, so at least one row fits).
+  const size_t fixed = sizeof(float) * ((size_t)a.H_I * a.d_I + a.H_I);
+  const size_t row = sizeof(float) * ((size_t)a.d_I + 1);
+  const size_t fit = (64 * 1024 - fixed) / row;
+  const int ept = (int)(fit > 256 ? 256 : fit);
+  const int tiles = (int)((a.N + ept - 1) / ept);
+  index_generic_kernel<<<(unsigned)((int64_t)tiles * a.Q.nq), 256, fixed + row * ept, s>>>(a, tiles,
+                                                                                           ept);
   return hipGetLastError();
 }
 
