@@ -63,6 +63,7 @@ class Step:
             self.lse = torch.empty((self.nq, wl.H), **f32)
             need = lib.hca_attend_workspace_bytes(self.nq, wl.H, d_c, N)
             self.ws["hca"] = torch.empty(max(need, 1), dtype=torch.uint8, device=self.dev)
+            self._bind()
             return
         self.scores = torch.empty((self.nq, N), **f32)
         self.idx = torch.empty((self.nq, wl.k), dtype=torch.int32, device=self.dev)
@@ -84,8 +85,10 @@ class Step:
             # The HCA layer reads nothing the CSA layer writes: it runs on a second stream (default
             # priority, like every stream here) beside the CSA attention.
             self._side = torch.cuda.Stream(device=self.dev)
+            self._side_h = self._side.cuda_stream
             self._fork = torch.cuda.Event()
             self._join = torch.cuda.Event()
+        self._bind()
 
     def _given_store(self, pfx: str, rows: int, pos0=None) -> lib.Store:
         wl = self.wl
@@ -94,66 +97,90 @@ class Step:
                          pos0=pos0)
 
     # ---- the individual calls ------------------------------------------------------------
-    def compress(self):
+    # Each call's arguments are marshalled once (lib's bind=True form); a call then costs the host
+    # one foreign call, on the stream current when it is made.
+    def _bind(self):
         wl, t = self.wl, self.t
-        if wl.d_model:
-            lib.csa_compress(None, None, lib.F32, t["bias"], wl.m, wl.B, wl.T, wl.d_c, wl.d_r,
-                             self.entries, hidden=t["hidden"], w_x=t["w_x"], w_g=t["w_g"],
-                             d_model=wl.d_model, raw_x_out=self.raw_x)
-        else:
-            lib.csa_compress(t["x"], t["g"], _DT[wl.kv_dtype], t["bias"], wl.m, wl.B, wl.T,
-                             wl.d_c, wl.d_r, self.entries)
+        b = {}
+        if wl.kind == "hca_prefill" or wl.compress_on_path:
+            if wl.d_model:
+                b["compress"] = lib.csa_compress(
+                    None, None, lib.F32, t["bias"], wl.m, wl.B, wl.T, wl.d_c, wl.d_r,
+                    self.entries, hidden=t["hidden"], w_x=t["w_x"], w_g=t["w_g"],
+                    d_model=wl.d_model, raw_x_out=self.raw_x, bind=True)
+            else:
+                b["compress"] = lib.csa_compress(t["x"], t["g"], _DT[wl.kv_dtype], t["bias"], wl.m,
+                                                 wl.B, wl.T, wl.d_c, wl.d_r, self.entries,
+                                                 bind=True)
+        if wl.kind == "hca_prefill":
+            b["hca"] = lib.hca_attend(self.seq, self.pos, t["q"], _DT[wl.q_dtype], wl.H,
+                                      self.entries, wl.m, self.sm_scale, self.out, self.lse,
+                                      ws=self.ws["hca"], bind=True)
+            self._b = b
+            return
+        b["index"] = lib.csa_index(self.seq, self.pos, t["q_i"], t["w_i"], t["k_i"], self.scores,
+                                   _DT[wl.idx_dtype], wl.H_I, wl.d_I, wl.B, wl.n_entries, wl.m,
+                                   q_i_scale=t.get("q_i_scale"), k_i_scale=t.get("k_i_scale"),
+                                   bind=True)
+        b["topk"] = lib.csa_topk(self.seq, self.pos, self.scores, self.idx, wl.n_entries, wl.m,
+                                 wl.k, ws=self.ws["topk"], bind=True)
+        b["attend"] = lib.csa_attend(self.seq, self.pos, t["q"], _DT[wl.q_dtype], wl.H,
+                                     self.entries, wl.m, self.idx, wl.k, self.raw, wl.window,
+                                     self.sm_scale, self.out, self.lse, ws=self.ws["attend"],
+                                     bind=True)
+        if wl.kind == "hybrid_decode":
+            b["hca"] = lib.hca_attend(self.seq, self.pos, t["q_hca"], _DT[wl.q_dtype], wl.H,
+                                      self.hca_entries, wl.m_hca, self.sm_scale, self.hca_out,
+                                      self.hca_lse, ws=self.ws["hca"], bind=True)
+        self._b = b
+
+    def _h(self) -> int:
+        return torch.cuda.current_stream(self.dev).cuda_stream
+
+    def compress(self):
+        self._b["compress"](self._h())
 
     def index(self):
-        wl, t = self.wl, self.t
-        lib.csa_index(self.seq, self.pos, t["q_i"], t["w_i"], t["k_i"], self.scores,
-                      _DT[wl.idx_dtype], wl.H_I, wl.d_I, wl.B, wl.n_entries, wl.m,
-                      q_i_scale=t.get("q_i_scale"), k_i_scale=t.get("k_i_scale"))
+        self._b["index"](self._h())
 
     def topk(self):
-        wl = self.wl
-        lib.csa_topk(self.seq, self.pos, self.scores, self.idx, wl.n_entries, wl.m, wl.k,
-                     ws=self.ws["topk"])
+        self._b["topk"](self._h())
 
     def attend(self, idx=None):
+        if idx is None:
+            self._b["attend"](self._h())
+            return
         wl = self.wl
         lib.csa_attend(self.seq, self.pos, self.t["q"], _DT[wl.q_dtype], wl.H, self.entries,
-                       wl.m, self.idx if idx is None else idx, wl.k, self.raw, wl.window,
-                       self.sm_scale, self.out, self.lse, ws=self.ws["attend"])
+                       wl.m, idx, wl.k, self.raw, wl.window, self.sm_scale, self.out, self.lse,
+                       ws=self.ws["attend"])
 
     def hca(self):
-        wl = self.wl
-        if wl.kind == "hca_prefill":
-            lib.hca_attend(self.seq, self.pos, self.t["q"], _DT[wl.q_dtype], wl.H, self.entries,
-                           wl.m, self.sm_scale, self.out, self.lse, ws=self.ws["hca"])
-        else:
-            lib.hca_attend(self.seq, self.pos, self.t["q_hca"], _DT[wl.q_dtype], wl.H,
-                           self.hca_entries, wl.m_hca, self.sm_scale, self.hca_out,
-                           self.hca_lse, ws=self.ws["hca"])
+        self._b["hca"](self._h())
 
     def run(self):
         """Enqueue one whole step of the workload's hot path on the current stream (the hybrid
         decode's HCA layer on a second stream that the current one waits for at the end)."""
-        wl = self.wl
+        wl, b = self.wl, self._b
+        main = torch.cuda.current_stream(self.dev)
+        h = main.cuda_stream
         if wl.kind == "hca_prefill":
-            self.compress()
-            self.hca()
+            b["compress"](h)
+            b["hca"](h)
             return
         if wl.compress_on_path:
-            self.compress()
-        self.index()
+            b["compress"](h)
+        b["index"](h)
         if wl.kind == "hybrid_decode":
             # The HCA layer needs nothing the CSA layer computes. It starts once the CSA index,
             # which streams at the memory's rate on every CU, is done, and runs beside the CSA
             # top-k and attention, whose few workgroups leave most CUs free (measured per hybrid
             # step: 128 us, against 129 us forked before the index and 150 us after the top-k).
-            main = torch.cuda.current_stream(self.dev)
             self._fork.record(main)
             self._side.wait_event(self._fork)
-            with torch.cuda.stream(self._side):
-                self.hca()
+            b["hca"](self._side_h)
             self._join.record(self._side)
-        self.topk()
-        self.attend()
+        b["topk"](h)
+        b["attend"](h)
         if wl.kind == "hybrid_decode":
             main.wait_event(self._join)

@@ -119,6 +119,30 @@ def _check(status: int, what: str):
                            f"({lib.csa_last_error().decode()})")
 
 
+class Bound:
+    """A library call with its arguments marshalled once (the bind=True form of the call
+    functions below): `bound(stream_handle)` enqueues the same call, on the same tensors, on a
+    raw stream handle (`torch.cuda.Stream.cuda_stream`). It keeps the tensors it points into
+    alive. Marshalling once keeps the host's cost per call at one foreign call, which matters
+    where a decode step's kernels are a few tens of microseconds each."""
+    __slots__ = ("fn", "args", "what", "keep")
+
+    def __init__(self, fn, args: tuple, what: str, keep: tuple):
+        self.fn, self.args, self.what, self.keep = fn, args, what, keep
+
+    def __call__(self, stream_handle: int):
+        status = self.fn(*self.args, stream_handle)
+        if status != 0:
+            _check(status, self.what)
+
+
+def _call(fn, args: tuple, what: str, stream, bind: bool, keep: tuple):
+    if bind:
+        return Bound(fn, args, what, keep)
+    _check(fn(*args, _stream(stream)), what)
+    return None
+
+
 @dataclass
 class Store:
     """A cache-row store (csa_kv_t): c [B, rows, ld_c], r [B, rows, ld_r] (or a view into c's
@@ -178,23 +202,25 @@ def csa_cache_append(x_new, g_new, in_dtype: int, bias, m: int, pos, d_c: int, d
 
 def csa_compress(x, g, in_dtype: int, bias, m: int, B: int, T: int, d_c: int, d_r: int,
                  out: Store, hidden=None, w_x=None, w_g=None, d_model: int = 0,
-                 raw_x_out=None, stream=None):
+                 raw_x_out=None, stream=None, bind: bool = False):
     lib = load()
     o = out.as_out()
-    _check(lib.csa_compress(_ptr(x), _ptr(g), in_dtype, _ptr(bias), m, B, T, d_c, d_r,
-                            _ptr(hidden), _ptr(w_x), _ptr(w_g), d_model, ctypes.byref(o),
-                            _ptr(raw_x_out), _stream(stream)), "csa_compress")
+    args = (_ptr(x), _ptr(g), in_dtype, _ptr(bias), m, B, T, d_c, d_r, _ptr(hidden), _ptr(w_x),
+            _ptr(w_g), d_model, ctypes.byref(o), _ptr(raw_x_out))
+    return _call(lib.csa_compress, args, "csa_compress", stream, bind,
+                 (x, g, bias, out, hidden, w_x, w_g, raw_x_out, o))
 
 
 def csa_index(seq, pos, q_i, w, k_i, scores, dtype: int, H_I: int, d_I: int, B: int, N: int,
               m: int, q_i_scale=None, k_i_scale=None, ld_scores: Optional[int] = None,
-              stream=None):
+              stream=None, bind: bool = False):
     lib = load()
     Q = _queries(seq, pos)
     ld = N if ld_scores is None else ld_scores
-    _check(lib.csa_index(ctypes.byref(Q), _ptr(q_i), _ptr(q_i_scale), dtype, _ptr(w), H_I, d_I,
-                         _ptr(k_i), _ptr(k_i_scale), dtype, B, N, m, _ptr(scores), ld,
-                         _stream(stream)), "csa_index")
+    args = (ctypes.byref(Q), _ptr(q_i), _ptr(q_i_scale), dtype, _ptr(w), H_I, d_I, _ptr(k_i),
+            _ptr(k_i_scale), dtype, B, N, m, _ptr(scores), ld)
+    return _call(lib.csa_index, args, "csa_index", stream, bind,
+                 (seq, pos, q_i, w, k_i, scores, q_i_scale, k_i_scale, Q))
 
 
 def csa_topk_workspace_bytes(nq: int, N: int, k: int) -> int:
@@ -202,15 +228,16 @@ def csa_topk_workspace_bytes(nq: int, N: int, k: int) -> int:
 
 
 def csa_topk(seq, pos, scores, idx, N: int, m: int, k: int, ld_scores: Optional[int] = None,
-             ws: Optional[torch.Tensor] = None, stream=None):
+             ws: Optional[torch.Tensor] = None, stream=None, bind: bool = False):
     lib = load()
     Q = _queries(seq, pos)
     need = lib.csa_topk_workspace_bytes(Q.nq, N, k)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ld = N if ld_scores is None else ld_scores
-    _check(lib.csa_topk(ctypes.byref(Q), _ptr(scores), ld, N, m, k, _ptr(idx), _ptr(ws),
-                        0 if ws is None else ws.numel(), _stream(stream)), "csa_topk")
+    args = (ctypes.byref(Q), _ptr(scores), ld, N, m, k, _ptr(idx), _ptr(ws),
+            0 if ws is None else ws.numel())
+    return _call(lib.csa_topk, args, "csa_topk", stream, bind, (seq, pos, scores, idx, ws, Q))
 
 
 def csa_index_mxfp4(seq, pos, q_i, q_i_scale, w, k_i, k_i_scale, scores, H_I: int, d_I: int,
@@ -260,7 +287,7 @@ def hca_attend_workspace_bytes(nq: int, H: int, d_c: int, N: int) -> int:
 
 def csa_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m: int, idx, k: int,
                raw: Optional[Store], window: int, sm_scale: float, out, lse=None,
-               ws: Optional[torch.Tensor] = None, stream=None):
+               ws: Optional[torch.Tensor] = None, stream=None, bind: bool = False):
     lib = load()
     Q = _queries(seq, pos)
     need = lib.csa_attend_workspace_bytes(Q.nq, H, entries.d_c, k + window)
@@ -268,10 +295,11 @@ def csa_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m: int, idx, k
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     e = entries.as_c()
     r = raw.as_c() if raw is not None else None
-    _check(lib.csa_attend(ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(e), m, _ptr(idx), k,
-                          ctypes.byref(r) if r is not None else None, window, sm_scale,
-                          _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
-                          _stream(stream)), "csa_attend")
+    args = (ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(e), m, _ptr(idx), k,
+            ctypes.byref(r) if r is not None else None, window, sm_scale, _ptr(out), _ptr(lse),
+            _ptr(ws), 0 if ws is None else ws.numel())
+    return _call(lib.csa_attend, args, "csa_attend", stream, bind,
+                 (seq, pos, q, entries, idx, raw, out, lse, ws, Q, e, r))
 
 
 def csa_attend_tokens(seq, pos, q, q_dtype: int, H: int, raw: Store, m: int, idx, k: int,
@@ -292,16 +320,18 @@ def csa_attend_tokens(seq, pos, q, q_dtype: int, H: int, raw: Store, m: int, idx
 
 
 def hca_attend(seq, pos, q, q_dtype: int, H: int, entries: Store, m_prime: int,
-               sm_scale: float, out, lse=None, ws: Optional[torch.Tensor] = None, stream=None):
+               sm_scale: float, out, lse=None, ws: Optional[torch.Tensor] = None, stream=None,
+               bind: bool = False):
     lib = load()
     Q = _queries(seq, pos)
     need = lib.hca_attend_workspace_bytes(Q.nq, H, entries.d_c, entries.rows)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     e = entries.as_c()
-    _check(lib.hca_attend(ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(e), m_prime,
-                          sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
-                          0 if ws is None else ws.numel(), _stream(stream)), "hca_attend")
+    args = (ctypes.byref(Q), _ptr(q), q_dtype, H, ctypes.byref(e), m_prime, sm_scale, _ptr(out),
+            _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel())
+    return _call(lib.hca_attend, args, "hca_attend", stream, bind,
+                 (seq, pos, q, entries, out, lse, ws, Q, e))
 
 
 def kernel_timing_enable(cap: int):
