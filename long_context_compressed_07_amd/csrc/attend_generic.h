@@ -107,15 +107,14 @@ __host__ __device__ constexpr size_t generic_smem_bytes(int d) {
 // The arithmetic of attend_generic_one (an online softmax over chunks of keys; within a chunk the
 // same sums in the same order), with chunks of `chunk` keys whose rows are first copied into LDS
 // by the whole block (the chunk boundaries, where the running sums are rescaled, differ, so results
-// agree to rounding): row elements are read once,
-// by consecutive threads, instead of one row per thread in the logits and one dependent load per
-// key in the output sums. A chunk holds `chunk` keys (at most kGenThreads); rows are stored with a
+// agree to rounding): row elements are read once, by the lanes of a wave across each row, instead
+// of one row per thread in the logits and one dependent load per key in the output sums. A chunk holds `chunk` keys (at most kGenThreads); rows are stored with a
 // stride of d + 1 floats so that the threads of the logit loop, one key each, read different banks.
 __host__ __device__ constexpr int staged_row_stride(int d) { return d + 1; }
 
 // Floats ahead of the 8-byte row indices: the query (d rounded up to even), probabilities and
 // row scales of the chunk, the reduction slots.
-__host__ __device__ constexpr int staged_floats(int d) { return ((d + 1) & ~1) + 2 * kGenThreads + 8; }
+__host__ __device__ constexpr int staged_floats(int d) { return ((d + 3) & ~3) + 2 * kGenThreads + 8; }
 
 __host__ __device__ constexpr size_t staged_fixed_bytes(int d) {
   return sizeof(float) * staged_floats(d) + 2 * sizeof(uint64_t) * kGenThreads;
@@ -142,47 +141,53 @@ __device__ __forceinline__ T gload(const void* base, int64_t off) {
   return ((GT*)base)[off];
 }
 
-// The chunk's cnt rows into sk (row j at j * ld), element by element in row order, from the rows'
-// addresses in s_cptr / s_rptr (0: no row; the row's c part, then its r part, of dtype DT): 32
-// loads per thread are issued before their LDS stores, so the copy is not a chain of load
-// latencies.
+// The chunk's cnt rows into sk (row j at j * ld) from the rows' addresses in s_cptr / s_rptr (0:
+// no row; the row's c part, then its r part, of dtype DT). Wave v copies rows v, v + 4, ..., 16
+// rows at a time, its lanes across each row's elements (64 apart), so a row's address is one
+// wave-uniform value and 32 loads per lane are in flight before their LDS stores.
+template <int DT>
+__device__ __forceinline__ float staged_elem(uint64_t cp, uint64_t rp, int e, int d_c) {
+  if (e < d_c) {
+    const void* c = (const void*)(uintptr_t)cp;
+    if constexpr (DT == CSA_F32) return gload<float>(c, e);
+    if constexpr (DT == CSA_BF16) return bf16_to_f32(gload<uint16_t>(c, e));
+    return e4m3_to_f32(gload<uint8_t>(c, e));
+  }
+  const void* r = (const void*)(uintptr_t)rp;
+  if constexpr (DT == CSA_F32) return gload<float>(r, e - d_c);
+  return bf16_to_f32(gload<uint16_t>(r, e - d_c));
+}
+
 template <int DT>
 __device__ void stage_rows(int d_c, int cnt, int d, int ld, const uint64_t* s_cptr,
                            const uint64_t* s_rptr, float* sk) {
-  constexpr int kBatch = 32;
-  const int n = cnt * d;
-  for (int i0 = 0; i0 < n; i0 += kBatch * kGenThreads) {
-    float v[kBatch];
+  constexpr int kRows = 16, kCols = 2;   // per wave and batch: 16 rows x 2 x 64 elements
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  constexpr int kWaves = kGenThreads / kWave;
+  for (int j0 = wv; j0 < cnt; j0 += kWaves * kRows)
+    for (int e0 = 0; e0 < d; e0 += kWave * kCols) {
+      float v[kRows][kCols];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kGenThreads + (int)threadIdx.x;
-      v[u] = 0.f;
-      if (i < n) {
-        const int j = i / d, e = i - j * d;
-        const uint64_t cp = s_cptr[j];
-        if (cp != 0) {
-          if (e < d_c) {
-            const void* c = (const void*)(uintptr_t)cp;
-            if constexpr (DT == CSA_F32) v[u] = gload<float>(c, e);
-            else if constexpr (DT == CSA_BF16) v[u] = bf16_to_f32(gload<uint16_t>(c, e));
-            else v[u] = e4m3_to_f32(gload<uint8_t>(c, e));
-          } else {
-            const void* r = (const void*)(uintptr_t)s_rptr[j];
-            if constexpr (DT == CSA_F32) v[u] = gload<float>(r, e - d_c);
-            else v[u] = bf16_to_f32(gload<uint16_t>(r, e - d_c));
-          }
+      for (int r = 0; r < kRows; ++r) {
+        const int j = j0 + kWaves * r;
+        const uint64_t cp = j < cnt ? s_cptr[j] : 0;
+        const uint64_t rp = j < cnt ? s_rptr[j] : 0;
+#pragma unroll
+        for (int q = 0; q < kCols; ++q) {
+          const int e = e0 + lane + kWave * q;
+          v[r][q] = cp != 0 && e < d ? staged_elem<DT>(cp, rp, e, d_c) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int j = j0 + kWaves * r;
+#pragma unroll
+        for (int q = 0; q < kCols; ++q) {
+          const int e = e0 + lane + kWave * q;
+          if (j < cnt && e < d) sk[j * ld + e] = v[r][q];
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kGenThreads + (int)threadIdx.x;
-      if (i < n) {
-        const int j = i / d;
-        sk[j * ld + (i - j * d)] = v[u];
-      }
-    }
-  }
 }
 
 static __device__ void attend_generic_staged(const AttendArgs& a, int qi, int h, float* smem,
@@ -190,7 +195,7 @@ static __device__ void attend_generic_staged(const AttendArgs& a, int qi, int h,
   const int d_c = a.ent.d_c, d_r = a.ent.d_r, d = d_c + d_r;
   const int ld = staged_row_stride(d);
   float* sq = smem;                                // [d]
-  float* sp = sq + ((d + 1) & ~1);                 // [kGenThreads] probabilities of the chunk
+  float* sp = sq + ((d + 3) & ~3);                 // [kGenThreads] probabilities of the chunk
   float* s_scale = sp + kGenThreads;               // [kGenThreads] row scale of each key
   float* s_red = s_scale + kGenThreads;            // [8]
   // [kGenThreads] address of each key's c row (0: no row) and r row
@@ -254,16 +259,28 @@ static __device__ void attend_generic_staged(const AttendArgs& a, int qi, int h,
 #pragma unroll
     for (int r = 0; r < kMaxPer; ++r) o[r] *= corr;
     run_max = new_max;
-#pragma unroll 4
-    for (int j = 0; j < cnt; ++j) {
-      const float pj = sp[j];
-      if (pj == 0.f) continue;
-      const float w = pj * s_scale[j];
-      const float* vr = sk + j * ld;
+    // Output sums in key order, four keys per step; a key without a row has p = 0 and a zero
+    // row, so no key is skipped (a test on p would serialise every step on its LDS read).
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      const float4 p4 = *reinterpret_cast<const float4*>(sp + j);
+      const float4 s4 = *reinterpret_cast<const float4*>(s_scale + j);
+      const float w[4] = {p4.x * s4.x, p4.y * s4.y, p4.z * s4.z, p4.w * s4.w};
 #pragma unroll
       for (int r = 0; r < kMaxPer; ++r) {
         const int e = threadIdx.x + r * kGenThreads;
-        if (e < d_c) o[r] = fmaf(w, vr[e], o[r]);
+        if (e < d_c) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[r] = fmaf(w[u], sk[(j + u) * ld + e], o[r]);
+        }
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float w = sp[j] * s_scale[j];
+#pragma unroll
+      for (int r = 0; r < kMaxPer; ++r) {
+        const int e = threadIdx.x + r * kGenThreads;
+        if (e < d_c) o[r] = fmaf(w, sk[j * ld + e], o[r]);
       }
     }
     __syncthreads();
