@@ -175,7 +175,8 @@ class Step:
             # The HCA layer needs nothing the CSA layer computes. It starts once the CSA index,
             # which streams at the memory's rate on every CU, is done, and runs beside the CSA
             # top-k and attention, whose few workgroups leave most CUs free (measured per hybrid
-            # step: 128 us, against 129 us forked before the index and 150 us after the top-k).
+            # step: 110.1 us, against 111.0 us forked before the index; forked after the top-k,
+            # with earlier kernels, it measured 150 against 128 us).
             self._fork.record(main)
             self._side.wait_event(self._fork)
             b["hca"](self._side_h)
