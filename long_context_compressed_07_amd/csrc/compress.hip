@@ -142,34 +142,29 @@ __global__ void __launch_bounds__(256) pool_kernel(CompressArgs a, int cpr, int 
   if (active) store_entry<VEC>(a.out, b, j, ch, acc, sigma);
 }
 
-// fp32 projection + pooling. Tile: 64 tokens x 32 channels of both x and g per workgroup of 512
-// threads; the model dims are split in two halves, one per 256 threads, and thread (ty, tx) of each
-// half owns tokens [4ty, 4ty+4) and channels [2tx, 2tx+2), so every block of m in {1, 2, 4} tokens
-// is thread-local. Each half's output is one fma chain over its dims in order; the second half's
-// sums are then added to the first's (always in that order) and the first half pools and stores.
-// The 4096-token, 128-channel projection runs 256 workgroups (one per CU, two waves per SIMD).
-__global__ void __launch_bounds__(512) project_pool_kernel(CompressArgs a) {
+// fp32 projection + pooling on fp32 MFMA. A workgroup of 4 waves takes 64 tokens x 32 channels:
+// wave w forms the 32 x 32 tile of tokens 32 (w & 1) .. + 32 of x (w < 2) or g (w >= 2) with
+// mfma_f32_32x32x2_f32 over the model dims, from 32-dim slices of hidden and weights staged in LDS
+// (the next slice loaded during the current one). In the MFMA's output layout a lane holds one
+// channel and tokens 8 q + 4 (lane >> 5) + (0..3), q < 4: every block of m in {1, 2, 4} tokens
+// is lane-local. The g waves hand their tiles to the x waves through LDS; the x waves store the
+// raw rows and pool.
+__global__ void __launch_bounds__(256) project_pool_kernel(CompressArgs a) {
+  typedef float floatx16 __attribute__((ext_vector_type(16)));
   constexpr int TK = 32;
   constexpr int TC = 32;
-  __shared__ float sh[2][64][TK + 1];
-  __shared__ float swx[2][TK][TC];
-  __shared__ float swg[2][TK][TC];
-  const int half = threadIdx.x >> 8;
-  const int tid = threadIdx.x & 255;
-  const int ty = tid >> 4, tx = tid & 15;
+  __shared__ float sh[64][TK + 1];
+  __shared__ float sw[2][TK][TC];        // w_x, w_g slices
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int64_t b = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int c0 = blockIdx.y * TC;
   const int d = a.d_c + a.d_r;
   const int dm = a.d_model;
-  // Dims [kb, ke) of this half (both bounds multiples of 4, as d_model is); both halves take the
-  // same number of slices so that they meet at every barrier.
-  const int kmid = ((dm / 2) + 3) & ~3;
-  const int kb = half ? kmid : 0, ke = half ? dm : kmid;
-  const int nsl = ((dm - kmid > kmid ? dm - kmid : kmid) + TK - 1) / TK;
-  // Slice kb + TK s of this half: hidden 64 tokens x 32 (two float4 per thread), w_x (waves 0-1
-  // of the half) or w_g (waves 2-3) 32 rows x 32 channels (two float4 per thread). The next
-  // slice's loads are issued before the current slice's products, so their latency overlaps them.
+  const int tg = w & 1, mat = w >> 1;    // token group, matrix (0: x, 1: g)
+  // Staging: hidden 64 tokens x 32 dims (two float4 per thread), w_x (threads 0-127) or w_g
+  // (128-255) 32 dims x 32 channels (two float4 per thread).
   const int tok = tid >> 2, kq = (tid & 3) * 4;
   const int wt = tid & 127, wr = wt >> 3, wc = (wt & 7) * 4;
   const float* W = tid < 128 ? a.w_x : a.w_g;
@@ -179,95 +174,67 @@ __global__ void __launch_bounds__(512) project_pool_kernel(CompressArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int k = k0 + kq + 16 * u;
-      hv[u] = t < a.T && k < ke ? *reinterpret_cast<const float4*>(a.hidden + (b * a.T + t) * dm + k)
+      hv[u] = t < a.T && k < dm ? *reinterpret_cast<const float4*>(a.hidden + (b * a.T + t) * dm + k)
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
       const int kr = k0 + wr + 16 * u;
-      wv[u] = kr < ke ? *reinterpret_cast<const float4*>(W + (int64_t)kr * d + c0 + wc)
+      wv[u] = kr < dm ? *reinterpret_cast<const float4*>(W + (int64_t)kr * d + c0 + wc)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  float ax[4][2] = {}, ag[4][2] = {};
-  load_slice(kb);
-  for (int sl = 0; sl < nsl; ++sl) {
-    const int k0 = kb + sl * TK;
+  floatx16 acc = floatx16{};
+  const int arow = 32 * tg + (lane & 31), kl = lane >> 5, bcol = lane & 31;
+  load_slice(0);
+  for (int k0 = 0; k0 < dm; k0 += TK) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kk = kq + 16 * u;
-      sh[half][tok][kk] = hv[u].x; sh[half][tok][kk + 1] = hv[u].y;
-      sh[half][tok][kk + 2] = hv[u].z; sh[half][tok][kk + 3] = hv[u].w;
-      *reinterpret_cast<float4*>(tid < 128 ? &swx[half][wr + 16 * u][wc]
-                                           : &swg[half][wr + 16 * u][wc]) = wv[u];
+      sh[tok][kk] = hv[u].x; sh[tok][kk + 1] = hv[u].y; sh[tok][kk + 2] = hv[u].z; sh[tok][kk + 3] = hv[u].w;
+      *reinterpret_cast<float4*>(&sw[tid < 128 ? 0 : 1][wr + 16 * u][wc]) = wv[u];
     }
     __syncthreads();
-    if (sl + 1 < nsl) load_slice(k0 + TK);
+    if (k0 + TK < dm) load_slice(k0 + TK);
 #pragma unroll
-    for (int kk = 0; kk < TK; ++kk) {
-      float h[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = sh[half][ty * 4 + r][kk];
-      const float2 wx = *reinterpret_cast<const float2*>(&swx[half][kk][tx * 2]);
-      const float2 wg = *reinterpret_cast<const float2*>(&swg[half][kk][tx * 2]);
-      const float wxv[2] = {wx.x, wx.y};
-      const float wgv[2] = {wg.x, wg.y};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          ax[r][c] = fmaf(h[r], wxv[c], ax[r][c]);
-          ag[r][c] = fmaf(h[r], wgv[c], ag[r][c]);
-        }
-    }
+    for (int kk = 0; kk < TK; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sh[arow][kk + kl], sw[mat][kk + kl][bcol], acc, 0, 0, 0);
     __syncthreads();
   }
-  // The second half's sums to the first half (through the idle hidden tiles: 256 x 16 floats).
-  float* red = &sh[0][0][0];
-  if (half) {
+  // g tiles to the x waves (through the idle hidden tile: 2 x 16 x 64 floats).
+  float* red = &sh[0][0];
+  if (mat == 1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        red[(4 * r + 2 * c) * 256 + tid] = ax[r][c];
-        red[(4 * r + 2 * c + 1) * 256 + tid] = ag[r][c];
-      }
+    for (int i = 0; i < 16; ++i) red[(tg * 16 + i) * 64 + lane] = acc[i];
   }
   __syncthreads();
-  if (half) return;
+  if (mat == 1) return;
+  float gv[16];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int i = 0; i < 16; ++i) gv[i] = red[(tg * 16 + i) * 64 + lane];
+  const int ch = c0 + (lane & 31);
+  // Token of element i: t0 + 32 tg + 8 (i >> 2) + 4 (lane >> 5) + (i & 3).
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      ax[r][c] += red[(4 * r + 2 * c) * 256 + tid];
-      ag[r][c] += red[(4 * r + 2 * c + 1) * 256 + tid];
-    }
-  const int ch = c0 + tx * 2;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t t = t0 + ty * 4 + r;
-    if (t < a.T) {
-      float* p = a.raw_x_out + (b * a.T + t) * d + ch;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) p[c] = ax[r][c];
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + 32 * tg + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    if (t < a.T) a.raw_x_out[(b * a.T + t) * d + ch] = acc[i];
   }
   const int m = a.m;
-  for (int blk = 0; blk < 4 / m; ++blk) {
-    const int64_t tb = t0 + ty * 4 + blk * m;  // first token of the block
-    if (tb + m > a.T) break;
-    float e[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tq = t0 + 32 * tg + 8 * q + 4 * (lane >> 5);   // first of this lane's four tokens
+    for (int blk = 0; blk < 4 / m; ++blk) {
+      const int64_t tb = tq + blk * m;
+      if (tb + m > a.T) break;
       float ai[4], xi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = blk * m + (i < m ? i : 0);
-        ai[i] = ag[t][c] + a.bias[i < m ? i : 0];
-        xi[i] = ax[t][c];
+        const int e = 4 * q + blk * m + (i < m ? i : 0);
+        ai[i] = gv[e] + a.bias[i < m ? i : 0];
+        xi[i] = acc[e];
       }
       PoolAcc pa = pool_start();
       pool_fold(pa, ai, xi, m);
-      e[c] = pool_value(pa);
+      const float ev = pool_value(pa);
+      store_entry<1>(a.out, b, tb / m, ch, &ev, 0.f);
     }
-    store_entry<2>(a.out, b, tb / m, ch, e, 0.f);
   }
 }
 
@@ -279,7 +246,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.hidden != nullptr) {
     if (a.T == 0) return hipSuccess;
     dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)(d / 32), (unsigned)a.B);
-    project_pool_kernel<<<grid, 512, 0, s>>>(a);
+    project_pool_kernel<<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
   if (nb == 0) return hipSuccess;
